@@ -1,0 +1,134 @@
+"""Block-wise mixed-bit weight-only quantization and the reference GEMM.
+
+Sources (cited by page title and section):
+
+* MixLLM page, section 2.1 "quantization principle": the affine map
+  X_q = clamp(round(X / s) + z, range) and its inverse X' = (X_q - z) * s; a
+  bitwidth b gives 2^b levels; scales and zeros may be per group.
+* ScaleBITS explainer page, section 1.2.2 (hardware-aligned block partition):
+  64x128 blocks with one bitwidth per block; section 4.2 gives the bitwidth
+  set {1,2,3,4,6,8}; section 3.2 the fused dequantize-multiply kernel.
+* SBVR page, section 4.1: groups of 128 run along the GEMV inner dimension.
+
+Readings where the pages are silent (all listed in the design doc):
+* a block is 64 output rows x 128 input columns, so each (row, 128-column
+  group) lies in one block and has one bitwidth;
+* s and z are chosen by min/max: s = (max - min) / (2^b - 1) rounded to fp16,
+  z = clamp(rint(-min / s), 0, 2^b - 1); rint is round-half-to-even and the
+  code is rint(v / s) + z, then clamped -- the order of the formula;
+* codes are computed with the fp16-rounded scale (the one that is stored);
+* a constant group c gets s = |c| (1 if c = 0); an fp16 scale that would
+  round to 0 becomes 2^-24;
+* the decisions are taken in fp64; dequantization (q - z) * s is exact in
+  fp32 (at most 8 + 11 significant bits).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK_ROWS = 64
+GROUP = 128
+ALLOWED_BITS = (1, 2, 3, 4, 6, 8)
+FP16_MIN_SUBNORMAL = 2.0 ** -24
+
+
+def fp16_rne(a) -> np.ndarray:
+    """Round fp64/fp32 values to the nearest fp16 (ties to even)."""
+    return np.asarray(a).astype(np.float16)
+
+
+def group_bits(bits: np.ndarray, N: int, K: int) -> np.ndarray:
+    """int64 [N][K/128]: the bitwidth of each (row, group) -- its block's."""
+    bits = np.asarray(bits)
+    if bits.shape != (N // BLOCK_ROWS, K // GROUP):
+        raise ValueError(f"bitmap shape {bits.shape} != {(N // BLOCK_ROWS, K // GROUP)}")
+    if not np.isin(bits, ALLOWED_BITS).all():
+        raise ValueError("bitwidth outside {1,2,3,4,6,8}")
+    return np.repeat(bits.astype(np.int64), BLOCK_ROWS, axis=0)
+
+
+def choose_scale_zero(lo: np.ndarray, hi: np.ndarray, levels: np.ndarray):
+    """Min/max scale and zero point of each group (fp64 decisions).
+
+    Returns (s16, z) with s16 float16 and z float64 holding integers."""
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    levels = np.asarray(levels, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s16 = fp16_rne((hi - lo) / levels)
+    s16 = np.where((hi > lo) & (s16 == 0), np.float16(FP16_MIN_SUBNORMAL), s16)
+    const = hi == lo
+    s16 = np.where(const & (lo != 0), fp16_rne(np.abs(lo)), s16)
+    s16 = np.where(const & (lo == 0), np.float16(1.0), s16).astype(np.float16)
+    s = s16.astype(np.float64)
+    z = np.clip(np.rint(-lo / s), 0, levels)
+    return s16, z
+
+
+def quantize_blocks(W16: np.ndarray, bits: np.ndarray):
+    """Asymmetric group-wise RTN of an fp16 [N][K] matrix, each (row, group)
+    at the bitwidth of its 64x128 block.
+
+    Returns q uint8 [N][K], s16 float16 [N][K/128], z16 float16 [N][K/128]."""
+    W16 = np.asarray(W16, np.float16)
+    N, K = W16.shape
+    if N % BLOCK_ROWS or K % GROUP:
+        raise ValueError("N must be a multiple of 64 and K of 128")
+    G = K // GROUP
+    gb = group_bits(bits, N, K)
+    q = np.empty((N, K), np.uint8)
+    s16 = np.empty((N, G), np.float16)
+    z16 = np.empty((N, G), np.float16)
+    for r0 in range(0, N, 1024):                       # row chunks bound memory
+        v = W16[r0:r0 + 1024].astype(np.float64).reshape(-1, G, GROUP)
+        levels = (2.0 ** gb[r0:r0 + 1024] - 1.0)
+        sc, z = choose_scale_zero(v.min(axis=2), v.max(axis=2), levels)
+        s = sc.astype(np.float64)[:, :, None]
+        code = np.clip(np.rint(v / s) + z[:, :, None], 0, levels[:, :, None])
+        q[r0:r0 + 1024] = code.reshape(-1, K).astype(np.uint8)
+        s16[r0:r0 + 1024] = sc
+        z16[r0:r0 + 1024] = z.astype(np.float16)
+    return q, s16, z16
+
+
+def dequant_fp32(q: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """w' = (q - z) * s in fp32 (exact: |q - z| < 2^8 and s has 11 bits)."""
+    N, K = q.shape
+    qz = q.astype(np.float32).reshape(N, -1, GROUP) - z16.astype(np.float32)[:, :, None]
+    return (qz * s16.astype(np.float32)[:, :, None]).reshape(N, K)
+
+
+def dequant_fp16(q, s16, z16) -> np.ndarray:
+    return fp16_rne(dequant_fp32(q, s16, z16))
+
+
+def gemm_fp64(x16: np.ndarray, w32: np.ndarray) -> np.ndarray:
+    """y = x . W'^T in fp64 (x [M][K], W' [N][K])."""
+    return np.asarray(x16, np.float64) @ np.asarray(w32, np.float64).T
+
+
+def reference_gemm(x16, W16, bits) -> np.ndarray:
+    """End-to-end reference: quantize, dequantize exactly, fp64 product."""
+    q, s16, z16 = quantize_blocks(W16, bits)
+    return gemm_fp64(x16, dequant_fp32(q, s16, z16))
+
+
+def reference_rows(x16, W16, bits, rows) -> np.ndarray:
+    """Reference outputs y[:, rows] for selected rows only (quantizes just the
+    64-row block rows that hold them), for sampled checks at full size."""
+    rows = np.asarray(rows)
+    out = np.empty((np.asarray(x16).shape[0], rows.size), np.float64)
+    for j, n in enumerate(rows):
+        br = int(n) // BLOCK_ROWS
+        q, s16, z16 = quantize_blocks(W16[br * 64:(br + 1) * 64], bits[br:br + 1])
+        w = dequant_fp32(q, s16, z16)[int(n) - br * 64]
+        out[:, j] = np.asarray(x16, np.float64) @ w.astype(np.float64)
+    return out
+
+
+def rel_inf_err(y, y_ref) -> float:
+    """||y - y_ref||_inf / ||y_ref||_inf."""
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    den = np.abs(y_ref).max()
+    return float(np.abs(y - y_ref).max() / (den if den > 0 else 1.0))
