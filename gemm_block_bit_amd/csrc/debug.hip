@@ -1,0 +1,83 @@
+// Debug exports over a device block image: the codes and the exactly
+// dequantized weights (q - z) * s in fp32 and rounded to fp16, for
+// bit-exactness tests of the packed layout.  One wave per 64x128 block.
+#include "device.h"
+#include "internal.h"
+#include "layout.h"
+
+namespace gbb {
+
+namespace {
+
+struct UnpackArgs {
+  const uint8_t* bits;
+  const uint32_t* offs;
+  const uint32_t* sz;
+  const uint8_t* codes;
+  uint8_t* q;
+  float* w32;
+  _Float16* w16;
+  int N, K, nbr, nbc;
+};
+
+template <int W0, int W1>
+__device__ void unpack_block(const UnpackArgs& a, int blk, int lane) {
+  constexpr int NP0 = 16 / W0;
+  constexpr int NP1 = W1 ? 16 / W1 : 1;
+  const int br = blk / a.nbc, bc = blk % a.nbc;
+  const uint8_t* cb = a.codes + size_t(a.offs[blk]) * 1024 + 16 * lane;
+  for (int P = 0; P < 64; ++P) {
+    const int d0 = P / NP0, s0 = P % NP0;
+    uint32_t pr = pair_bits<W0>(*reinterpret_cast<const uint32_t*>(cb + 1024 * (d0 >> 2) + 4 * (d0 & 3)), s0);
+    if constexpr (W1 != 0) {
+      const int d1 = P / NP1, s1 = P % NP1;
+      pr |= pair_bits<W1>(*reinterpret_cast<const uint32_t*>(cb + 1024 * (W0 + (d1 >> 2)) + 4 * (d1 & 3)), s1) << W0;
+    }
+    const int u = P >> 2, p = P & 3, rt = u >> 2, kt = u & 3;
+    const int row = br * 64 + 16 * rt + (lane & 15);
+    const int col = bc * 128 + 32 * kt + 8 * (lane >> 4) + 2 * p;
+    const uint32_t e = a.sz[size_t(blk) * 64 + 16 * rt + (lane & 15)];
+    const float s = lo_half(e), z = hi_half(e);
+    const uint32_t qa = pr & 0xffffu, qb = pr >> 16;
+    const size_t o = size_t(row) * a.K + col;
+    if (a.q) a.q[o] = uint8_t(qa), a.q[o + 1] = uint8_t(qb);
+    const float va = (float(qa) - z) * s, vb = (float(qb) - z) * s;
+    if (a.w32) a.w32[o] = va, a.w32[o + 1] = vb;
+    if (a.w16) a.w16[o] = (_Float16)va, a.w16[o + 1] = (_Float16)vb;
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(UnpackArgs a) {
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blk >= a.nbr * a.nbc) return;
+  switch (a.bits[blk]) {
+    case 1: unpack_block<1, 0>(a, blk, lane); break;
+    case 2: unpack_block<2, 0>(a, blk, lane); break;
+    case 3: unpack_block<2, 1>(a, blk, lane); break;
+    case 4: unpack_block<4, 0>(a, blk, lane); break;
+    case 6: unpack_block<4, 2>(a, blk, lane); break;
+    default: unpack_block<4, 4>(a, blk, lane); break;
+  }
+}
+
+}  // namespace
+
+int launch_unpack(const BlockImageView& im, uint8_t* q, float* w32, uint16_t* w16, void* stream) {
+  UnpackArgs a;
+  a.bits = im.bits;
+  a.offs = im.offs;
+  a.sz = im.sz;
+  a.codes = im.codes;
+  a.q = q;
+  a.w32 = w32;
+  a.w16 = reinterpret_cast<_Float16*>(w16);
+  a.N = im.N;
+  a.K = im.K;
+  a.nbr = im.nbr;
+  a.nbc = im.nbc;
+  const int nblk = im.nbr * im.nbc;
+  hipLaunchKernelGGL(unpack_kernel, dim3(unsigned((nblk + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  return int(hipGetLastError());
+}
+
+}  // namespace gbb

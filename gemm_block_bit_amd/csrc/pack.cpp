@@ -1,0 +1,421 @@
+// Offline quantizer and packer for both weight images (host only).
+//
+// Quantization follows the affine map of the MixLLM page, section 2.1:
+// q = clamp(rint(w / s) + z, range), w' = (q - z) * s, with min/max ranges per
+// (row, 128-column group).  Every decision is taken in binary64 and rounds
+// half to even; scales are stored as binary16.  Build without -ffast-math and
+// with -ffp-contract=off so the arithmetic is plain IEEE.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+#include "layout.h"
+
+namespace gbb {
+
+// ---------------------------------------------------------------------------
+// error text
+// ---------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+gbb_status fail(gbb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gbb_status ok() { return GBB_OK; }
+
+// ---------------------------------------------------------------------------
+// binary16 conversions
+// ---------------------------------------------------------------------------
+double half_to_double(uint16_t h) {
+  const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = std::ldexp(double(m), -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = std::ldexp(double(m | 1024), e - 25);
+  return sign ? -v : v;
+}
+
+uint16_t double_to_half(double d) {
+  uint64_t u;
+  std::memcpy(&u, &d, 8);
+  const uint16_t sign = uint16_t((u >> 48) & 0x8000u);
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  if (a >= 0x7ff0000000000000ull) return sign | (a > 0x7ff0000000000000ull ? 0x7e00 : 0x7c00);
+  const int ebits = int(a >> 52);
+  if (ebits == 0) return sign;                       // binary64 subnormal: far below 2^-25
+  const int e = ebits - 1023;                        // value = 1.f * 2^e
+  if (e < -25) return sign;                          // below half the smallest subnormal
+  if (e > 15) return sign | 0x7c00;
+  const uint64_t m = (a & ((1ull << 52) - 1)) | (1ull << 52);
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);  // bits dropped from the 53-bit significand
+  uint64_t keep = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1), halfway = 1ull << (shift - 1);
+  if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
+  if (e >= -14) return uint16_t(sign | ((uint32_t(e + 15) << 10) + uint32_t(keep - 1024)));  // carry may reach inf
+  return uint16_t(sign | uint32_t(keep));            // subnormal (keep == 1024 is the smallest normal)
+}
+
+// Runs f(i) for i in [0, n) on up to hardware_concurrency threads; each i
+// writes a disjoint part of the output, so the result does not depend on the
+// thread count.
+template <class F>
+static void parallel_for(long n, F&& f) {
+  unsigned nt = std::max(1u, std::thread::hardware_concurrency());
+  nt = unsigned(std::min<long>(nt, std::max<long>(1, n)));
+  if (nt <= 1) {
+    for (long i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (long i = t; i < n; i += nt) f(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+// ---------------------------------------------------------------------------
+// group quantizers (binary64 decisions)
+// ---------------------------------------------------------------------------
+namespace {
+
+struct GroupQ {
+  uint16_t s16, z16;
+  double s, z;
+};
+
+// min/max asymmetric scale and zero over n values at `levels` = 2^b - 1.
+GroupQ asym_scale_zero(const double* v, int n, double levels) {
+  double lo = v[0], hi = v[0];
+  for (int i = 1; i < n; ++i) {
+    lo = std::min(lo, v[i]);
+    hi = std::max(hi, v[i]);
+  }
+  GroupQ g;
+  if (hi > lo) {
+    g.s16 = double_to_half((hi - lo) / levels);
+    if ((g.s16 & 0x7fff) == 0) g.s16 = 0x0001;  // 2^-24
+  } else {
+    g.s16 = lo != 0 ? double_to_half(std::fabs(lo)) : uint16_t(0x3c00);
+  }
+  g.s = half_to_double(g.s16);
+  g.z = std::min(std::max(std::nearbyint(-lo / g.s), 0.0), levels) + 0.0;  // +0 for -0
+  g.z16 = double_to_half(g.z);
+  return g;
+}
+
+inline uint8_t asym_code(double v, const GroupQ& g, double levels) {
+  const double q = std::nearbyint(v / g.s) + g.z;
+  return uint8_t(std::min(std::max(q, 0.0), levels));
+}
+
+// 8-bit symmetric: s = fp16(max|v| / 127), q = clamp(rint(v / s), -127, 127).
+uint16_t sym8_scale(const double* v, int n) {
+  double a = 0;
+  for (int i = 0; i < n; ++i) a = std::max(a, std::fabs(v[i]));
+  if (a == 0) return 0x3c00;
+  uint16_t s = double_to_half(a / 127.0);
+  if ((s & 0x7fff) == 0) s = 0x0001;
+  return s;
+}
+
+inline int8_t sym8_code(double v, double s) {
+  const double q = std::nearbyint(v / s);
+  return int8_t(std::min(std::max(q, -127.0), 127.0));
+}
+
+bool all_finite(const uint16_t* W, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if ((W[i] & 0x7c00) == 0x7c00) return false;
+  return true;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// block image
+// ---------------------------------------------------------------------------
+static gbb_status check_bits(const uint8_t* bits, int N, int K) {
+  if (!bits) return fail(GBB_E_ARG, "bits is NULL");
+  if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
+  if (N % kBlockRows || K % kGroup)
+    return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);
+  const size_t nblk = size_t(N / kBlockRows) * size_t(K / kGroup);
+  for (size_t i = 0; i < nblk; ++i)
+    if (!valid_bits(bits[i]))
+      return fail(GBB_E_BITS, "block %zu has bitwidth %d, not in {1,2,3,4,6,8}", i, int(bits[i]));
+  return GBB_OK;
+}
+
+static size_t packed_bytes_unchecked(const uint8_t* bits, int N, int K) {
+  const BlockLayout l = block_layout(N, K);
+  size_t kib = 0;
+  for (size_t i = 0; i < l.nblk; ++i) kib += bits[i];
+  return l.codes_off + 1024 * kib;
+}
+
+// Write one plane of a block: codes q[64][128] (row, column within the block),
+// plane width w, bit shift sh, into dst (w KiB).
+static void write_plane(const uint8_t (*q)[128], int w, int sh, uint8_t* dst) {
+  const int npair = 16 / w;
+  const uint32_t mask = (1u << w) - 1u;
+  for (int lane = 0; lane < 64; ++lane) {
+    for (int d = 0; d < 4 * w; ++d) {
+      uint32_t word = 0;
+      for (int i = 0; i < npair; ++i) {
+        const int P = d * npair + i, u = P >> 2, p = P & 3;
+        const int rt = u >> 2, kt = u & 3;
+        const int row = 16 * rt + (lane & 15);
+        const int col = 32 * kt + 8 * (lane >> 4) + 2 * p;
+        word |= ((uint32_t(q[row][col]) >> sh) & mask) << (w * i);
+        word |= ((uint32_t(q[row][col + 1]) >> sh) & mask) << (16 + w * i);
+      }
+      std::memcpy(dst + 1024 * (d >> 2) + 16 * lane + 4 * (d & 3), &word, 4);
+    }
+  }
+}
+
+}  // namespace gbb
+
+using namespace gbb;
+
+extern "C" const char* gbb_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" size_t gbb_packed_bytes(const uint8_t* bits, int N, int K) {
+  if (check_bits(bits, N, K) != GBB_OK) return 0;
+  return packed_bytes_unchecked(bits, N, K);
+}
+
+extern "C" gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits,
+                                      uint16_t* scale, uint16_t* zero, unsigned flags, void* image,
+                                      size_t image_cap) {
+  gbb_status st = check_bits(bits, N, K);
+  if (st != GBB_OK) return st;
+  if (!W || !image) return fail(GBB_E_ARG, "W and image must not be NULL");
+  if (flags & ~GBB_PACK_GIVEN_SZ) return fail(GBB_E_ARG, "unknown flag bits 0x%x", flags);
+  const bool given = flags & GBB_PACK_GIVEN_SZ;
+  if (given && (!scale || !zero)) return fail(GBB_E_ARG, "GBB_PACK_GIVEN_SZ needs scale and zero");
+  const size_t need = packed_bytes_unchecked(bits, N, K);
+  if (image_cap < need) return fail(GBB_E_SPACE, "image needs %zu bytes, capacity %zu", need, image_cap);
+  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+
+  const int nbr = N / kBlockRows, nbc = K / kGroup, G = nbc;
+  if (given) {
+    for (size_t r = 0; r < size_t(N); ++r)
+      for (int g = 0; g < G; ++g) {
+        const int b = bits[(r / kBlockRows) * nbc + g];
+        const double s = half_to_double(scale[r * G + g]), z = half_to_double(zero[r * G + g]);
+        if (!(s > 0) || !std::isfinite(s))
+          return fail(GBB_E_ARG, "given scale of row %zu group %d is not finite and > 0", r, g);
+        if (!(z >= 0 && z <= double((1 << b) - 1) && z == std::floor(z)))
+          return fail(GBB_E_BITS, "given zero of row %zu group %d is not an integer in [0, 2^b-1]", r, g);
+      }
+  }
+
+  const BlockLayout l = block_layout(N, K);
+  uint8_t* img = static_cast<uint8_t*>(image);
+  std::memset(img, 0, l.codes_off);
+  std::vector<size_t> kib(l.nblk + 1, 0);
+  for (size_t i = 0; i < l.nblk; ++i) kib[i + 1] = kib[i] + bits[i];
+
+  BlockHeader h{};
+  h.magic = kMagicBlocks;
+  h.version = kVersion;
+  h.N = uint32_t(N);
+  h.K = uint32_t(K);
+  h.nbr = uint32_t(nbr);
+  h.nbc = uint32_t(nbc);
+  h.bits_off = l.bits_off;
+  h.offs_off = l.offs_off;
+  h.sz_off = l.sz_off;
+  h.codes_off = l.codes_off;
+  h.codes_bytes = 1024 * kib[l.nblk];
+  std::memcpy(img, &h, sizeof h);
+  std::memcpy(img + l.bits_off, bits, l.nblk);
+  for (size_t i = 0; i <= l.nblk; ++i) {
+    const uint32_t o = uint32_t(kib[i]);
+    std::memcpy(img + l.offs_off + 4 * i, &o, 4);
+  }
+
+  parallel_for(long(l.nblk), [&](long blk) {
+    const int br = int(blk / nbc), bc = int(blk % nbc);
+    const int b = bits[blk];
+    const double levels = double((1 << b) - 1);
+    uint8_t q[64][128];
+    double v[128];
+    for (int r = 0; r < 64; ++r) {
+      const size_t row = size_t(br) * 64 + r;
+      const uint16_t* src = W + row * size_t(K) + size_t(bc) * 128;
+      for (int k = 0; k < 128; ++k) v[k] = half_to_double(src[k]);
+      GroupQ gq;
+      if (given) {
+        gq.s16 = scale[row * G + bc];
+        gq.z16 = zero[row * G + bc];
+        gq.s = half_to_double(gq.s16);
+        gq.z = half_to_double(gq.z16);
+      } else {
+        gq = asym_scale_zero(v, 128, levels);
+        if (scale) scale[row * G + bc] = gq.s16;
+        if (zero) zero[row * G + bc] = gq.z16;
+      }
+      for (int k = 0; k < 128; ++k) q[r][k] = asym_code(v[k], gq, levels);
+      const uint32_t e = uint32_t(gq.s16) | (uint32_t(gq.z16) << 16);
+      std::memcpy(img + l.sz_off + 256 * size_t(blk) + 4 * r, &e, 4);
+    }
+    uint8_t* dst = img + l.codes_off + 1024 * kib[blk];
+    const int w0 = plane0_width(b), w1 = plane1_width(b);
+    write_plane(q, w0, 0, dst);
+    if (w1) write_plane(q, w1, w0, dst + 1024 * w0);
+  });
+  return GBB_OK;
+}
+
+extern "C" gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K) {
+  if (!image) return fail(GBB_E_ARG, "image is NULL");
+  if (image_bytes < 64) return fail(GBB_E_FORMAT, "image shorter than its header");
+  BlockHeader h;
+  std::memcpy(&h, image, sizeof h);
+  if (h.magic != kMagicBlocks || h.version != kVersion) return fail(GBB_E_FORMAT, "not a version-1 block image");
+  if (int(h.N) != N || int(h.K) != K) return fail(GBB_E_FORMAT, "image is %ux%u, call says %dx%d", h.N, h.K, N, K);
+  const BlockLayout l = block_layout(N, K);
+  if (h.bits_off != l.bits_off || h.offs_off != l.offs_off || h.sz_off != l.sz_off || h.codes_off != l.codes_off)
+    return fail(GBB_E_FORMAT, "section offsets do not match the layout for %dx%d", N, K);
+  if (image_bytes < h.codes_off + h.codes_bytes) return fail(GBB_E_FORMAT, "image truncated");
+  return GBB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// W4/W8 image
+// ---------------------------------------------------------------------------
+static gbb_status check_w48(int N, int K, const int32_t* rows8, int n8) {
+  if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
+  if (K % kGroup) return fail(GBB_E_SHAPE, "K must be a multiple of 128 (K=%d)", K);
+  if (n8 < 0 || n8 > N) return fail(GBB_E_SHAPE, "n8=%d outside [0, N=%d]", n8, N);
+  if (n8 > 0 && !rows8) return fail(GBB_E_ARG, "rows8 is NULL");
+  for (int i = 0; i < n8; ++i) {
+    if (rows8[i] < 0 || rows8[i] >= N) return fail(GBB_E_SHAPE, "rows8[%d]=%d outside [0, N)", i, rows8[i]);
+    if (i && rows8[i] <= rows8[i - 1]) return fail(GBB_E_SHAPE, "rows8 must be strictly ascending");
+  }
+  return GBB_OK;
+}
+
+extern "C" size_t gbb_w48_packed_bytes(int N, int K, int n8) {
+  if (N <= 0 || K <= 0 || K % kGroup || n8 < 0 || n8 > N) {
+    fail(GBB_E_ARG, "bad shape N=%d K=%d n8=%d", N, K, n8);
+    return 0;
+  }
+  return w48_layout(N, K, n8).total;
+}
+
+extern "C" gbb_status gbb_pack_w48(const uint16_t* W, int N, int K, const int32_t* rows8, int n8,
+                                   uint16_t* scale, uint8_t* zero, void* image, size_t image_cap) {
+  gbb_status st = check_w48(N, K, rows8, n8);
+  if (st != GBB_OK) return st;
+  if (!W || !image) return fail(GBB_E_ARG, "W and image must not be NULL");
+  const W48Layout l = w48_layout(N, K, n8);
+  if (image_cap < l.total) return fail(GBB_E_SPACE, "image needs %zu bytes, capacity %zu", l.total, image_cap);
+  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+
+  const int n4 = N - n8, G = K / kGroup, KT = K / 64;
+  std::vector<int32_t> packed_rows(size_t(16) * (l.T8 + l.T4), -1);
+  {
+    std::vector<char> is8(size_t(N), 0);
+    for (int i = 0; i < n8; ++i) is8[size_t(rows8[i])] = 1;
+    int j8 = 0, j4 = 0;
+    for (int r = 0; r < N; ++r) {
+      if (is8[size_t(r)])
+        packed_rows[size_t(j8++)] = r;
+      else
+        packed_rows[size_t(16) * l.T8 + size_t(j4++)] = r;
+    }
+  }
+  uint8_t* img = static_cast<uint8_t*>(image);
+  std::memset(img, 0, l.total);
+  W48Header h{};
+  h.magic = kMagicW48;
+  h.version = kVersion;
+  h.N = uint32_t(N);
+  h.K = uint32_t(K);
+  h.n8 = uint32_t(n8);
+  h.n4 = uint32_t(n4);
+  h.T8 = uint32_t(l.T8);
+  h.T4 = uint32_t(l.T4);
+  h.rows_off = l.rows_off;
+  h.s_off = l.s_off;
+  h.z_off = l.z_off;
+  h.c8_off = l.c8_off;
+  h.c4_off = l.c4_off;
+  std::memcpy(img, &h, 72);
+  std::memcpy(img + l.rows_off, packed_rows.data(), 4 * packed_rows.size());
+
+  uint16_t* s_sec = reinterpret_cast<uint16_t*>(img + l.s_off);
+  uint8_t* z_sec = img + l.z_off;
+  int8_t* c8 = reinterpret_cast<int8_t*>(img + l.c8_off);
+  uint8_t* c4 = img + l.c4_off;
+
+  // one packed tile of 16 rows per task
+  parallel_for(long(l.T8 + l.T4), [&](long t) {
+    const bool eight = t < l.T8;
+    std::vector<int8_t> q8(eight ? 16 * size_t(K) : 0, 0);
+    std::vector<uint8_t> q4(eight ? 0 : 16 * size_t(K), 0);
+    double v[kGroup];
+    for (int r = 0; r < 16; ++r) {
+      const int row = packed_rows[size_t(16) * t + r];
+      if (row < 0) continue;  // padding: codes 0, scale 0
+      const uint16_t* src = W + size_t(row) * size_t(K);
+      for (int g = 0; g < G; ++g) {
+        for (int k = 0; k < kGroup; ++k) v[k] = half_to_double(src[g * kGroup + k]);
+        uint16_t s16;
+        uint8_t zz = 0;
+        if (eight) {
+          s16 = sym8_scale(v, kGroup);
+          const double s = half_to_double(s16);
+          for (int k = 0; k < kGroup; ++k) q8[size_t(r) * K + g * kGroup + k] = sym8_code(v[k], s);
+        } else {
+          const GroupQ gq = asym_scale_zero(v, kGroup, 15.0);
+          s16 = gq.s16;
+          zz = uint8_t(gq.z);
+          for (int k = 0; k < kGroup; ++k) q4[size_t(r) * K + g * kGroup + k] = asym_code(v[k], gq, 15.0);
+          z_sec[(size_t(t - l.T8) * G + g) * 16 + r] = zz;
+        }
+        s_sec[(size_t(t) * G + g) * 16 + r] = s16;
+        if (scale) scale[size_t(row) * G + g] = s16;
+        if (zero) zero[size_t(row) * G + g] = zz;
+      }
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      for (int lane = 0; lane < 64; ++lane) {
+        const int r = lane & 15, c0 = 64 * kt + 16 * (lane >> 4);
+        if (eight) {
+          int8_t* dst = c8 + (size_t(t) * KT + kt) * 1024 + 16 * lane;
+          for (int e = 0; e < 16; ++e) dst[e] = q8[size_t(r) * K + c0 + e];
+        } else {
+          uint8_t* dst = c4 + (size_t(t - l.T8) * KT + kt) * 512 + 8 * lane;
+          for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < 4; ++i) {
+              const int e = 8 * j + i;
+              dst[4 * j + i] = uint8_t(q4[size_t(r) * K + c0 + e] | (q4[size_t(r) * K + c0 + e + 4] << 4));
+            }
+        }
+      }
+    }
+  });
+  return GBB_OK;
+}

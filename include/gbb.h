@@ -1,0 +1,181 @@
+/*
+ * gbb -- fused dequantize-and-multiply GEMV/GEMM over weight-only quantized
+ * LLM layers, for AMD Instinct MI355X (gfx950).
+ *
+ * Two weight formats:
+ *
+ *  1. Block format.  The weight matrix W [N out][K in] is cut into blocks of
+ *     64 output rows x 128 input columns; every block has one bitwidth
+ *     b in {1,2,3,4,6,8} ("ScaleBITS: Scalable Bitwidth Search for
+ *     Hardware-Aligned Mixed-Precision LLMs", explainer page, section 1.2.2
+ *     "hardware-aligned block partition" and section 4.2 for the bitwidth set).
+ *     Each (row, 128-column group) has an fp16 scale s and zero z; codes are
+ *     q = clamp(rint(w / s) + z, 0, 2^b - 1) and dequantize as (q - z) * s
+ *     ("MixLLM: LLM Quantization with Global Mixed-precision between
+ *     Output-features and Highly-efficient System Design", section 2.1).
+ *
+ *  2. Output-feature mixed format ("W4.4A8", MixLLM page, sections 3.1.1 and
+ *     3.3): a set of salient output rows is quantized 8-bit symmetric, the
+ *     other rows 4-bit asymmetric, both with group 128, and multiplied with
+ *     8-bit symmetric activations by a two-step dequantization: an integer
+ *     product per group, then the two scales.
+ *
+ * Conventions for every entry point:
+ *  - Matrices are row-major.  fp16 values are passed as their 16-bit patterns
+ *    (uint16_t).  y = x . W^T: x is [M][K], y is [M][N].
+ *  - "host" pointers are CPU memory; "device" pointers are GPU memory of the
+ *    current HIP device (hipMalloc or a torch tensor).  The caller owns every
+ *    buffer.  `stream` is a hipStream_t (NULL = the default stream).
+ *  - Device entry points only validate arguments and enqueue kernels on
+ *    `stream`; they never allocate, never synchronize and return before the
+ *    work finishes.  Faults inside kernels are not reported by the call.
+ *  - Nothing throws, aborts or prints.  A negative status is an error; the
+ *    text of the last error of the calling thread is gbb_last_error().
+ *  - Device pointers must be 16-byte aligned; x and y must not overlap.
+ */
+#ifndef GBB_H
+#define GBB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int gbb_status;
+
+enum {
+  GBB_OK = 0,
+  GBB_E_ARG = -1,     /* null pointer, non-positive size, bad flag or option */
+  GBB_E_SHAPE = -2,   /* N % 64 != 0 or K % 128 != 0 (block format), or bad row set */
+  GBB_E_BITS = -3,    /* a bitwidth outside {1,2,3,4,6,8}, or a bad given zero */
+  GBB_E_ALIGN = -4,   /* a device pointer that is not 16-byte aligned */
+  GBB_E_SPACE = -5,   /* an output or workspace capacity that is too small */
+  GBB_E_FORMAT = -6,  /* an image header that does not match the arguments */
+  GBB_E_DEVICE = -7   /* a HIP runtime or launch error */
+};
+
+/* Text of the last non-OK status returned to this thread ("" if none). */
+const char* gbb_last_error(void);
+
+/* Library version: 10000 * major + 100 * minor + patch. */
+int gbb_version(void);
+
+/* ======================================================================== */
+/* Block format                                                             */
+/* ======================================================================== */
+
+/* Byte size of the packed image for an N x K matrix with the per-block
+ * bitwidth map `bits` (host, uint8 [N/64][K/128], block-row major).  The size
+ * is a 64-byte header, then 256-byte aligned sections: one byte per block,
+ * 4 * (blocks + 1) bytes of offsets, 256 bytes of scale/zero per block and
+ * 64 * 128 * b / 8 = 1024 * b bytes of codes per block.  Returns 0 on a bad
+ * argument (see gbb_last_error). */
+size_t gbb_packed_bytes(const uint8_t* bits, int N, int K);
+
+#define GBB_PACK_GIVEN_SZ 1u  /* use the caller's scale/zero instead of min/max */
+
+/* Quantize and pack (host, synchronous, deterministic; may use several CPU
+ * threads).
+ *   W      host fp16 [N][K].
+ *   bits   host uint8 [N/64][K/128], each in {1,2,3,4,6,8}.
+ *   scale, zero  host fp16 [N][K/128].  Without GBB_PACK_GIVEN_SZ they are
+ *          outputs (may be NULL): per (row, group) s = fp16((max - min) /
+ *          (2^b - 1)) and z = clamp(rint(-min / s), 0, 2^b - 1), decisions in
+ *          fp64, round-half-even (MixLLM page, section 2.1, with min/max
+ *          ranges).  With GBB_PACK_GIVEN_SZ they are inputs (e.g. scales from
+ *          a clipping search): s must be finite and > 0, z an integer in
+ *          [0, 2^b - 1].
+ *   image  host output of gbb_packed_bytes(bits, N, K) bytes (image_cap).
+ * Codes q = clamp(rint(w / s) + z, 0, 2^b - 1).  The image can be copied to
+ * the device as is and shared by any number of streams. */
+gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits,
+                           uint16_t* scale, uint16_t* zero, unsigned flags,
+                           void* image, size_t image_cap);
+
+/* Check a host copy of an image header against N and K (GBB_E_FORMAT). */
+gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
+
+/* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M); may be 0.  The
+ * workspace must be zero-filled once before its first use; every call leaves
+ * it zero-filled again.  Calls that run at the same time need separate
+ * workspaces. */
+size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
+
+/* y = x . dequant(W)^T over a packed block image (ScaleBITS explainer page,
+ * section 3.2: the weight is dequantized inside the matrix product, one
+ * bitwidth per 64x128 block).
+ *   image  device copy of gbb_pack_blocks' output for this N, K.
+ *   x      device fp16 [M][K];  y device fp16 [M][N] (fp32 accumulation,
+ *          round-to-nearest-even at the end).
+ *   M >= 1.  M <= 32 runs the decode kernel (weights streamed once, matrix
+ *   cores for the dot products); larger M runs the tiled prefill kernel.
+ *   workspace/ws_bytes  device memory of gbb_gemm_mixed_w_workspace(N, K, M)
+ *          bytes (NULL allowed when that is 0). */
+gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
+                            uint16_t* y, int M, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Same as gbb_gemm_mixed_w with the kernel chosen by `path`: 0 = automatic,
+ * 1 = decode kernel (requires M <= 32), 2 = prefill kernel.  For tests. */
+gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t* x,
+                                 uint16_t* y, int M, void* workspace, size_t ws_bytes,
+                                 int path, void* stream);
+
+/* Debug exports over a device image, for bit-exactness tests.
+ *   gbb_unpack_codes: q device uint8 [N][K], the codes.
+ *   gbb_dequant: w32 device fp32 [N][K] = (q - z) * s (exact), and/or w16
+ *   device fp16 [N][K] = its round-to-nearest-even (either may be NULL). */
+gbb_status gbb_unpack_codes(const void* image, int N, int K, uint8_t* q, void* stream);
+gbb_status gbb_dequant(const void* image, int N, int K, float* w32, uint16_t* w16,
+                       void* stream);
+
+/* ======================================================================== */
+/* Output-feature mixed format, W8 (symmetric) / W4 (asymmetric) x A8       */
+/* ======================================================================== */
+
+/* Byte size of the W4/W8 image for N x K with n8 8-bit rows (0 on error). */
+size_t gbb_w48_packed_bytes(int N, int K, int n8);
+
+/* Quantize and pack (host, synchronous, deterministic).
+ *   W      host fp16 [N][K], K % 128 == 0.
+ *   rows8  host int32 [n8], strictly ascending output rows that get 8-bit
+ *          symmetric codes (s = fp16(max|w| / 127), q = clamp(rint(w / s),
+ *          -127, 127)); every other row gets 4-bit asymmetric codes as in
+ *          gbb_pack_blocks (MixLLM page, sections 3.1.1 and 3.1.2).
+ *   scale  host fp16 [N][K/128] output in original row order (may be NULL).
+ *   zero   host uint8 [N][K/128] output, 0 for 8-bit rows (may be NULL).
+ *   image  host output of gbb_w48_packed_bytes(N, K, n8) bytes. */
+gbb_status gbb_pack_w48(const uint16_t* W, int N, int K, const int32_t* rows8, int n8,
+                        uint16_t* scale, uint8_t* zero, void* image, size_t image_cap);
+
+/* 8-bit symmetric activation quantization (MixLLM page, section 3.1.2):
+ * per token (ga == K) or per group of 128 columns (ga == 128).  Decisions in
+ * fp32: s = fp16(max|x| / 127) (1 if the group is all zero),
+ * xq = clamp(rint(x / s), -127, 127).
+ *   x  device fp16 [M][K];  xq device int8 [M][K];  xs device fp16 [M][K/ga]. */
+gbb_status gbb_quant_act_i8(const uint16_t* x, int M, int K, int ga, int8_t* xq,
+                            uint16_t* xs, void* stream);
+
+/* y = dequant(xq) . dequant(W)^T by two-step dequantization (MixLLM page,
+ * section 3.3): per 128-group an exact int32 product xq . (q - z) on the int8
+ * matrix cores, then scaled by s_a * s_w and accumulated in fp32; each output
+ * is written straight to its original row (fused scatter).
+ *   image  device copy of gbb_pack_w48's output.
+ *   xq, xs as produced by gbb_quant_act_i8 with the same ga (K or 128).
+ *   y      device fp16 [M][N]. */
+gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, const int8_t* xq,
+                          const uint16_t* xs, int ga, uint16_t* y, int M, void* stream);
+
+/* Debug export: the int32 group products acc[m][n][g] = sum over the group of
+ * xq[m][k] * (q[n][k] - z[n][g]) for every original row n (device int32
+ * [M][N][K/128]), for bit-exact tests on small shapes. */
+gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq,
+                             int32_t* acc, int M, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBB_H */

@@ -83,12 +83,27 @@ def quantize_blocks(W16: np.ndarray, bits: np.ndarray):
         v = W16[r0:r0 + 1024].astype(np.float64).reshape(-1, G, GROUP)
         levels = (2.0 ** gb[r0:r0 + 1024] - 1.0)
         sc, z = choose_scale_zero(v.min(axis=2), v.max(axis=2), levels)
-        s = sc.astype(np.float64)[:, :, None]
-        code = np.clip(np.rint(v / s) + z[:, :, None], 0, levels[:, :, None])
-        q[r0:r0 + 1024] = code.reshape(-1, K).astype(np.uint8)
+        q[r0:r0 + 1024] = _codes(v, sc, z, levels).reshape(-1, K)
         s16[r0:r0 + 1024] = sc
         z16[r0:r0 + 1024] = z.astype(np.float16)
     return q, s16, z16
+
+
+def _codes(v, s16, z, levels):
+    """q = clamp(rint(v / s) + z, 0, levels) per group (fp64)."""
+    s = np.asarray(s16, np.float16).astype(np.float64)[:, :, None]
+    code = np.clip(np.rint(v / s) + np.asarray(z, np.float64)[:, :, None], 0, levels[:, :, None])
+    return code.astype(np.uint8)
+
+
+def codes_with(W16: np.ndarray, bits: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """Codes of W for given per-(row, group) scales and zeros (for example
+    scales from a clipping search), with the same rounding as quantize_blocks."""
+    W16 = np.asarray(W16, np.float16)
+    N, K = W16.shape
+    gb = group_bits(bits, N, K)
+    v = W16.astype(np.float64).reshape(N, K // GROUP, GROUP)
+    return _codes(v, s16, np.asarray(z16, np.float64), 2.0 ** gb - 1.0).reshape(N, K)
 
 
 def dequant_fp32(q: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:

@@ -31,9 +31,9 @@ codes  block i occupies 1024 * b_i bytes, split into planes of width
 
 W4/W8 image ("GW48")
 --------------------
-header (64 B): u32 magic 0x38345747, u32 version 1, u32 N, u32 K, u32 n8,
-u32 n4, u32 T8 = ceil(n8/16), u32 T4 = ceil(n4/16), u64 offsets of rows, s,
-z, codes8, codes4 (each 256-byte aligned, rows at 256).
+header (first 72 B): u32 magic 0x38345747, u32 version 1, u32 N, u32 K,
+u32 n8, u32 n4, u32 T8 = ceil(n8/16), u32 T4 = ceil(n4/16), u64 offsets of
+rows, s, z, codes8, codes4 (each 256-byte aligned, rows at 256).
 rows   i32 [16 (T8 + T4)]: original output row of each packed row (8-bit rows
        first, then 4-bit rows, each ascending); -1 for padding rows.
 s      fp16 [T8 + T4][K/128][16]: scale of packed row 16 t + r in group g.
@@ -156,7 +156,7 @@ def read_w48_image(buf) -> dict:
     magic, ver, N, K, n8, n4, T8, T4 = (int(v) for v in b[:32].view("<u4"))
     if magic != GW48_MAGIC or ver != 1 or n8 + n4 != N:
         raise ValueError("not a version-1 W4/W8 image")
-    rows_off, s_off, z_off, c8_off, c4_off = (int(v) for v in b[24 + 8:24 + 8 + 40].view("<u8"))
+    rows_off, s_off, z_off, c8_off, c4_off = (int(v) for v in b[32:72].view("<u8"))
     G, KT = K // 128, K // 64
     rows = b[rows_off:rows_off + 4 * 16 * (T8 + T4)].view("<i4")
     s = b[s_off:s_off + 2 * (T8 + T4) * G * 16].view("<u2").reshape(T8 + T4, G, 16)

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Bars: codes and int32 group products bit-exact; dequantized weights bit-exact
+against the oracle's fp32 (q - z) * s; one-hot activations give fp16(w')
+exactly on every path; fp16 outputs within ||y - y_ref||_inf / ||y_ref||_inf
+<= 2e-3 of the fp64 oracle.  Full-size workloads are checked on sampled output
+rows in the same launch configuration the benchmark uses.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import blockquant as bq
+from oracle import w48 as ow48
+
+torch = pytest.importorskip("torch")
+gbb = pytest.importorskip("gemm_block_bit_amd")
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+ALLOWED = (1, 2, 3, 4, 6, 8)
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def to_dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if t.dtype == torch.uint16:
+        t = t.view(torch.float16)
+    return t.to(dev())
+
+
+def small(N, K, seed):
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((N, K))).astype(np.float16)
+    W[g.random((N, K)) < 0.005] *= np.float16(10)
+    return W
+
+
+def rand_x(M, K, seed):
+    return np.random.default_rng(1000 + seed).standard_normal((M, K)).astype(np.float16)
+
+
+def packed(W, bits):
+    img, s, z = gbb.pack_blocks(W, bits)
+    return to_dev(img)
+
+
+def rel_err(y_gpu, y_ref):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y))
+    return bq.rel_inf_err(y, y_ref)
+
+
+# ----------------------------------------------------------------------------
+# bit-exact unpack / dequant
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,seed", [(64, 128, 0), (192, 384, 1), (448, 1280, 2)])
+def test_unpack_dequant_bit_exact(N, K, seed):
+    W = small(N, K, seed)
+    bits = synth.random_bitmap(N, K, ALLOWED, seed)
+    img = packed(W, bits)
+    q, s16, z16 = bq.quantize_blocks(W, bits)
+    qg = gbb.unpack_codes(img, N, K).cpu().numpy()
+    assert np.array_equal(qg, q)
+    w32, w16 = gbb.dequant(img, N, K)
+    ref = bq.dequant_fp32(q, s16, z16)
+    assert np.array_equal(w32.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(w16.cpu().numpy().view(np.uint16), bq.fp16_rne(ref).view(np.uint16))
+
+
+def test_unpack_linear_4096_bit_exact():
+    W, bits, _ = synth.linear_4096()
+    img = packed(W, bits)
+    q, s16, z16 = bq.quantize_blocks(W, bits)
+    assert np.array_equal(gbb.unpack_codes(img, 4096, 4096).cpu().numpy(), q)
+    w32, _ = gbb.dequant(img, 4096, 4096)
+    assert np.array_equal(w32.cpu().numpy().view(np.uint32), bq.dequant_fp32(q, s16, z16).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# one-hot activations: exact on every path
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 16), (1, 32), (2, 1), (2, 200)])
+def test_one_hot_rows_exact(path, M):
+    N, K = 192, 1280
+    W = small(N, K, 3)
+    bits = synth.random_bitmap(N, K, ALLOWED, 3)
+    img = packed(W, bits)
+    ks = np.random.default_rng(M).choice(K, size=M, replace=M > K)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1
+    y = gbb.gemm_mixed_w_path(img, N, K, to_dev(x), path).cpu().numpy()
+    q, s16, z16 = bq.quantize_blocks(W, bits)
+    w16 = bq.dequant_fp16(q, s16, z16)
+    assert np.array_equal(y.view(np.uint16), w16[:, ks].T.view(np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# random activations: 2e-3 of the fp64 oracle
+# ----------------------------------------------------------------------------
+DECODE_CASES = [(64, 128, 1), (128, 256, 3), (192, 384, 5), (1024, 4096, 1), (1024, 4096, 8),
+                (320, 2560, 16), (960, 1408, 17), (512, 4096, 32), (64, 28672, 2)]
+
+
+@pytest.mark.parametrize("N,K,M", DECODE_CASES)
+def test_decode_parity(N, K, M):
+    W = small(N, K, N + K)
+    bits = synth.random_bitmap(N, K, ALLOWED, N + M)
+    x = rand_x(M, K, M)
+    img = packed(W, bits)
+    ref = bq.reference_gemm(x, W, bits)
+    xd = to_dev(x)
+    for _ in range(3):                      # split-K counters must reset between calls
+        y = gbb.gemm_mixed_w_path(img, N, K, xd, 1)
+        assert rel_err(y, ref) <= TOL
+
+
+PREFILL_CASES = [(64, 128, 33), (192, 384, 100), (128, 1280, 257), (320, 512, 129), (256, 4096, 600)]
+
+
+@pytest.mark.parametrize("N,K,M", PREFILL_CASES)
+def test_prefill_parity(N, K, M):
+    W = small(N, K, N * 7 + K)
+    bits = synth.random_bitmap(N, K, ALLOWED, N + 2 * M)
+    x = rand_x(M, K, M)
+    img = packed(W, bits)
+    y = gbb.gemm_mixed_w_path(img, N, K, to_dev(x), 2)
+    assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
+
+
+def test_auto_path_and_empty_batch():
+    N, K = 128, 256
+    W = small(N, K, 5)
+    bits = synth.random_bitmap(N, K, ALLOWED, 5)
+    img = packed(W, bits)
+    for M in (1, 32, 33):
+        x = rand_x(M, K, M)
+        y = gbb.gemm_mixed_w(img, N, K, to_dev(x))
+        assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
+    y0 = gbb.gemm_mixed_w(img, N, K, torch.empty((0, K), dtype=torch.float16, device=dev()))
+    assert y0.shape == (0, N)
+
+
+def test_device_argument_errors():
+    N, K = 128, 256
+    W = small(N, K, 6)
+    img = packed(W, synth.uniform_bitmap(N, K, 4))
+    x = torch.zeros((3, K + 8), dtype=torch.float16, device=dev())
+    L = gbb.lib()
+    y = torch.empty((3, N), dtype=torch.float16, device=dev())
+    # x shifted by one element is not 16-byte aligned
+    assert L.gbb_gemm_mixed_w(img.data_ptr(), N, K, x.data_ptr() + 2, y.data_ptr(), 3, None, 0, None) == -4
+    assert L.gbb_gemm_mixed_w(img.data_ptr(), N, 200, x.data_ptr(), y.data_ptr(), 3, None, 0, None) == -2
+    need = gbb.gemm_mixed_w_workspace(1024, 4096, 1)
+    assert need > 0
+    img2 = packed(small(1024, 4096, 1), synth.uniform_bitmap(1024, 4096, 2))
+    x1 = torch.zeros((1, 4096), dtype=torch.float16, device=dev())
+    y1 = torch.empty((1, 1024), dtype=torch.float16, device=dev())
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    assert L.gbb_gemm_mixed_w(img2.data_ptr(), 1024, 4096, x1.data_ptr(), y1.data_ptr(), 1, ws.data_ptr(),
+                              need - 16, None) == -5
+    assert L.gbb_gemm_mixed_w(img2.data_ptr(), 1024, 4096, x1.data_ptr(), y1.data_ptr(), 1, None, 0, None) == -1
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ----------------------------------------------------------------------------
+@functools.lru_cache(maxsize=4)
+def workload(name, i):
+    if name == "8b":
+        p, W, bits = synth.llama3_8b_proj(i)
+    elif name == "70b":
+        p, W, bits = synth.llama3_70b_proj(i)
+    else:
+        p, W, bits = synth.prefill_70b_mlp(i)
+    img, _, _ = gbb.pack_blocks(W, bits)
+    return p, W, bits, to_dev(img)
+
+
+def sample_rows(N, seed, n=48):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 63, 64, N - 1], g.choice(N, n, replace=False)]))
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_llama3_8b_layer_decode(i):
+    p, W, bits, img = workload("8b", i)
+    assert abs(synth.mean_bits(bits) - 3.1) < 0.01
+    for M in (1, 8):
+        x = synth.activations(M, p.K, synth.WL_LLAMA3_8B, i)
+        y = gbb.gemm_mixed_w(img, p.N, p.K, to_dev(x)).cpu().numpy()
+        rows = sample_rows(p.N, i)
+        ref = bq.reference_rows(x, W, bits, rows)
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+@pytest.mark.parametrize("i", [1, 4, 6])
+def test_llama3_70b_layer_decode(i):
+    p, W, bits, img = workload("70b", i)
+    assert abs(synth.mean_bits(bits) - 2.1) < 0.01
+    for M in (1, 8, 32):
+        x = synth.activations(M, p.K, synth.WL_LLAMA3_70B, i)
+        y = gbb.gemm_mixed_w(img, p.N, p.K, to_dev(x)).cpu().numpy()
+        rows = sample_rows(p.N, 10 + i, 24)
+        ref = bq.reference_rows(x, W, bits, rows)
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+@pytest.mark.parametrize("i", [0, 1])
+def test_prefill_70b_mlp_m2048(i):
+    p, W, bits, img = workload("prefill", i)
+    x = synth.prefill_x(2048, p.K, i)
+    y = gbb.gemm_mixed_w(img, p.N, p.K, to_dev(x)).cpu().numpy()
+    rows = sample_rows(p.N, 20 + i, 12)
+    ref = bq.reference_rows(x, W, bits, rows)
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+# ----------------------------------------------------------------------------
+# W4/W8 x A8
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,ga", [(1, 256, None), (5, 384, None), (7, 512, 128), (64, 8192, None), (33, 4096, 128)])
+def test_act_quant_bit_exact(M, K, ga):
+    x = rand_x(M, K, M + K)
+    x[0, :128] = 0
+    if M > 2:
+        x[2] = 0
+    xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+    A, s = ow48.quant_act(x, ga)
+    assert np.array_equal(xq.cpu().numpy(), A)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint16), s.view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K,M,frac", [(48, 256, 3, 0.1), (200, 384, 40, 0.1), (64, 128, 17, 0.0),
+                                        (40, 256, 70, 1.0), (300, 1024, 130, 0.2)])
+def test_w48_group_acc_bit_exact(N, K, M, frac):
+    W = small(N, K, N + M)
+    rows8 = synth.salient_rows_by_l2(W, frac) if frac < 1 else np.arange(N, dtype=np.int32)
+    img, _, _ = gbb.pack_w48(W, rows8)
+    x = rand_x(M, K, N)
+    xq, _ = gbb.quant_act_i8(to_dev(x))
+    acc = gbb.w48_group_acc(to_dev(img), N, K, rows8.size, xq).cpu().numpy()
+    qd = ow48.quantize_w48(W, rows8)
+    A, _ = ow48.quant_act(x)
+    ref = np.zeros((M, N, K // 128), np.int64)
+    if qd["rows8"].size:
+        ref[:, qd["rows8"]] = ow48.group_acc(A, qd["q8"].astype(np.int64))
+    if qd["rows4"].size:
+        Wz = qd["q4"].astype(np.int64) - np.repeat(qd["z4"].astype(np.int64), 128, axis=1)
+        ref[:, qd["rows4"]] = ow48.group_acc(A, Wz)
+    assert np.array_equal(acc.astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("N,K,M,ga", [(48, 256, 3, None), (200, 384, 40, None), (300, 1024, 130, None),
+                                      (300, 1024, 77, 128), (1000, 4096, 1, None)])
+def test_w48_parity(N, K, M, ga):
+    W = small(N, K, 3 * N + M)
+    rows8 = synth.salient_rows_by_l2(W, 0.1)
+    img, _, _ = gbb.pack_w48(W, rows8)
+    x = rand_x(M, K, 2 * N)
+    xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+    y = gbb.gemm_w48a8(to_dev(img), N, K, rows8.size, xq, xs, ga)
+    ref = ow48.reference(x, W, rows8, act_group=ga)
+    assert rel_err(y, ref) <= TOL
+
+
+@functools.lru_cache(maxsize=1)
+def w44a8_image():
+    W, rows8 = synth.w44a8_28672x8192()
+    img, _, _ = gbb.pack_w48(W, rows8)
+    return W, rows8, to_dev(img)
+
+
+@pytest.mark.parametrize("M", [32, 512, 4096])
+def test_w44a8_28672x8192(M):
+    W, rows8, img = w44a8_image()
+    assert rows8.size == 2867
+    x = synth.activations(M, 8192, synth.WL_W44A8, 0)
+    xq, xs = gbb.quant_act_i8(to_dev(x))
+    y = gbb.gemm_w48a8(img, 28672, 8192, rows8.size, xq, xs).cpu().numpy()
+    rows = np.unique(np.concatenate([rows8[:8], sample_rows(28672, M, 16)]))
+    qd = ow48.quantize_w48(W[rows], np.nonzero(np.isin(rows, rows8))[0])
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0], quant=qd)
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
