@@ -230,7 +230,10 @@ DecodePlan decode_plan(int N, int K, int M) {
   p.seg_len = (nbc + nseg - 1) / nseg;
   p.nseg = (nbc + p.seg_len - 1) / p.seg_len;
   if (p.nseg > 1) {
-    p.ctr_bytes = align256(size_t(p.nrg) * 4);
+    // the counters sit in a fixed region at the start of every workspace, so
+    // one zero-filled buffer serves calls of any shape: partial sums of one
+    // call never land where another call's counters live
+    p.ctr_bytes = kCounterBytes;
     p.part_bytes = size_t(p.nseg) * size_t(M) * size_t(N) * 4;
   } else {
     p.ctr_bytes = p.part_bytes = 0;

@@ -25,6 +25,9 @@ struct BlockImageView {
 };
 
 // Decode (M <= 32) launch plan: row groups of 4 block rows x K segments.
+// Split-K calls keep one u32 counter per row group in the first
+// kCounterBytes of the workspace (N up to 4 194 304 rows).
+constexpr size_t kCounterBytes = 65536;
 struct DecodePlan {
   int nseg, seg_len, nrg;
   size_t part_bytes, ctr_bytes;

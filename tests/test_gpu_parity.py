@@ -135,6 +135,18 @@ def test_prefill_parity(N, K, M):
     assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
 
 
+def test_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves split-K calls of different shapes: a
+    call with few row groups followed by one with more than 64 of them."""
+    ws = torch.zeros(gbb.gemm_mixed_w_workspace(16640, 1024, 8) + (1 << 20), dtype=torch.uint8, device=dev())
+    for N, K, M in ((256, 4096, 8), (16640, 1024, 1), (256, 4096, 8), (16640, 1024, 8)):
+        W = small(N, K, N)
+        bits = synth.random_bitmap(N, K, ALLOWED, K)
+        x = rand_x(M, K, N + M)
+        y = gbb.gemm_mixed_w_path(packed(W, bits), N, K, to_dev(x), 1, workspace=ws)
+        assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
+
+
 def test_auto_path_and_empty_batch():
     N, K = 128, 256
     W = small(N, K, 5)
