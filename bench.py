@@ -1,0 +1,332 @@
+"""Benchmark of the fused dequantize-and-multiply path on one MI355X.
+
+Headline (one JSON line): decode (M = 1) weight GB/s over Llama-3-8B-shaped
+decoder layers -- q, k, v, o, gate, up, down at 64x128 blocks with bitwidths
+from {1,2,3,4,6,8} (mean 3.1) -- against the 8 TB/s HBM peak.  One step is
+one token through a stack of distinct layer copies whose packed weights
+(732 MB) exceed the 256 MiB Infinity Cache, so every weight byte comes from
+HBM.  The step is replayed from a HIP graph of its 56 launches.
+
+Also reported: M = 8 on the same layers, the 70B-shaped layer at M = 1, the
+M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
+an fp16 library GEMM on the dequantized weights for context, the W4.4A8 layer
+(M = 32, 512, 4096) and the oracle timed on the host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+LAYER_COPIES_8B = 8       # 8 x 91.5 MB > 512 MiB
+LAYER_COPIES_70B = 3      # 3 x 252 MB
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes(bits: np.ndarray) -> int:
+    """Algorithmic bytes of one packed matrix: codes (1024 b per 64x128
+    block), 256 B of fp16 scale/zero per block, 1 B bitwidth and 4 B offset
+    per block (+4)."""
+    nblk = bits.size
+    return 1024 * int(bits.astype(np.int64).sum()) + 256 * nblk + nblk + 4 * (nblk + 1)
+
+
+class DecodeLayerSet:
+    """R copies of one decoder layer's packed projections on the GPU, with
+    their activations, outputs and one shared split-K workspace."""
+
+    def __init__(self, torch, gbb, synth, gen, copies, M, dev):
+        self.torch, self.gbb = torch, gbb
+        self.M = M
+        self.projs = []
+        host = []
+        for i in range(7):
+            p, W, bits = gen(i)
+            img, _, _ = gbb.pack_blocks(W, bits)
+            host.append((p, img, bits))
+            del W
+        self.images = [[torch.from_numpy(img).to(dev) for (_, img, _) in host] for _ in range(copies)]
+        self.shapes = [(p.N, p.K) for (p, _, _) in host]
+        self.names = [p.name for (p, _, _) in host]
+        self.bytes = [weight_bytes(b) for (_, _, b) in host]
+        self.layer_bytes = sum(self.bytes)
+        self.copies = copies
+        g = np.random.default_rng(7)
+        self.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
+        self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (N, _) in self.shapes]
+        ws = max(gbb.gemm_mixed_w_workspace(N, K, M) for (N, K) in self.shapes)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        # raw arguments for direct C calls (no per-call Python marshalling)
+        self.fn = gbb.lib().gbb_gemm_mixed_w
+
+    def launches(self):
+        for r in range(self.copies):
+            for i, (N, K) in enumerate(self.shapes):
+                yield r, i, N, K
+
+    def step(self, stream_handle, events=None):
+        fn, ws = self.fn, self.ws
+        for r, i, N, K in self.launches():
+            if events is not None:
+                events[r][i][0].record()
+            st = fn(self.images[r][i].data_ptr(), N, K, self.x[i].data_ptr(), self.y[i].data_ptr(), self.M,
+                    ws.data_ptr(), ws.numel(), stream_handle)
+            if st:
+                raise RuntimeError(self.gbb.lib().gbb_last_error().decode())
+            if events is not None:
+                events[r][i][1].record()
+
+
+def time_graph(torch, fn, steps, warmup):
+    """Capture fn() in a HIP graph, replay warmup + steps times, return
+    seconds per step over the timed replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()          # eager warm run outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3 / steps, wall / steps, graph
+
+
+def time_eager(torch, fn, reps, warmup):
+    """Seconds per call of fn() from events around reps back-to-back calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads, no cpu baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the fused dequant-GEMM path has no multi-GPU component here "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_block_bit_amd as gbb
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+
+    # ---------------- headline: Llama-3-8B layers, decode M = 1 ----------------
+    log("packing Llama-3-8B-shaped layer (7 projections)")
+    L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
+    log(f"layer weight bytes {L8.layer_bytes / 1e6:.1f} MB x {L8.copies} copies")
+    h = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    sec, wall, _ = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
+    total_bytes = L8.layer_bytes * L8.copies
+    value = total_bytes / sec / 1e9
+    log(f"decode M=1: {sec * 1e6:.1f} us/step, {value:.0f} GB/s")
+
+    # per-launch events over the same timed work (eager launches, one stream)
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)] for _ in range(L8.copies)]
+    durs = np.zeros((args.steps, L8.copies, 7))
+    for _ in range(args.warmup):
+        L8.step(h())
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        L8.step(h(), ev)
+        torch.cuda.synchronize()
+        for r in range(L8.copies):
+            for i in range(7):
+                durs[s, r, i] = ev[r][i][0].elapsed_time(ev[r][i][1]) * 1e3   # us
+    mean_us = float(durs.mean())
+    mean_bytes = float(np.mean(L8.bytes))
+    per_proj = {}
+    for i, n in enumerate(L8.names):
+        d = float(durs[:, :, i].mean())
+        per_proj[n] = {"us": round(d, 2), "MB": round(L8.bytes[i] / 1e6, 2),
+                       "GBps": round(L8.bytes[i] / d / 1e3, 1),
+                       "frac_hbm": round(L8.bytes[i] / d / 1e3 / HBM_PEAK_GBS, 3)}
+    achieved = mean_bytes / mean_us / 1e3
+    log(f"decode kernel: mean {mean_us:.2f} us/launch, {achieved:.0f} GB/s; per projection {per_proj}")
+
+    extra = {"per_projection_m1": per_proj,
+             "kernel_sum_us_per_step": round(float(durs.sum(axis=(1, 2)).mean()), 1),
+             "graph_step_us": round(sec * 1e6, 1), "host_wall_us_per_step": round(wall * 1e6, 1)}
+
+    if not args.quick:
+        # ---------------- same layers at M = 8 ----------------
+        L8b = DecodeLayerSet.__new__(DecodeLayerSet)
+        L8b.__dict__.update(L8.__dict__)
+        L8b.M = 8
+        g = np.random.default_rng(8)
+        L8b.x = [torch.from_numpy(g.standard_normal((8, K)).astype(np.float16)).to(dev) for (_, K) in L8.shapes]
+        L8b.y = [torch.empty((8, N), dtype=torch.float16, device=dev) for (N, _) in L8.shapes]
+        ws = max(gbb.gemm_mixed_w_workspace(N, K, 8) for (N, K) in L8.shapes)
+        L8b.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        s8, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)
+        extra["llama3_8b_decode_m8_GBps"] = round(total_bytes / s8 / 1e9, 1)
+        log(f"decode M=8: {total_bytes / s8 / 1e9:.0f} GB/s")
+        del L8b
+
+    # keep the headline layers for the cpu baseline sample; free the device copies
+    host_layer = [(L8.shapes[i], L8.names[i]) for i in range(7)]
+    del L8
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        # ---------------- Llama-3-70B layer, decode M = 1 ----------------
+        log("packing Llama-3-70B-shaped layer")
+        L70 = DecodeLayerSet(torch, gbb, synth, synth.llama3_70b_proj, LAYER_COPIES_70B, 1, dev)
+        s70, _, _ = time_graph(torch, lambda: L70.step(h()), max(10, args.steps // 2), args.warmup)
+        b70 = L70.layer_bytes * L70.copies
+        extra["llama3_70b_decode_m1_GBps"] = round(b70 / s70 / 1e9, 1)
+        extra["llama3_70b_layer_MB"] = round(L70.layer_bytes / 1e6, 1)
+        log(f"70B decode M=1: {b70 / s70 / 1e9:.0f} GB/s")
+        del L70
+        torch.cuda.empty_cache()
+
+        # ---------------- prefill M = 2048 on the 70B MLP ----------------
+        pre = {}
+        for i in range(2):
+            p, W, bits = synth.prefill_70b_mlp(i)
+            img, _, _ = gbb.pack_blocks(W, bits)
+            del W
+            imgd = torch.from_numpy(img).to(dev)
+            x = torch.from_numpy(synth.prefill_x(2048, p.K, i)).to(dev)
+            y = torch.empty((2048, p.N), dtype=torch.float16, device=dev)
+            fl = 2.0 * 2048 * p.N * p.K
+            sp = time_eager(torch, lambda: gbb.gemm_mixed_w(imgd, p.N, p.K, x, out=y), 10, 3)
+            w32, w16 = gbb.dequant(imgd, p.N, p.K)
+            del w32
+            sl = time_eager(torch, lambda: torch.matmul(x, w16.t(), out=y), 10, 3)
+            pre[p.name] = {"N": p.N, "K": p.K, "ms": round(sp * 1e3, 3), "TFLOPs": round(fl / sp / 1e12, 1),
+                           "frac_fp16_peak": round(fl / sp / 1e12 / FP16_PEAK_TFLOPS, 3),
+                           "fp16_library_gemm_on_dequantized_TFLOPs": round(fl / sl / 1e12, 1)}
+            log(f"prefill {p.name}: {fl / sp / 1e12:.0f} TFLOP/s (library fp16 GEMM {fl / sl / 1e12:.0f})")
+            del imgd, x, y, w16
+            torch.cuda.empty_cache()
+        extra["prefill_m2048_70b_mlp"] = pre
+
+        # ---------------- W4.4A8 28672 x 8192 ----------------
+        W, rows8 = synth.w44a8_28672x8192()
+        img, _, _ = gbb.pack_w48(W, rows8)
+        del W
+        imgd = torch.from_numpy(img).to(dev)
+        w48 = {}
+        for M in (32, 512, 4096):
+            x = torch.from_numpy(synth.activations(M, 8192, synth.WL_W44A8, 0)).to(dev)
+            xq, xs = gbb.quant_act_i8(x)
+            y = torch.empty((M, 28672), dtype=torch.float16, device=dev)
+            sw = time_eager(torch, lambda: gbb.gemm_w48a8(imgd, 28672, 8192, rows8.size, xq, xs, out=y), 20, 3)
+            ops = 2.0 * M * 28672 * 8192
+            w48[f"M{M}"] = {"us": round(sw * 1e6, 1), "TOPs": round(ops / sw / 1e12, 1),
+                            "frac_int8_peak": round(ops / sw / 1e12 / INT8_PEAK_TOPS, 3),
+                            "weight_GBps": round(img.size / sw / 1e9, 1)}
+            log(f"w44a8 M={M}: {w48[f'M{M}']}")
+        extra["w44a8_28672x8192"] = w48
+        del imgd
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.quick and not args.no_cpu_baseline:
+        cpu = cpu_baseline(gbb, synth, host_layer)
+
+    out = {
+        "metric": "fused dequant-GEMM: weight GB/s (%HBM peak) at M=1; TFLOP/s (%MFMA) at M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded random weights and activations of Llama-3 layer shapes)",
+        "config": {"workload": "llama3_8b_layer_decode_m1", "layers_per_step": LAYER_COPIES_8B,
+                   "projections": "q,k,v,o,gate,up,down", "M": 1, "block": "64x128",
+                   "bits": "{1,2,3,4,6,8} mean 3.10", "group": 128,
+                   "weight_MB_per_step": round(total_bytes / 1e6, 1), "parallelism": "single GPU"},
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 3), "traffic": None,
+                     "kernel": "decode_kernel<1>", "mean_launch_us": round(mean_us, 3),
+                     "mean_algorithmic_bytes_per_launch": round(mean_bytes)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(gbb, synth, host_layer):
+    """The oracle as it stands -- its own unpacker, exact fp32 dequant and an
+    fp64 product -- over one copy of the headline layer (7 projections, M=1)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import blockquant as bq
+    from oracle import image as oimg
+
+    log("cpu baseline: oracle over one Llama-3-8B-shaped layer at M=1")
+    total_bytes = 0
+    t = 0.0
+    for i in range(7):
+        p, W, bits = synth.llama3_8b_proj(i)
+        img, _, _ = gbb.pack_blocks(W, bits)
+        del W
+        x = np.random.default_rng(7).standard_normal((1, p.K)).astype(np.float16)
+        t0 = time.perf_counter()
+        d = oimg.read_block_image(img)
+        w = bq.dequant_fp32(d["q"], d["s16"], d["z16"])
+        bq.gemm_fp64(x, w)
+        t += time.perf_counter() - t0
+        total_bytes += weight_bytes(bits)
+        del d, w
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(total_bytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one layer copy (7 projections, {total_bytes / 1e6:.1f} MB packed) at M=1: oracle unpack + "
+                      f"fp32 dequant + fp64 GEMV, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

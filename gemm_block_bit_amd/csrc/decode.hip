@@ -20,9 +20,9 @@
 //    s * (C - (1024 * bias_planes + z) * X) = s * sum_k x_k (q_k - z) to the
 //    fp32 accumulator with two fused multiply-adds per output;
 //  * K is split into segments when that is needed to fill the GPU; partial
-//    sums go to fp32 workspace and the last workgroup of each row group (an
-//    agent-scope atomic counter that resets itself) adds them in segment
-//    order, so results are deterministic.
+//    sums go to fp32 workspace through device-scope stores and the last
+//    workgroup of each row group (an atomic counter that resets itself) adds
+//    them in segment order, so results are deterministic.
 #include "device.h"
 #include "internal.h"
 #include "layout.h"
@@ -186,33 +186,41 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     return;
   }
 
+  // Split K: hand the partial sums over through device-scope (sc1) atomic
+  // stores and loads, which are coherent across the XCDs' L2 caches without
+  // writing back or invalidating whole caches.  The barrier waits for every
+  // store of the workgroup to complete before one lane bumps the row group's
+  // counter; the workgroup that brings it to nseg sums the partials in
+  // segment order and resets the counter for the next call.
   if (br < a.nbr) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = 16 * mt + r16;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        *reinterpret_cast<f32x4*>(a.part + (size_t(seg) * a.M + m) * a.N + nrow + 16 * rt) = acc[rt][mt];
+      for (int rt = 0; rt < 4; ++rt) {
+        float* pp = a.part + (size_t(seg) * a.M + m) * a.N + nrow + 16 * rt;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) __hip_atomic_store(pp + v, acc[rt][mt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   __shared__ int s_last;
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.ctr + rg, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(a.ctr + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == uint32_t(a.nseg - 1);
     if (last) __hip_atomic_store(a.ctr + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const int n = rg * 256 + threadIdx.x;
   if (n >= a.N) return;
   for (int m = 0; m < a.M; ++m) {
     float s = 0.0f;
-    for (int sg = 0; sg < a.nseg; ++sg) s += a.part[(size_t(sg) * a.M + m) * a.N + n];
+    for (int sg = 0; sg < a.nseg; ++sg)
+      s += __hip_atomic_load(a.part + (size_t(sg) * a.M + m) * a.N + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.y[size_t(m) * a.N + n] = (_Float16)s;
   }
 }

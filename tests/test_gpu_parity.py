@@ -147,6 +147,59 @@ def test_workspace_reuse_across_shapes():
         assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
 
 
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_split_k_deterministic_over_many_calls(M):
+    """Split-K partial sums cross workgroups (and XCDs) through device-scope
+    memory; the reduction order is fixed, so 200 back-to-back calls must give
+    bit-identical outputs."""
+    N, K = 2048, 8192
+    W = small(N, K, 77)
+    bits = synth.random_bitmap(N, K, ALLOWED, 77)
+    img = packed(W, bits)
+    x = to_dev(rand_x(M, K, 77))
+    assert gbb.gemm_mixed_w_workspace(N, K, M) > 0
+    outs = [gbb.gemm_mixed_w_path(img, N, K, x, 1) for _ in range(200)]
+    first = outs[0].cpu()
+    for o in outs[1:]:
+        assert torch.equal(o.cpu().view(torch.int16), first.view(torch.int16))
+    rows = sample_rows(N, 3, 32)
+    assert bq.rel_inf_err(first.float().numpy()[:, rows], bq.reference_rows(rand_x(M, K, 77), W, bits, rows)) <= TOL
+
+
+def test_graph_replay_matches_eager():
+    """The decode and prefill launches captured in a HIP graph: every replay,
+    with eager work in between, reproduces the eager result bit for bit."""
+    N, K = 1024, 4096
+    W = small(N, K, 88)
+    bits = synth.random_bitmap(N, K, ALLOWED, 88)
+    img = packed(W, bits)
+    xs = [to_dev(rand_x(M, K, 88 + M)) for M in (1, 8, 64)]
+    eager = [gbb.gemm_mixed_w(img, N, K, x) for x in xs]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    ws = torch.zeros(gbb.gemm_mixed_w_workspace(N, K, 8) + 256, dtype=torch.uint8, device=dev())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for x, o in zip(xs, outs):
+            gbb.gemm_mixed_w(img, N, K, x, out=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x, o in zip(xs, outs):
+            gbb.gemm_mixed_w(img, N, K, x, out=o, workspace=ws)
+    for rep in range(5):
+        for o in outs:
+            o.fill_(0)
+        junk = gbb.gemm_mixed_w(img, N, K, xs[1])      # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), rep
+        del junk
+
+
 def test_auto_path_and_empty_batch():
     N, K = 128, 256
     W = small(N, K, 5)
