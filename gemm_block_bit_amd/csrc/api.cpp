@@ -21,7 +21,7 @@ gbb_status device_status(int err, const char* what) {
 gbb_status check_block_args(const void* image, int N, int K, int M) {
   if (!image) return fail(GBB_E_ARG, "image is NULL");
   if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
-  if (size_t(N) > kCounterBytes / 4 * 256) return fail(GBB_E_SHAPE, "N=%d exceeds 4194304", N);
+  if (size_t(N) > kCounterBytes / 4 * 64) return fail(GBB_E_SHAPE, "N=%d exceeds 1048576", N);
   if (M < 0) return fail(GBB_E_ARG, "M must not be negative (M=%d)", M);
   if (N % kBlockRows || K % kGroup)
     return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);

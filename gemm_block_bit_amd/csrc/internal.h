@@ -24,12 +24,12 @@ struct BlockImageView {
   int N, K, nbr, nbc;
 };
 
-// Decode (M <= 32) launch plan: row groups of 4 block rows x K segments.
-// Split-K calls keep one u32 counter per row group in the first
-// kCounterBytes of the workspace (N up to 4 194 304 rows).
+// Decode (M <= 32) launch plan: one workgroup of nw waves per block row and
+// K segment.  Split-K calls keep one u32 counter per block row in the first
+// kCounterBytes of the workspace (N up to 1 048 576 rows).
 constexpr size_t kCounterBytes = 65536;
 struct DecodePlan {
-  int nseg, seg_len, nrg;
+  int nw, nseg, seg_cols;
   size_t part_bytes, ctr_bytes;
 };
 DecodePlan decode_plan(int N, int K, int M);
