@@ -36,7 +36,7 @@ __device__ void unpack_block(const UnpackArgs& a, int blk, int lane) {
     const int u = P >> 2, p = P & 3, rt = u >> 2, kt = u & 3;
     const int row = br * 64 + 16 * rt + (lane & 15);
     const int col = bc * 128 + 32 * kt + 8 * (lane >> 4) + 2 * p;
-    const uint32_t e = a.sz[size_t(blk) * 64 + 16 * rt + (lane & 15)];
+    const uint32_t e = a.sz[size_t(blk) * 64 + 4 * (lane & 15) + rt];
     const float s = lo_half(e), z = hi_half(e);
     const uint32_t qa = pr & 0xffffu, qb = pr >> 16;
     const size_t o = size_t(row) * a.K + col;

@@ -14,11 +14,18 @@
 //    lane, each holding exactly the lane's codes for the B operands of
 //    v_mfma_f32_16x16x32_f16 (32 columns x 16 rows per tile, 16 tiles per
 //    block; b = 3, 6, 8 are split into planes of widths 2+1, 4+2, 4+4).  The
-//    bitwidth is read once per block as a scalar, so the switch on it is
+//    bitwidth is read once per block as a scalar, so every branch on it is
 //    wave-uniform.
-//  * Each wave runs a two-stage pipeline over its work units (one bit plane
-//    of one block, at most 4 KiB): the activations, scales/zeros and codes of
-//    the next unit are loaded while the current unit is computed.
+//  * Each wave streams its blocks through a 13-slot (24 for M > 16) LDS ring
+//    filled by
+//    global->LDS loads (global_load_lds_dword[x4]), one load per "record":
+//    per block one scale/zero record, the activation record(s) and the b code
+//    slots.  Whole blocks are issued ahead as long as they fit in the ring, so
+//    up to 12 (23) loads are in flight while a block is computed; the wait for a
+//    block is an exact vmcnt, and the in-flight data costs no registers.
+//  * The high plane of a 2-plane block is unpacked with the fp16 exponent of
+//    2^(10 + shift): its codes come out as 2^(10 + shift) + q 2^shift and
+//    accumulate into the same MFMA accumulator as the low plane.
 //  * Unpacking is one AND (plus a shift) and one OR per code pair: the code
 //    lands in the mantissa of fp16 1024.0, giving 1024 + q exactly.  The
 //    matrix cores form C = sum_k x_k (1024 + q_k) per 16-row tile and group
@@ -52,142 +59,206 @@ struct DecodeArgs {
 __device__ __forceinline__ int plane0_w(int b) { return b == 3 ? 2 : (b >= 4 ? 4 : b); }
 __device__ __forceinline__ int plane1_w(int b) { return b == 3 ? 1 : (b == 6 ? 2 : (b == 8 ? 4 : 0)); }
 
-// registers of one work unit (one bit plane of one block) in flight
+// Records in flight per wave: a per-wave ring of RING 1 KiB LDS slots filled
+// by global->LDS loads, one load per record.  A block has at most
+// 1 + 4 MT + 8 records, which must fit: 13 slots for MT = 1 (three 4-wave
+// workgroups per CU), 24 for MT = 2.
 template <int MT>
-struct UnitBuf {
-  u32x4 code[4];     // the plane's w KiB of codes (lane's 16 bytes of each)
-  uint32_t sz[4];    // fp16 s | fp16 z << 16 of row 16 rt + r16
-  half8 xa[4][MT];   // A operands: x[16 mt + r16][32 kt + 8 g .. + 7]
+struct Ring {
+  static constexpr int kSlots = MT == 1 ? 13 : 24;
+  static_assert(1 + 4 * MT + 8 <= kSlots, "a block's records fit in the ring");
 };
 
-// Loads of one unit: activations and scales first, then exactly w code
-// slots.  Every stage waits for all loads before its unit is used, so the
-// load count may differ from unit to unit.
-template <int MT>
-__device__ __forceinline__ void issue(UnitBuf<MT>& u, const DecodeArgs& a, int br, int col, int w, uint32_t kib) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const size_t blk = size_t(br) * a.nbc + col;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + r16;
-    const _Float16* xp = a.x + size_t(m) * a.K + size_t(col) * 128 + 8 * g;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      u32x4 v = {0, 0, 0, 0};
-      if (m < a.M) v = ld16(xp + 32 * kt);
-      u.xa[kt][mt] = __builtin_bit_cast(half8, v);
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) u.sz[rt] = a.sz[blk * 64 + 16 * rt + r16];
-  const uint8_t* cp = a.codes + size_t(kib) * 1024 + 16 * lane;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (t < w) u.code[t] = ld16(cp + 1024 * t);
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
-// One plane of width W.  LOW: the plane holding the low bits, which carries
-// the zero point; otherwise the plane's codes weigh 2^shift.
-// D[token][row] of each 16x16 tile: lane holds tokens 16 mt + 4 g + v, row r16.
-template <int W, bool LOW, int MT>
-__device__ __forceinline__ void plane_mma(const UnitBuf<MT>& u, int shift, const f32x4 (&xsum)[MT],
-                                          f32x4 (&acc)[4][MT]) {
-  constexpr int NP = 16 / W;
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    f32x4 c[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) c[mt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int t = 4 * rt + kt;
-      uint32_t p4[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int P = 4 * t + p, d = P / NP;
-        p4[p] = pair_bits<W>(u.code[d >> 2][d & 3], P % NP) | kMagicPair;
-      }
-      const half8 B = as_half8(p4[0], p4[1], p4[2], p4[3]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) c[mt] = mfma16(u.xa[kt][mt], B, c[mt]);
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left alone (gfx9 encoding), and
+// a compiler barrier so no LDS read is moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most n (uniform, 0 <= n < 24) of this wave's loads are
+// outstanding.
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    default: wait_vmcnt<23>(); break;
+  }
+}
+
+// One global->LDS load of 16 or 4 bytes per lane: lane l's bytes land at LDS
+// address lds + l * size.  Written as inline assembly with no output
+// registers (the data goes to LDS), so the compiler does not track it: every
+// read of the ring is preceded by an explicit vmcnt wait instead, and each
+// load first waits for this wave's earlier LDS reads (lgkmcnt), so a slot is
+// never refilled while a read of it is outstanding.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+// A copy of v in a vector register.  Code-pair extraction is
+// ((word >> shift) & mask) | exponent; with mask and exponent in vector
+// registers it is one v_and_or_b32 (VOP3 can take neither a literal nor two
+// scalar operands on gfx9), i.e. two instructions per pair.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+// Records of one block, in ring order: its scale/zero (256 B: entry
+// 4 r16 + t is row 16 t + r16), nx activation records (M = 1: the 128
+// activations of the block column, 256 B; else 4 tokens x 128 activations
+// each, 1 KiB), then its b code slots (1 KiB each).
+template <int R>
+__device__ __forceinline__ void issue_block(const DecodeArgs& a, int nx, int br, int col, uint32_t kib, int b,
+                                            const u32x4* ring, int first) {
+  const int lane = threadIdx.x & 63;
+  int n = first;
+  dma4(a.sz + (size_t(br) * a.nbc + col) * 64 + lane, lds_addr(ring + (n % R) * 64));
+  ++n;
+  if (a.M == 1) {
+    dma4(a.x + size_t(col) * 128 + 2 * lane, lds_addr(ring + (n % R) * 64));
+    ++n;
+  } else {
+    for (int xi = 0; xi < nx; ++xi, ++n) {
+      const int m = min(4 * xi + (lane >> 4), a.M - 1);
+      dma16(a.x + size_t(m) * a.K + size_t(col) * 128 + 8 * (lane & 15), lds_addr(ring + (n % R) * 64));
     }
-    const uint32_t e = u.sz[rt];
-    const float s = LOW ? lo_half(e) : __builtin_ldexpf(lo_half(e), shift);
-    const float z = LOW ? hi_half(e) : 0.0f;
+  }
+  const uint8_t* cp = a.codes + size_t(kib) * 1024 + 16 * lane;
+  for (int q = 0; q < b; ++q, ++n) dma16(cp + 1024 * q, lds_addr(ring + (n % R) * 64));
+}
+
+// B operand of tile (rt, kt) of a plane of width PW whose lane dwords are
+// w[slot][0..3]: its four code pairs with the fp16 exponent pattern `magic`.
+// Codes of weight 2^shift become 2^(10 + shift) + q 2^shift, so every plane
+// adds into the same accumulator.
+template <int PW>
+__device__ __forceinline__ half8 tile_b(const u32x4 (&w)[PW], int rt, int kt, uint32_t magic, uint32_t mask) {
+  constexpr int NP = 16 / PW;
+  uint32_t p4[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int P = 4 * (4 * rt + kt) + p, d = P / NP, i = P % NP;
+    p4[p] = ((w[d >> 2][d & 3] >> (PW * i)) & mask) | magic;
+  }
+  return as_half8(p4[0], p4[1], p4[2], p4[3]);
+}
+
+// All 16 tiles of one plane of width PW whose slots start at ring record
+// `rec`, issued k-tile by k-tile so the four row-tile accumulation chains
+// interleave on the matrix cores.
+template <int PW, int MT, int R>
+__device__ __forceinline__ void plane_mma(const u32x4* ring, int rec, uint32_t magic, const half8 (&xa)[4][MT],
+                                          f32x4 (&c)[4][MT]) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t mask = in_vgpr(((1u << PW) - 1u) * 0x00010001u);
+  u32x4 w[PW];
+#pragma unroll
+  for (int t = 0; t < PW; ++t) w[t] = ring[((rec + t) % R) * 64 + lane];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const half8 B = tile_b<PW>(w, rt, kt, magic, mask);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) c[rt][mt] = mfma16(xa[kt][mt], B, c[rt][mt]);
+    }
+}
+
+// One block whose records start at ring record `first`: planes of width W0
+// (shift 0) and W1 (shift W0; 0 = none).  acc += s (C - (bias + z) X) with
+// C = sum_k x_k (bias_k + q_k 2^shift) and bias = sum over planes of 1024 2^shift.
+template <int W0, int W1, int MT, int R = Ring<MT>::kSlots>
+__device__ __forceinline__ void block_mma(const DecodeArgs& a, const u32x4* ring, int first, int nx,
+                                          f32x4 (&acc)[4][MT]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const u32x4 sz = ring[(first % R) * 64 + r16];
+  half8 xa[4][MT];
+  if (a.M == 1) {
+    const u32x4* xr = ring + ((first + 1) % R) * 64;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) xa[kt][0] = __builtin_bit_cast(half8, xr[4 * kt + g]);
+  } else {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(16 * mt + r16, a.M - 1);
+      const u32x4* xr = ring + ((first + 1 + (m >> 2)) % R) * 64;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float corr = __builtin_fmaf(z, xsum[mt][v], 1024.0f * xsum[mt][v]);
-        acc[rt][mt][v] = __builtin_fmaf(s, c[mt][v] - corr, acc[rt][mt][v]);
-      }
+      for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
     }
   }
-}
-
-template <int MT>
-__device__ __forceinline__ void compute(const UnitBuf<MT>& u, int w, bool low, int shift, f32x4 (&acc)[4][MT]) {
   const half8 ones = as_half8(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
-  f32x4 xsum[MT];  // X[token] = sum of the group's activations, per lane token
+  f32x4 xsum[MT], c[4][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     xsum[mt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) xsum[mt] = mfma16(u.xa[kt][mt], ones, xsum[mt]);
+    for (int kt = 0; kt < 4; ++kt) xsum[mt] = mfma16(xa[kt][mt], ones, xsum[mt]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) c[rt][mt] = f32x4{0, 0, 0, 0};
   }
-  if (low) {
-    if (w == 4)
-      plane_mma<4, true, MT>(u, 0, xsum, acc);
-    else if (w == 2)
-      plane_mma<2, true, MT>(u, 0, xsum, acc);
-    else
-      plane_mma<1, true, MT>(u, 0, xsum, acc);
-  } else {
-    if (w == 4)
-      plane_mma<4, false, MT>(u, shift, xsum, acc);
-    else if (w == 2)
-      plane_mma<2, false, MT>(u, shift, xsum, acc);
-    else
-      plane_mma<1, false, MT>(u, shift, xsum, acc);
+  const int codes = first + 1 + nx;
+  plane_mma<W0, MT, R>(ring, codes, in_vgpr(kMagicPair), xa, c);
+  if constexpr (W1 != 0) plane_mma<W1, MT, R>(ring, codes + W0, in_vgpr(kMagicPair + W0 * 0x04000400u), xa, c);
+  constexpr float bias = 1024.0f * (1.0f + (W1 ? float(1 << W0) : 0.0f));
+  // lane holds tokens 16 mt + 4 g + v; with one token only v = 0 is live
+  const int nv = a.M == 1 ? 1 : 4;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const float s = lo_half(sz[rt]), z = hi_half(sz[rt]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (v >= nv) break;
+        const float corr = __builtin_fmaf(z, xsum[mt][v], bias * xsum[mt][v]);
+        acc[rt][mt][v] = __builtin_fmaf(s, c[rt][mt][v] - corr, acc[rt][mt][v]);
+      }
   }
-}
-
-// The unit after (j, plane p) in a chunk of S blocks with bitwidths in bvec.
-struct UnitCursor {
-  int j, p;       // block in the chunk, plane (0 low, 1 high)
-  int w, shift;   // plane width and weight 2^shift of its codes
-  uint32_t kib;   // first code KiB of the plane
-};
-
-__device__ __forceinline__ UnitCursor unit_at(int bvec, int ovec, int j, int p) {
-  UnitCursor u;
-  u.j = j;
-  u.p = p;
-  const int b = __builtin_amdgcn_readlane(bvec, j);
-  const int w0 = plane0_w(b);
-  u.w = p == 0 ? w0 : plane1_w(b);
-  u.shift = p == 0 ? 0 : w0;
-  u.kib = uint32_t(__builtin_amdgcn_readlane(ovec, j)) + uint32_t(p == 0 ? 0 : w0);
-  return u;
-}
-
-__device__ __forceinline__ UnitCursor unit_next(const UnitCursor& c, int bvec, int ovec) {
-  const int b = __builtin_amdgcn_readlane(bvec, c.j);
-  if (c.p == 0 && plane1_w(b) != 0) return unit_at(bvec, ovec, c.j, 1);
-  return unit_at(bvec, ovec, c.j + 1, 0);
-}
-
-// Wait for every load of this wave; the scheduling barriers keep the loads
-// issued after it from being hoisted above it.
-__device__ __forceinline__ void wait_all_loads() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 3 : 1))) void decode_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(DecodeArgs a) {
+  constexpr int R = Ring<MT>::kSlots;
+  // wave-uniform values go through readfirstlane so the compiler keeps them
+  // in scalar registers and branches on them with scalar branches
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int br = blockIdx.x / a.nseg, seg = blockIdx.x - br * a.nseg;
   // this workgroup's columns, split evenly between its waves
@@ -195,6 +266,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MT == 1
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
   const int w_begin = wg_begin + (wg_cols * wave) / NW;
   const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
+  const int nx = a.M == 1 ? 1 : (a.M + 3) / 4;
+
+  __shared__ u32x4 lds[NW * R * 64];   // per-wave rings; reused for the reduction
+  const u32x4* ring = lds + wave * R * 64;
 
   f32x4 acc[4][MT];
 #pragma unroll
@@ -202,35 +277,49 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MT == 1
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0, 0, 0, 0};
 
-  // Units (bit planes of blocks) in column order; the loads of the next unit
-  // are in flight while the current one is computed.
   for (int col0 = w_begin; col0 < w_end; col0 += 64) {
     const int S = min(64, w_end - col0);
     const bool in = lane < S;
     const size_t blk = size_t(br) * a.nbc + col0 + (in ? lane : 0);
     const int bvec = in ? int(a.bits[blk]) : 0;
     const int ovec = in ? int(a.offs[blk]) : 0;
-    UnitBuf<MT> A, B;
-    UnitCursor ca = unit_at(bvec, ovec, 0, 0), cb;
-    issue<MT>(A, a, br, col0 + ca.j, ca.w, ca.kib);
-    while (true) {
-      wait_all_loads();
-      cb = unit_next(ca, bvec, ovec);
-      const bool hb = cb.j < S;
-      if (hb) issue<MT>(B, a, br, col0 + cb.j, cb.w, cb.kib);
-      compute<MT>(A, ca.w, ca.p == 0, ca.shift, acc);
-      if (!hb) break;
-      wait_all_loads();
-      ca = unit_next(cb, bvec, ovec);
-      const bool ha = ca.j < S;
-      if (ha) issue<MT>(A, a, br, col0 + ca.j, ca.w, ca.kib);
-      compute<MT>(B, cb.w, cb.p == 0, cb.shift, acc);
-      if (!ha) break;
+    // The compiler tracks only these two loads; wait for them here, before any
+    // ring load is issued, so that it never waits for them (and with them for
+    // every in-flight ring load) inside the block loop.
+    wait_vmcnt<0>();
+    // Blocks in column order.  Block j's records are ring records
+    // [first_j, first_j + 1 + nx + b_j); blocks are issued ahead as long as
+    // all their records fit in the R slots after the block being computed.
+    int issued = 0;   // records issued so far
+    int jn = 0;       // next block to issue
+    int first = 0;    // first record of block j
+    for (int j = 0; j < S; ++j) {
+      const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
+      while (jn < S) {
+        const int bn = uniform(__builtin_amdgcn_readlane(bvec, jn));
+        if (issued + 1 + nx + bn > first + R) break;
+        issue_block<R>(a, nx, br, col0 + jn, uint32_t(uniform(__builtin_amdgcn_readlane(ovec, jn))), bn, ring, issued);
+        issued = uniform(issued + 1 + nx + bn);
+        ++jn;
+      }
+      // block j's last record is first + nx + bj; later records may still fly
+      wait_vmcnt_at_most(issued - (first + 1 + nx + bj));
+      switch (bj) {
+        case 1: block_mma<1, 0, MT>(a, ring, first, nx, acc); break;
+        case 2: block_mma<2, 0, MT>(a, ring, first, nx, acc); break;
+        case 3: block_mma<2, 1, MT>(a, ring, first, nx, acc); break;
+        case 4: block_mma<4, 0, MT>(a, ring, first, nx, acc); break;
+        case 6: block_mma<4, 2, MT>(a, ring, first, nx, acc); break;
+        default: block_mma<4, 4, MT>(a, ring, first, nx, acc); break;
+      }
+      first = uniform(first + 1 + nx + bj);
     }
   }
+  __syncthreads();
 
   // waves meet in LDS; wave w < 4 adds row tile w over the waves in order
-  __shared__ f32x4 red[NW][4][MT][64];
+  static_assert(NW * 4 * MT <= NW * R, "reduction fits in the rings");
+  f32x4 (*red)[4][MT][64] = reinterpret_cast<f32x4 (*)[4][MT][64]>(lds);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll

@@ -25,7 +25,8 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 // Block image: 64-byte header, then 256-byte aligned sections
 //   bits  u8 [nblk]            block index = block_row * (K/128) + block_col
 //   offs  u32 [nblk + 1]       start of each block's codes, in KiB
-//   sz    u32 [nblk][64]       per row of the block: fp16 s (low), fp16 z (high)
+//   sz    u32 [nblk][16][4]    entry [r][t] is row 16 t + r of the block:
+//                              fp16 s (low half), fp16 z (high half)
 //   codes 1024 * b bytes per block, planes of width 1|2|4 (low bits first)
 struct BlockLayout {
   size_t nblk, bits_off, offs_off, sz_off, codes_off;

@@ -277,7 +277,7 @@ extern "C" gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uin
       }
       for (int k = 0; k < 128; ++k) q[r][k] = asym_code(v[k], gq, levels);
       const uint32_t e = uint32_t(gq.s16) | (uint32_t(gq.z16) << 16);
-      std::memcpy(img + l.sz_off + 256 * size_t(blk) + 4 * r, &e, 4);
+      std::memcpy(img + l.sz_off + 256 * size_t(blk) + 4 * (4 * (r % 16) + r / 16), &e, 4);
     }
     uint8_t* dst = img + l.codes_off + 1024 * kib[blk];
     const int w0 = plane0_width(b), w1 = plane1_width(b);

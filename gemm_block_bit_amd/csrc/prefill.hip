@@ -67,7 +67,7 @@ __device__ __forceinline__ void dequant_rows(const uint8_t* __restrict__ blk_cod
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int rt = rt0 + h;
-    const uint32_t e = blk_sz[16 * rt + r16];
+    const uint32_t e = blk_sz[4 * r16 + rt];
     const half2v s2 = as_half2((e & 0xffffu) * 0x00010001u);
     const _Float16 zf = __builtin_bit_cast(_Float16, (unsigned short)(e >> 16));
     const _Float16 nz = -((_Float16)1024.0f + zf);  // exact: an integer below 2048

@@ -17,8 +17,9 @@ on 256-byte boundaries (bits at 256).
 
 bits   u8 per block, block index = block_row * (K/128) + block_col.
 offs   u32 per block + 1: start of each block in the code section in KiB.
-sz     per block 64 u32, one per row of the block: low half fp16 s, high half
-       fp16 z (an integer 0 .. 2^b - 1).
+sz     per block 64 u32; entry 4 r + t belongs to row 16 t + r of the block
+       (r < 16, t < 4): low half fp16 s, high half fp16 z (an integer
+       0 .. 2^b - 1).
 codes  block i occupies 1024 * b_i bytes, split into planes of width
        1 (b=1), 2 (b=2), 2+1 (b=3), 4 (b=4), 4+2 (b=6), 4+4 (b=8); the first
        plane holds the low bits.  A plane of width w is w KiB; its dword
@@ -113,7 +114,8 @@ def read_block_image(buf) -> dict:
         raise ValueError("block offsets disagree with bitwidths")
     if offs[-1] * 1024 != codes_bytes or b.size < codes_off + codes_bytes:
         raise ValueError("code section size")
-    sz = b[sz_off:sz_off + 256 * nblk].view("<u2").reshape(nbr, nbc, 64, 2)
+    sz = b[sz_off:sz_off + 256 * nblk].view("<u2").reshape(nbr, nbc, 16, 4, 2)
+    sz = sz.transpose(0, 1, 3, 2, 4).reshape(nbr, nbc, 64, 2)        # row 16 t + r
     s16 = sz[..., 0].copy().view(np.float16).transpose(0, 2, 1).reshape(N, nbc)
     z16 = sz[..., 1].copy().view(np.float16).transpose(0, 2, 1).reshape(N, nbc)
 

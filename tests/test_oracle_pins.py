@@ -282,7 +282,7 @@ def _slow_block_image(q, s16, z16, bits):
             buf[bits_off + blk] = b
             buf[offs_off + 4 * blk:offs_off + 4 * blk + 4] = int(kib).to_bytes(4, "little")
             for r in range(64):
-                o = sz_off + 256 * blk + 4 * r
+                o = sz_off + 256 * blk + 4 * (4 * (r % 16) + r // 16)
                 buf[o:o + 2] = np.float16(s16[64 * br + r, bc]).tobytes()
                 buf[o + 2:o + 4] = np.float16(z16[64 * br + r, bc]).tobytes()
             base = codes_off + 1024 * kib
