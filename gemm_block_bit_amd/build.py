@@ -28,6 +28,9 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-Wall",
 CXX_FLAGS = ["-O2", "-Wall", "-Wextra", "-fno-fast-math"] + COMMON
 
 HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip"]
+# per-source extra flags: the decode kernel reads its MFMA results with VALU
+# code right away, so it keeps them in VGPRs rather than accumulation registers
+HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["pack.cpp", "api.cpp"]
 
 
@@ -45,7 +48,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, s + ".o")
-        jobs.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])
+        jobs.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(s, []) + ["-c", os.path.join(CSRC, s), "-o", obj])
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, s + ".o")
         jobs.append([CXX] + CXX_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])

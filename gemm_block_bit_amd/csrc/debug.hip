@@ -20,30 +20,36 @@ struct UnpackArgs {
   int N, K, nbr, nbc;
 };
 
+// Field i of word c of slot j of a plane of width W holds the code pair of
+// tile 4 kt + rt = j (16 / W) + i: row 16 rt + lane % 16, columns
+// 32 kt + 8 (lane / 16) + 2 c (low half) and + 1 (high half).
+template <int W>
+__device__ __forceinline__ uint32_t plane_pair(const uint8_t* cb, int u, int c) {
+  constexpr int NP = 16 / W;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(cb + 1024 * (u / NP) + 4 * c);
+  return (w >> (W * (u % NP))) & (((1u << W) - 1u) * 0x00010001u);
+}
+
 template <int W0, int W1>
 __device__ void unpack_block(const UnpackArgs& a, int blk, int lane) {
-  constexpr int NP0 = 16 / W0;
-  constexpr int NP1 = W1 ? 16 / W1 : 1;
   const int br = blk / a.nbc, bc = blk % a.nbc;
   const uint8_t* cb = a.codes + size_t(a.offs[blk]) * 1024 + 16 * lane;
-  for (int P = 0; P < 64; ++P) {
-    const int d0 = P / NP0, s0 = P % NP0;
-    uint32_t pr = pair_bits<W0>(*reinterpret_cast<const uint32_t*>(cb + 1024 * (d0 >> 2) + 4 * (d0 & 3)), s0);
-    if constexpr (W1 != 0) {
-      const int d1 = P / NP1, s1 = P % NP1;
-      pr |= pair_bits<W1>(*reinterpret_cast<const uint32_t*>(cb + 1024 * (W0 + (d1 >> 2)) + 4 * (d1 & 3)), s1) << W0;
-    }
-    const int u = P >> 2, p = P & 3, rt = u >> 2, kt = u & 3;
+  for (int u = 0; u < 16; ++u) {
+    const int kt = u >> 2, rt = u & 3;
     const int row = br * 64 + 16 * rt + (lane & 15);
-    const int col = bc * 128 + 32 * kt + 8 * (lane >> 4) + 2 * p;
     const uint32_t e = a.sz[size_t(blk) * 64 + 4 * (lane & 15) + rt];
     const float s = lo_half(e), z = hi_half(e);
-    const uint32_t qa = pr & 0xffffu, qb = pr >> 16;
-    const size_t o = size_t(row) * a.K + col;
-    if (a.q) a.q[o] = uint8_t(qa), a.q[o + 1] = uint8_t(qb);
-    const float va = (float(qa) - z) * s, vb = (float(qb) - z) * s;
-    if (a.w32) a.w32[o] = va, a.w32[o + 1] = vb;
-    if (a.w16) a.w16[o] = (_Float16)va, a.w16[o + 1] = (_Float16)vb;
+    for (int c = 0; c < 4; ++c) {
+      uint32_t pr = plane_pair<W0>(cb, u, c);
+      if constexpr (W1 != 0) pr |= plane_pair<W1>(cb + 1024 * W0, u, c) << W0;
+      const int col = bc * 128 + 32 * kt + 8 * (lane >> 4) + 2 * c;
+      const uint32_t qa = pr & 0xffffu, qb = pr >> 16;
+      const size_t o = size_t(row) * a.K + col;
+      if (a.q) a.q[o] = uint8_t(qa), a.q[o + 1] = uint8_t(qb);
+      const float va = (float(qa) - z) * s, vb = (float(qb) - z) * s;
+      if (a.w32) a.w32[o] = va, a.w32[o + 1] = vb;
+      if (a.w16) a.w16[o] = (_Float16)va, a.w16[o + 1] = (_Float16)vb;
+    }
   }
 }
 

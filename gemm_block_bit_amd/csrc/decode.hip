@@ -11,27 +11,23 @@
 //    waves split the block columns; their sums meet in LDS and are added in a
 //    fixed order.
 //  * A block of bitwidth b is b KiB of codes: b coalesced 16-byte loads per
-//    lane, each holding exactly the lane's codes for the B operands of
-//    v_mfma_f32_16x16x32_f16 (32 columns x 16 rows per tile, 16 tiles per
-//    block; b = 3, 6, 8 are split into planes of widths 2+1, 4+2, 4+4).  The
-//    bitwidth is read once per block as a scalar, so every branch on it is
-//    wave-uniform.
-//  * Each wave streams its blocks through a 13-slot (24 for M > 16) LDS ring
-//    filled by
-//    global->LDS loads (global_load_lds_dword[x4]), one load per "record":
-//    per block one scale/zero record, the activation record(s) and the b code
-//    slots.  Whole blocks are issued ahead as long as they fit in the ring, so
-//    up to 12 (23) loads are in flight while a block is computed; the wait for a
-//    block is an exact vmcnt, and the in-flight data costs no registers.
-//  * The high plane of a 2-plane block is unpacked with the fp16 exponent of
-//    2^(10 + shift): its codes come out as 2^(10 + shift) + q 2^shift and
-//    accumulate into the same MFMA accumulator as the low plane.
-//  * Unpacking is one AND (plus a shift) and one OR per code pair: the code
-//    lands in the mantissa of fp16 1024.0, giving 1024 + q exactly.  The
-//    matrix cores form C = sum_k x_k (1024 + q_k) per 16-row tile and group
-//    (x is the A operand, one row per token) and X = sum_k x_k against an
-//    all-ones B operand; the epilogue adds s (C - (1024 bias + z) X) to fp32
-//    accumulators, which equals s sum_k x_k (q_k - z).
+//    lane.  The four words of one 1 KiB slot at one bit field are exactly a
+//    v_mfma_f32_16x16x32_f16 B operand (16 rows x 32 columns), so unpacking
+//    is one AND per word (plus one shift shared by a few fields): the masked
+//    field q << o read as fp16 is the subnormal q 2^(o - 24), which the matrix
+//    cores multiply exactly.  o depends only on the row tile, so each row
+//    tile's accumulator carries one power of two, removed in the epilogue.
+//    b = 3, 6, 8 are two planes (2+1, 4+2, 4+4) with accumulators of their own.
+//  * The matrix cores form C = sum_k x_k q_k 2^(o - 24) per 16-row tile and
+//    X = sum_k x_k against an all-ones B operand; the epilogue adds
+//    s (2^(24 - o) C - z X) = s sum_k x_k (q_k - z) to fp32 accumulators.
+//  * Each wave streams its blocks through a 16-slot (32 for M > 16) LDS ring
+//    filled by global->LDS loads (global_load_lds_dword[x4]): per block one
+//    slot for the scale/zero record (and, for one token, the activations),
+//    the activation slots of larger batches and the b code slots.  Blocks are
+//    issued ahead while they fit, so the in-flight data costs no registers;
+//    the wait for a block is a vmcnt bound, and a block's slots are refilled
+//    as soon as its LDS reads have completed.
 //  * With K segments, partial sums cross workgroups (and XCDs) through
 //    device-scope (sc1) stores and loads, which need no cache writeback; the
 //    last workgroup of a block row (an atomic counter that resets itself)
@@ -56,16 +52,12 @@ struct DecodeArgs {
   int N, K, M, nbr, nbc, seg_cols, nseg;
 };
 
-__device__ __forceinline__ int plane0_w(int b) { return b == 3 ? 2 : (b >= 4 ? 4 : b); }
-__device__ __forceinline__ int plane1_w(int b) { return b == 3 ? 1 : (b == 6 ? 2 : (b == 8 ? 4 : 0)); }
-
-// Records in flight per wave: a per-wave ring of RING 1 KiB LDS slots filled
-// by global->LDS loads, one load per record.  A block has at most
-// 1 + 4 MT + 8 records, which must fit: 13 slots for MT = 1 (three 4-wave
-// workgroups per CU), 24 for MT = 2.
+// Ring slots per wave (a power of two): a block takes 1 + nx + b slots
+// (nx = activation slots: 0 for one token, ceil(M / 4) otherwise).
 template <int MT>
 struct Ring {
-  static constexpr int kSlots = MT == 1 ? 13 : 24;
+  static constexpr int kSlots = MT == 1 ? 16 : 32;
+  static constexpr uint32_t kMask = kSlots * 1024 - 1;  // ring byte offsets wrap with this
   static_assert(1 + 4 * MT + 8 <= kSlots, "a block's records fit in the ring");
 };
 
@@ -84,178 +76,154 @@ __device__ __forceinline__ void wait_vmcnt() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wait until at most n (uniform, 0 <= n < 24) of this wave's loads are
-// outstanding.
+// s_waitcnt lgkmcnt(0): every LDS read of this wave has returned its data.
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most n (uniform, n >= 0) of this wave's loads are in
+// flight; n is rounded down to a few levels, which only waits a little longer.
 __device__ __forceinline__ void wait_vmcnt_at_most(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    case 16: wait_vmcnt<16>(); break;
-    case 17: wait_vmcnt<17>(); break;
-    case 18: wait_vmcnt<18>(); break;
-    case 19: wait_vmcnt<19>(); break;
-    case 20: wait_vmcnt<20>(); break;
-    case 21: wait_vmcnt<21>(); break;
-    case 22: wait_vmcnt<22>(); break;
-    default: wait_vmcnt<23>(); break;
-  }
-}
-
-// One global->LDS load of 16 or 4 bytes per lane: lane l's bytes land at LDS
-// address lds + l * size.  Written as inline assembly with no output
-// registers (the data goes to LDS), so the compiler does not track it: every
-// read of the ring is preceded by an explicit vmcnt wait instead, and each
-// load first waits for this wave's earlier LDS reads (lgkmcnt), so a slot is
-// never refilled while a read of it is outstanding.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-
-// A copy of v in a vector register.  Code-pair extraction is
-// ((word >> shift) & mask) | exponent; with mask and exponent in vector
-// registers it is one v_and_or_b32 (VOP3 can take neither a literal nor two
-// scalar operands on gfx9), i.e. two instructions per pair.
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
-  return r;
-}
-
-// Records of one block, in ring order: its scale/zero (256 B: entry
-// 4 r16 + t is row 16 t + r16), nx activation records (M = 1: the 128
-// activations of the block column, 256 B; else 4 tokens x 128 activations
-// each, 1 KiB), then its b code slots (1 KiB each).
-template <int R>
-__device__ __forceinline__ void issue_block(const DecodeArgs& a, int nx, int br, int col, uint32_t kib, int b,
-                                            const u32x4* ring, int first) {
-  const int lane = threadIdx.x & 63;
-  int n = first;
-  dma4(a.sz + (size_t(br) * a.nbc + col) * 64 + lane, lds_addr(ring + (n % R) * 64));
-  ++n;
-  if (a.M == 1) {
-    dma4(a.x + size_t(col) * 128 + 2 * lane, lds_addr(ring + (n % R) * 64));
-    ++n;
-  } else {
-    for (int xi = 0; xi < nx; ++xi, ++n) {
-      const int m = min(4 * xi + (lane >> 4), a.M - 1);
-      dma16(a.x + size_t(m) * a.K + size_t(col) * 128 + 8 * (lane & 15), lds_addr(ring + (n % R) * 64));
+  if (n < 4) {
+    if (n < 2) {
+      if (n < 1) wait_vmcnt<0>(); else wait_vmcnt<1>();
+    } else {
+      if (n < 3) wait_vmcnt<2>(); else wait_vmcnt<3>();
     }
+  } else if (n < 12) {
+    if (n < 8) {
+      if (n < 6) wait_vmcnt<4>(); else wait_vmcnt<6>();
+    } else {
+      if (n < 10) wait_vmcnt<8>(); else wait_vmcnt<10>();
+    }
+  } else {
+    if (n < 16) wait_vmcnt<12>(); else wait_vmcnt<16>();
   }
-  const uint8_t* cp = a.codes + size_t(kib) * 1024 + 16 * lane;
-  for (int q = 0; q < b; ++q, ++n) dma16(cp + 1024 * q, lds_addr(ring + (n % R) * 64));
 }
 
-// B operand of tile (rt, kt) of a plane of width PW whose lane dwords are
-// w[slot][0..3]: its four code pairs with the fp16 exponent pattern `magic`.
-// Codes of weight 2^shift become 2^(10 + shift) + q 2^shift, so every plane
-// adds into the same accumulator.
-template <int PW>
-__device__ __forceinline__ half8 tile_b(const u32x4 (&w)[PW], int rt, int kt, uint32_t magic, uint32_t mask) {
-  constexpr int NP = 16 / PW;
-  uint32_t p4[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int P = 4 * (4 * rt + kt) + p, d = P / NP, i = P % NP;
-    p4[p] = ((w[d >> 2][d & 3] >> (PW * i)) & mask) | magic;
-  }
-  return as_half8(p4[0], p4[1], p4[2], p4[3]);
+// One global->LDS load of 16 or 4 bytes per lane from sbase + voff: lane l's
+// bytes land at LDS address ring + off + l * size.  Inline assembly with no
+// output registers (the data goes to LDS), so the compiler does not track it:
+// every read of the ring is preceded by an explicit vmcnt wait instead, and a
+// slot is only refilled after the reads of its previous record completed.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t ring, uint32_t off) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(ring), "s"(off)
+               : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t ring, uint32_t off) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(ring), "s"(off)
+               : "memory", "m0", "scc");
 }
 
-// All 16 tiles of one plane of width PW whose slots start at ring record
-// `rec`, issued k-tile by k-tile so the four row-tile accumulation chains
-// interleave on the matrix cores.
-template <int PW, int MT, int R>
-__device__ __forceinline__ void plane_mma(const u32x4* ring, int rec, uint32_t magic, const half8 (&xa)[4][MT],
-                                          f32x4 (&c)[4][MT]) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t mask = in_vgpr(((1u << PW) - 1u) * 0x00010001u);
-  u32x4 w[PW];
-#pragma unroll
-  for (int t = 0; t < PW; ++t) w[t] = ring[((rec + t) % R) * 64 + lane];
+// MFMAs of one plane of width W whose slots are w[0..W): tile 4 kt + rt is
+// bit field i = (4 kt + rt) % (16 / W) of slot (4 kt + rt) / (16 / W).  The
+// field is shifted down by sh and masked at offset o = W (i % Q), so the B
+// operand holds q 2^(o - 24); o is a function of rt alone.  Tiles go k-tile
+// by k-tile so the four row-tile accumulation chains interleave.
+template <int W>
+struct PlaneGeom {
+  static constexpr int NP = 16 / W;
+  static constexpr int Q = W == 4 ? 2 : 4;
+  static constexpr int off(int rt) { return W * (rt % Q); }  // o of row tile rt
+};
+
+template <int W, int MT>
+__device__ __forceinline__ void plane_mma(const u32x4 (&w)[W], const half8 (&xa)[4][MT], f32x4 (&c)[4][MT]) {
+  using G = PlaneGeom<W>;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const half8 B = tile_b<PW>(w, rt, kt, magic, mask);
+      const int u = 4 * kt + rt, j = u / G::NP, i = u % G::NP;
+      const int o = G::off(rt), sh = W * i - o;
+      const uint32_t mask = (((1u << W) - 1u) * 0x00010001u) << o;
+      const half8 B = as_half8((w[j][0] >> sh) & mask, (w[j][1] >> sh) & mask, (w[j][2] >> sh) & mask,
+                               (w[j][3] >> sh) & mask);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) c[rt][mt] = mfma16(xa[kt][mt], B, c[rt][mt]);
     }
 }
 
-// One block whose records start at ring record `first`: planes of width W0
-// (shift 0) and W1 (shift W0; 0 = none).  acc += s (C - (bias + z) X) with
-// C = sum_k x_k (bias_k + q_k 2^shift) and bias = sum over planes of 1024 2^shift.
-template <int W0, int W1, int MT, int R = Ring<MT>::kSlots>
-__device__ __forceinline__ void block_mma(const DecodeArgs& a, const u32x4* ring, int first, int nx,
-                                          f32x4 (&acc)[4][MT]) {
+// 2^e as a float, e a small compile-time integer.
+__device__ __forceinline__ constexpr float pow2(int e) {
+  return e >= 0 ? float(1ull << e) : 1.0f / float(1ull << -e);
+}
+
+// One block of planes W0 (shift 0) and W1 (shift W0; 0 = none) whose records
+// start at ring byte offset sb: read them, let `refill` reuse the slots, then
+// acc += s (sum over planes of 2^(24 + shift - o) C - z X).  ONE: a single
+// token, whose activations share the scale/zero slot; all rows of A are that
+// token, so every row of an accumulator tile holds the same sums.
+template <int W0, int W1, int MT, bool ONE, class Refill>
+__device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx, int M, f32x4 (&acc)[4][MT],
+                                          Refill&& refill) {
+  constexpr uint32_t MASK = Ring<MT>::kMask;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const u32x4 sz = ring[(first % R) * 64 + r16];
+  const u32x4 sz = ring[(sb >> 4) + r16];
   half8 xa[4][MT];
-  if (a.M == 1) {
-    const u32x4* xr = ring + ((first + 1) % R) * 64;
+  if constexpr (ONE) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) xa[kt][0] = __builtin_bit_cast(half8, xr[4 * kt + g]);
+    for (int kt = 0; kt < 4; ++kt) xa[kt][0] = __builtin_bit_cast(half8, ring[(sb >> 4) + 16 + 4 * kt + g]);
   } else {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = min(16 * mt + r16, a.M - 1);
-      const u32x4* xr = ring + ((first + 1 + (m >> 2)) % R) * 64;
+      const int m = min(16 * mt + r16, M - 1);
+      const u32x4* xr = ring + (((sb + 1024 * (1 + (m >> 2))) & MASK) >> 4);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
     }
   }
+  u32x4 w0[W0], w1[W1 ? W1 : 1];
+  {
+    const uint32_t cb = sb + 1024 * (1 + nx);
+#pragma unroll
+    for (int q = 0; q < W0; ++q) w0[q] = ring[(((cb + 1024 * q) & MASK) >> 4) + lane];
+#pragma unroll
+    for (int q = 0; q < W1; ++q) w1[q] = ring[(((cb + 1024 * (W0 + q)) & MASK) >> 4) + lane];
+  }
+  wait_lds();
+  refill();
+
   const half8 ones = as_half8(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
-  f32x4 xsum[MT], c[4][MT];
+  f32x4 xsum[MT], c0[4][MT], c1[4][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     xsum[mt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) xsum[mt] = mfma16(xa[kt][mt], ones, xsum[mt]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) c[rt][mt] = f32x4{0, 0, 0, 0};
+    for (int rt = 0; rt < 4; ++rt) c0[rt][mt] = c1[rt][mt] = f32x4{0, 0, 0, 0};
   }
-  const int codes = first + 1 + nx;
-  plane_mma<W0, MT, R>(ring, codes, in_vgpr(kMagicPair), xa, c);
-  if constexpr (W1 != 0) plane_mma<W1, MT, R>(ring, codes + W0, in_vgpr(kMagicPair + W0 * 0x04000400u), xa, c);
-  constexpr float bias = 1024.0f * (1.0f + (W1 ? float(1 << W0) : 0.0f));
-  // lane holds tokens 16 mt + 4 g + v; with one token only v = 0 is live
-  const int nv = a.M == 1 ? 1 : 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xsum[mt] = mfma16(xa[kt][mt], ones, xsum[mt]);
+  plane_mma<W0, MT>(w0, xa, c0);
+  if constexpr (W1 != 0) plane_mma<W1, MT>(w1, xa, c1);
+  // lane holds tokens 16 mt + 4 g + v
+  constexpr int NV = ONE ? 1 : 4;
+  constexpr int W1g = W1 ? W1 : 1;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const float s = lo_half(sz[rt]), z = hi_half(sz[rt]);
+    constexpr float k0[4] = {pow2(24 - PlaneGeom<W0>::off(0)), pow2(24 - PlaneGeom<W0>::off(1)),
+                             pow2(24 - PlaneGeom<W0>::off(2)), pow2(24 - PlaneGeom<W0>::off(3))};
+    constexpr float k1[4] = {pow2(24 + W0 - PlaneGeom<W1g>::off(0)), pow2(24 + W0 - PlaneGeom<W1g>::off(1)),
+                             pow2(24 + W0 - PlaneGeom<W1g>::off(2)), pow2(24 + W0 - PlaneGeom<W1g>::off(3))};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (v >= nv) break;
-        const float corr = __builtin_fmaf(z, xsum[mt][v], bias * xsum[mt][v]);
-        acc[rt][mt][v] = __builtin_fmaf(s, c[rt][mt][v] - corr, acc[rt][mt][v]);
+      for (int v = 0; v < NV; ++v) {
+        float t = c0[rt][mt][v] * k0[rt];
+        if constexpr (W1 != 0) t = __builtin_fmaf(c1[rt][mt][v], k1[rt], t);
+        acc[rt][mt][v] = __builtin_fmaf(s, __builtin_fmaf(-z, xsum[mt][v], t), acc[rt][mt][v]);
       }
   }
 }
 
-template <int NW, int MT>
+template <int NW, int MT, bool ONE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int R = Ring<MT>::kSlots;
+  constexpr uint32_t MASK = Ring<MT>::kMask;
   // wave-uniform values go through readfirstlane so the compiler keeps them
   // in scalar registers and branches on them with scalar branches
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -266,10 +234,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
   const int w_begin = wg_begin + (wg_cols * wave) / NW;
   const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
-  const int nx = a.M == 1 ? 1 : (a.M + 3) / 4;
+  const int M = ONE ? 1 : a.M;
+  const int nx = ONE ? 0 : (M + 3) / 4;   // activation slots per block
+  const int xd = ONE ? 1 : nx;            // activation loads per block
+  // byte offset of lane's activation chunk in activation record xi
+  uint32_t xoff[8];
+#pragma unroll
+  for (int xi = 0; xi < 8; ++xi) xoff[xi] = uint32_t(min(4 * xi + g, M - 1)) * uint32_t(2 * a.K) + 16 * r16;
 
   __shared__ u32x4 lds[NW * R * 64];   // per-wave rings; reused for the reduction
   const u32x4* ring = lds + wave * R * 64;
+  const uint32_t ring_lds = lds_addr(ring);
 
   f32x4 acc[4][MT];
 #pragma unroll
@@ -282,37 +257,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
     const bool in = lane < S;
     const size_t blk = size_t(br) * a.nbc + col0 + (in ? lane : 0);
     const int bvec = in ? int(a.bits[blk]) : 0;
-    const int ovec = in ? int(a.offs[blk]) : 0;
-    // The compiler tracks only these two loads; wait for them here, before any
+    const int o0 = int(a.offs[size_t(br) * a.nbc + col0]);
+    // The compiler tracks only these loads; wait for them here, before any
     // ring load is issued, so that it never waits for them (and with them for
     // every in-flight ring load) inside the block loop.
     wait_vmcnt<0>();
-    // Blocks in column order.  Block j's records are ring records
-    // [first_j, first_j + 1 + nx + b_j); blocks are issued ahead as long as
-    // all their records fit in the R slots after the block being computed.
-    int issued = 0;   // records issued so far
-    int jn = 0;       // next block to issue
-    int first = 0;    // first record of block j
-    for (int j = 0; j < S; ++j) {
-      const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
+    // The chunk's blocks are consecutive in the image, so their scale/zero
+    // records, activation columns and codes are three contiguous streams.
+    const uint32_t* szp = a.sz + (size_t(br) * a.nbc + col0) * 64;
+    const _Float16* xp = a.x + size_t(col0) * 128;
+    const uint8_t* cp = a.codes + size_t(uniform(o0)) * 1024;
+    int jn = 0;          // next block to issue
+    int used = 0;        // ring slots holding blocks not yet read
+    uint32_t sbn = 0;    // ring byte offset of the next block to issue
+    int issued = 0;      // loads issued
+    auto fill = [&]() {
       while (jn < S) {
         const int bn = uniform(__builtin_amdgcn_readlane(bvec, jn));
-        if (issued + 1 + nx + bn > first + R) break;
-        issue_block<R>(a, nx, br, col0 + jn, uint32_t(uniform(__builtin_amdgcn_readlane(ovec, jn))), bn, ring, issued);
-        issued = uniform(issued + 1 + nx + bn);
+        const int ns = 1 + nx + bn;
+        if (used + ns > R) break;
+        dma4(szp, 4 * lane, ring_lds, sbn);
+        szp += 64;
+        if constexpr (ONE) {
+          dma4(xp, 4 * lane, ring_lds, sbn + 256);
+        } else {
+          for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
+        }
+        xp += 128;
+        uint32_t sc = sbn + 1024 * (1 + nx);
+        for (int q = 0; q < bn; ++q) {
+          dma16(cp, 16 * lane, ring_lds, sc & MASK);
+          cp += 1024;
+          sc += 1024;
+        }
+        sbn = sc & MASK;
+        used += ns;
+        issued += 1 + xd + bn;
         ++jn;
       }
-      // block j's last record is first + nx + bj; later records may still fly
-      wait_vmcnt_at_most(issued - (first + 1 + nx + bj));
+    };
+    fill();
+    uint32_t sb = 0;   // ring byte offset of block j
+    int done = 0;      // loads of blocks 0..j
+    for (int j = 0; j < S; ++j) {
+      const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
+      done += 1 + xd + bj;
+      wait_vmcnt_at_most(issued - done);
+      auto refill = [&]() {
+        used -= 1 + nx + bj;
+        fill();
+      };
       switch (bj) {
-        case 1: block_mma<1, 0, MT>(a, ring, first, nx, acc); break;
-        case 2: block_mma<2, 0, MT>(a, ring, first, nx, acc); break;
-        case 3: block_mma<2, 1, MT>(a, ring, first, nx, acc); break;
-        case 4: block_mma<4, 0, MT>(a, ring, first, nx, acc); break;
-        case 6: block_mma<4, 2, MT>(a, ring, first, nx, acc); break;
-        default: block_mma<4, 4, MT>(a, ring, first, nx, acc); break;
+        case 1: block_mma<1, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        case 2: block_mma<2, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        case 3: block_mma<2, 1, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        case 4: block_mma<4, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        case 6: block_mma<4, 2, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        default: block_mma<4, 4, MT, ONE>(ring, sb, nx, M, acc, refill); break;
       }
-      first = uniform(first + 1 + nx + bj);
+      sb = (sb + 1024 * (1 + nx + bj)) & MASK;
     }
   }
   __syncthreads();
@@ -336,11 +339,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * mt + 4 * g + v;
-        if (m >= a.M) continue;
+        if (m >= M) continue;
         if (a.nseg == 1)
           a.y[size_t(m) * a.N + n] = (_Float16)s[v];
         else
-          __hip_atomic_store(a.part + (size_t(seg) * a.M + m) * a.N + n, s[v], __ATOMIC_RELAXED,
+          __hip_atomic_store(a.part + (size_t(seg) * M + m) * a.N + n, s[v], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
   }
   __syncthreads();
   if (!s_last) return;
-  const size_t stride = size_t(a.M) * a.N;
-  for (int o = threadIdx.x; o < 64 * a.M; o += NW * 64) {
+  const size_t stride = size_t(M) * a.N;
+  for (int o = threadIdx.x; o < 64 * M; o += NW * 64) {
     const int m = o >> 6, n = br * 64 + (o & 63);
     const float* pp = a.part + size_t(m) * a.N + n;
     float s = 0.0f;
@@ -378,19 +381,212 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
   }
 }
 
+// Single-token decode.  With one token the activations of a block column are
+// 256 bytes, so each wave keeps two small rings: an 8-slot ring of 1 KiB code
+// slots and a 4-entry ring of 512-byte records (scale/zero 256 B, then the
+// block column's activations 256 B).  That is 10 KiB of LDS per wave, so four
+// 4-wave workgroups (16 waves) are resident per CU, which hides the latency
+// of each wave's LDS reads and matrix-core results behind the others.
+constexpr int kCodeSlots1 = 8;
+constexpr uint32_t kCodeMask1 = kCodeSlots1 * 1024 - 1;
+constexpr int kMetaSlots1 = 4;
+constexpr uint32_t kMetaMask1 = kMetaSlots1 * 512 - 1;
+constexpr int kWaveLds1 = kCodeSlots1 * 1024 + kMetaSlots1 * 512;   // bytes per wave
+
+// The b code loads of one block, code slot i at ring offset (c0 + 1024 i) & mask.
+template <int B>
+__device__ __forceinline__ void issue_codes1(const uint8_t* cp, const uint32_t (&voff)[8], uint32_t ring,
+                                             uint32_t c0) {
+#pragma unroll
+  for (int q = 0; q < B; ++q) dma16(cp, voff[q], ring, (c0 + 1024 * q) & kCodeMask1);
+}
+
+template <int W0, int W1, class Refill>
+__device__ __forceinline__ void block1(const u32x4* code, const u32x4* meta, uint32_t cj, uint32_t mj, float (&acc)[4],
+                                       Refill&& refill) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const u32x4 sz = meta[(mj >> 4) + r16];
+  half8 xa[4][1];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) xa[kt][0] = __builtin_bit_cast(half8, meta[(mj >> 4) + 16 + 4 * kt + g]);
+  u32x4 w0[W0], w1[W1 ? W1 : 1];
+#pragma unroll
+  for (int q = 0; q < W0; ++q) w0[q] = code[(((cj + 1024 * q) & kCodeMask1) >> 4) + lane];
+#pragma unroll
+  for (int q = 0; q < W1; ++q) w1[q] = code[(((cj + 1024 * (W0 + q)) & kCodeMask1) >> 4) + lane];
+  wait_lds();
+  refill();
+
+  const half8 ones = as_half8(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
+  f32x4 xsum = f32x4{0, 0, 0, 0}, c0[4][1], c1[4][1];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) c0[rt][0] = c1[rt][0] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) xsum = mfma16(xa[kt][0], ones, xsum);
+  plane_mma<W0, 1>(w0, xa, c0);
+  if constexpr (W1 != 0) plane_mma<W1, 1>(w1, xa, c1);
+  constexpr int W1g = W1 ? W1 : 1;
+  constexpr float k0[4] = {pow2(24 - PlaneGeom<W0>::off(0)), pow2(24 - PlaneGeom<W0>::off(1)),
+                           pow2(24 - PlaneGeom<W0>::off(2)), pow2(24 - PlaneGeom<W0>::off(3))};
+  constexpr float k1[4] = {pow2(24 + W0 - PlaneGeom<W1g>::off(0)), pow2(24 + W0 - PlaneGeom<W1g>::off(1)),
+                           pow2(24 + W0 - PlaneGeom<W1g>::off(2)), pow2(24 + W0 - PlaneGeom<W1g>::off(3))};
+  // every row of the tiles is the one token: use element 0
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const float s = lo_half(sz[rt]), z = hi_half(sz[rt]);
+    float t = c0[rt][0][0] * k0[rt];
+    if constexpr (W1 != 0) t = __builtin_fmaf(c1[rt][0][0], k1[rt], t);
+    acc[rt] = __builtin_fmaf(s, __builtin_fmaf(-z, xsum[0], t), acc[rt]);
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode1_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int br = blockIdx.x / a.nseg, seg = blockIdx.x - br * a.nseg;
+  const int wg_begin = seg * a.seg_cols;
+  const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
+  const int w_begin = wg_begin + (wg_cols * wave) / NW;
+  const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
+  uint32_t voff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) voff[q] = 16 * lane + 1024 * q;
+
+  __shared__ u32x4 lds[NW * kWaveLds1 / 16];   // per-wave rings; reused for the reduction
+  const u32x4* code = lds + wave * (kWaveLds1 / 16);
+  const u32x4* meta = code + kCodeSlots1 * 64;
+  const uint32_t code_lds = lds_addr(code), meta_lds = lds_addr(meta);
+
+  float acc[4] = {0, 0, 0, 0};
+  for (int col0 = w_begin; col0 < w_end; col0 += 64) {
+    const int S = min(64, w_end - col0);
+    const bool in = lane < S;
+    const size_t blk0 = size_t(br) * a.nbc + col0;
+    const int bvec = in ? int(a.bits[blk0 + lane]) : 0;
+    const int o0 = int(a.offs[blk0]);
+    // the compiler tracks only these loads: wait for them before any ring load
+    wait_vmcnt<0>();
+    // the chunk's blocks are consecutive in the image: scale/zero records,
+    // activation columns and codes are three contiguous streams
+    const uint32_t* szp = a.sz + blk0 * 64;
+    const _Float16* xp = a.x + size_t(col0) * 128;
+    const uint8_t* cp = a.codes + size_t(uniform(o0)) * 1024;
+    int jn = 0, cfree = kCodeSlots1, mfree = kMetaSlots1, issued = 0;
+    uint32_t cn = 0, mn = 0;   // ring offsets of the next block to issue
+    auto fill = [&]() {
+      while (jn < S) {
+        const int bn = uniform(__builtin_amdgcn_readlane(bvec, jn));
+        if (bn > cfree || mfree == 0) break;
+        dma4(szp, 4 * lane, meta_lds, mn);
+        dma4(xp, 4 * lane, meta_lds, mn + 256);
+        switch (bn) {
+          case 1: issue_codes1<1>(cp, voff, code_lds, cn); break;
+          case 2: issue_codes1<2>(cp, voff, code_lds, cn); break;
+          case 3: issue_codes1<3>(cp, voff, code_lds, cn); break;
+          case 4: issue_codes1<4>(cp, voff, code_lds, cn); break;
+          case 6: issue_codes1<6>(cp, voff, code_lds, cn); break;
+          default: issue_codes1<8>(cp, voff, code_lds, cn); break;
+        }
+        szp += 64;
+        xp += 128;
+        cp += 1024 * bn;
+        cn = (cn + 1024 * bn) & kCodeMask1;
+        mn = (mn + 512) & kMetaMask1;
+        cfree -= bn;
+        mfree -= 1;
+        issued += 2 + bn;
+        ++jn;
+      }
+    };
+    fill();
+    uint32_t cj = 0, mj = 0;
+    int done = 0;
+    for (int j = 0; j < S; ++j) {
+      const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
+      done += 2 + bj;
+      wait_vmcnt_at_most(issued - done);
+      auto refill = [&]() {
+        cfree += bj;
+        mfree += 1;
+        fill();
+      };
+      switch (bj) {
+        case 1: block1<1, 0>(code, meta, cj, mj, acc, refill); break;
+        case 2: block1<2, 0>(code, meta, cj, mj, acc, refill); break;
+        case 3: block1<2, 1>(code, meta, cj, mj, acc, refill); break;
+        case 4: block1<4, 0>(code, meta, cj, mj, acc, refill); break;
+        case 6: block1<4, 2>(code, meta, cj, mj, acc, refill); break;
+        default: block1<4, 4>(code, meta, cj, mj, acc, refill); break;
+      }
+      cj = (cj + 1024 * bj) & kCodeMask1;
+      mj = (mj + 512) & kMetaMask1;
+    }
+  }
+  __syncthreads();
+
+  // waves meet in LDS; wave w < 4 adds row tile w over the waves in order
+  static_assert(NW * 4 * 64 * 4 + 4 <= NW * kWaveLds1, "reduction fits in the rings");
+  float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(lds);
+  int* s_last = reinterpret_cast<int*>(lds) + NW * 4 * 64;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt];
+  __syncthreads();
+  if (wave < 4 && g == 0) {
+    const int rt = wave;
+    const int n = br * 64 + 16 * rt + r16;
+    float s = red[0][rt][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += red[w][rt][lane];
+    if (a.nseg == 1)
+      a.y[n] = (_Float16)s;
+    else
+      __hip_atomic_store(a.part + size_t(seg) * a.N + n, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (a.nseg == 1) return;
+
+  // K segments: the barrier waits for every partial store of the workgroup;
+  // the workgroup that completes the block row's count sums the segments.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(a.ctr + br, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == uint32_t(a.nseg - 1);
+    if (last) __hip_atomic_store(a.ctr + br, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last || threadIdx.x >= 64) return;
+  const int n = br * 64 + lane;
+  const float* pp = a.part + n;
+  float s = 0.0f;
+  for (int s0 = 0; s0 < a.nseg; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = s0 + i < a.nseg ? __hip_atomic_load(pp + size_t(s0 + i) * a.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  a.y[n] = (_Float16)s;
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int N, int K, int M) {
   DecodePlan p;
   const int nbr = N / 64, nbc = K / 128;
   p.nw = 4;
-  // one workgroup per block row when that gives about 8 waves per CU;
-  // otherwise split K into segments of at least 2 columns per wave, capped
-  // by the partial-sum traffic (nseg * M * N * 8 bytes against ~N * K / 2)
-  const int target_waves = 2048;
+  // 4-wave workgroups resident per CU: four for one token (40 KiB of LDS
+  // rings each), two for M <= 16 (64 KiB), one for larger M (128 KiB).
+  // One workgroup per block row when that fills the resident slots; else
+  // split K into as many segments as still fit in one resident wave of
+  // workgroups, with at least 2 columns per wave, capped by the partial-sum
+  // traffic (nseg * M * N * 8 bytes against ~N * K / 2).
+  const int resident = (M == 1 ? 4 : M <= 16 ? 2 : 1) * 256;
   int nseg = 1;
-  if (nbr * p.nw < target_waves) {
-    nseg = (target_waves + nbr * p.nw - 1) / (nbr * p.nw);
+  if (nbr < resident) {
+    nseg = resident / nbr;
     nseg = min(nseg, max(1, nbc / (2 * p.nw)));
     nseg = min(nseg, max(1, K / (64 * M)));
   }
@@ -427,10 +623,12 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   a.nseg = plan.nseg;
   const dim3 grid(unsigned(im.nbr * plan.nseg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 16)
-    hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
+  if (M == 1)
+    hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a);
+  else if (M <= 16)
+    hipLaunchKernelGGL((decode_kernel<4, 1, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<4, 2, false>), grid, dim3(256), 0, s, a);
   return int(hipGetLastError());
 }
 

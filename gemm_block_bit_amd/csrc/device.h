@@ -44,12 +44,4 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Code pair `slot` of a plane word of width W (W = 1, 2, 4): the low-half
-// code in bits [W slot, W slot + W), the high-half code 16 bits above.
-template <int W>
-__device__ __forceinline__ uint32_t pair_bits(uint32_t word, int slot) {
-  constexpr uint32_t mask = ((1u << W) - 1u) * 0x00010001u;
-  return (word >> (W * slot)) & mask;
-}
-
 }  // namespace gbb

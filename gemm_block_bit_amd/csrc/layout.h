@@ -27,7 +27,13 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 //   offs  u32 [nblk + 1]       start of each block's codes, in KiB
 //   sz    u32 [nblk][16][4]    entry [r][t] is row 16 t + r of the block:
 //                              fp16 s (low half), fp16 z (high half)
-//   codes 1024 * b bytes per block, planes of width 1|2|4 (low bits first)
+//   codes 1024 * b bytes per block, planes of width 1|2|4 (low bits first).
+//         A plane of width w is w slots of 1 KiB; lane l's 16 bytes of slot j
+//         are four u32 words c = 0..3 whose bit field i (width w) of the low
+//         half holds the code of row 16 rt + l % 16, column
+//         32 kt + 8 (l / 16) + 2 c, and of the high half the next column, for
+//         4 kt + rt = j (16 / w) + i.  So the four words of a slot at one field
+//         are one v_mfma_f32_16x16x32_f16 B operand (tile rt, kt).
 struct BlockLayout {
   size_t nblk, bits_off, offs_off, sz_off, codes_off;
 };

@@ -176,20 +176,19 @@ static size_t packed_bytes_unchecked(const uint8_t* bits, int N, int K) {
 static void write_plane(const uint8_t (*q)[128], int w, int sh, uint8_t* dst) {
   const int npair = 16 / w;
   const uint32_t mask = (1u << w) - 1u;
-  for (int lane = 0; lane < 64; ++lane) {
-    for (int d = 0; d < 4 * w; ++d) {
-      uint32_t word = 0;
-      for (int i = 0; i < npair; ++i) {
-        const int P = d * npair + i, u = P >> 2, p = P & 3;
-        const int rt = u >> 2, kt = u & 3;
-        const int row = 16 * rt + (lane & 15);
-        const int col = 32 * kt + 8 * (lane >> 4) + 2 * p;
-        word |= ((uint32_t(q[row][col]) >> sh) & mask) << (w * i);
-        word |= ((uint32_t(q[row][col + 1]) >> sh) & mask) << (16 + w * i);
+  for (int j = 0; j < w; ++j)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int c = 0; c < 4; ++c) {
+        uint32_t word = 0;
+        for (int i = 0; i < npair; ++i) {
+          const int u = j * npair + i, kt = u >> 2, rt = u & 3;
+          const int row = 16 * rt + (lane & 15);
+          const int col = 32 * kt + 8 * (lane >> 4) + 2 * c;
+          word |= ((uint32_t(q[row][col]) >> sh) & mask) << (w * i);
+          word |= ((uint32_t(q[row][col + 1]) >> sh) & mask) << (16 + w * i);
+        }
+        std::memcpy(dst + 1024 * j + 16 * lane + 4 * c, &word, 4);
       }
-      std::memcpy(dst + 1024 * (d >> 2) + 16 * lane + 4 * (d & 3), &word, 4);
-    }
-  }
 }
 
 }  // namespace gbb

@@ -41,50 +41,62 @@ struct PrefillArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
-// Dequantize the two row tiles rt0, rt0 + 1 of one block into LDS rows
-// base_row + 16 rt + r16.  W0/W1 are the plane widths (W1 = 0: one plane).
-template <int W0, int W1>
-__device__ __forceinline__ void dequant_rows(const uint8_t* __restrict__ blk_codes, const uint32_t* __restrict__ blk_sz,
-                                             int rt0, int lane, u32x4* __restrict__ lds, int base_row) {
-  constexpr int NP0 = 16 / W0;
-  constexpr int NP1 = W1 ? 16 / W1 : 1;
-  const int g = lane >> 4, r16 = lane & 15;
-  const uint8_t* cb = blk_codes + 16 * lane;
-  // dwords of row tile rt are [rt W, rt W + W) of each plane: slot (rt W) / 4
-  uint32_t w0[2 * W0], w1[2 * (W1 ? W1 : 1)];
+// Code pairs of the column half h (column tiles kt = 2h, 2h + 1) of one plane
+// of width W: tile 4 kt + rt is field (4 kt + rt) % (16 / W) of slot
+// (4 kt + rt) / (16 / W), so the half lives in the slots [8h / NP, ..] and,
+// for W = 1, in the byte of each half word selected by h.
+template <int W>
+struct PlaneHalf {
+  static constexpr int NP = 16 / W;
+  static constexpr int NS = W == 1 ? 1 : 8 / NP;  // slots of one half
+  uint32_t w[NS][4];
+  __device__ __forceinline__ void load(const uint8_t* cb, int h) {
 #pragma unroll
-  for (int j = 0; j < 2 * W0; ++j) {
-    const int d = rt0 * W0 + j;
-    w0[j] = *reinterpret_cast<const uint32_t*>(cb + 1024 * (d >> 2) + 4 * (d & 3));
-  }
-  if constexpr (W1 != 0) {
+    for (int t = 0; t < NS; ++t) {
+      const u32x4 v = ld16(reinterpret_cast<const uint32_t*>(cb + 1024 * ((8 * h) / NP + t)));
 #pragma unroll
-    for (int j = 0; j < 2 * W1; ++j) {
-      const int d = rt0 * W1 + j;
-      w1[j] = *reinterpret_cast<const uint32_t*>(cb + 1024 * (W0 + (d >> 2)) + 4 * (d & 3));
+      for (int c = 0; c < 4; ++c) w[t][c] = W == 1 ? v[c] >> (8 * h) : v[c];
     }
   }
+  // pair of word c of local tile ul = 4 (kt - 2h) + rt
+  __device__ __forceinline__ uint32_t pair(int ul, int c) const {
+    return (w[ul / NP][c] >> (W * (ul % NP))) & (((1u << W) - 1u) * 0x00010001u);
+  }
+};
+
+// Dequantize the column half h of one block into LDS rows base_row + 0..63:
+// exactly fp16((q - z) s), as (1024 + q) - (1024 + z) is an exact small
+// integer in fp16 and the product is rounded once.
+template <int W0, int W1>
+__device__ __forceinline__ void dequant_half(const uint8_t* __restrict__ blk_codes, const uint32_t* __restrict__ blk_sz,
+                                             int h, int lane, u32x4* __restrict__ lds, int base_row) {
+  const int g = lane >> 4, r16 = lane & 15;
+  const uint8_t* cb = blk_codes + 16 * lane;
+  PlaneHalf<W0> p0;
+  PlaneHalf<W1 ? W1 : 1> p1;
+  p0.load(cb, h);
+  if constexpr (W1 != 0) p1.load(cb + 1024 * W0, h);
+  // entry 4 r16 + rt of the block's scale/zero record is row 16 rt + r16
+  const u32x4 sz = ld16(blk_sz + 4 * r16);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rt = rt0 + h;
-    const uint32_t e = blk_sz[4 * r16 + rt];
+  for (int rt = 0; rt < 4; ++rt) {
+    const uint32_t e = sz[rt];
     const half2v s2 = as_half2((e & 0xffffu) * 0x00010001u);
     const _Float16 zf = __builtin_bit_cast(_Float16, (unsigned short)(e >> 16));
     const _Float16 nz = -((_Float16)1024.0f + zf);  // exact: an integer below 2048
     const half2v z2 = {nz, nz};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int u = 4 * rt + kt;
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ul = 4 * k2 + rt;
       uint32_t o[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int P = 4 * u + p;
-        uint32_t q = pair_bits<W0>(w0[P / NP0 - rt0 * W0], P % NP0);
-        if constexpr (W1 != 0) q |= pair_bits<W1>(w1[P / NP1 - rt0 * W1], P % NP1) << W0;
+      for (int c = 0; c < 4; ++c) {
+        uint32_t q = p0.pair(ul, c);
+        if constexpr (W1 != 0) q |= p1.pair(ul, c) << W0;
         const half2v v = (as_half2(q | kMagicPair) + z2) * s2;
-        o[p] = as_u32(v);
+        o[c] = as_u32(v);
       }
-      lds[swz(base_row + 16 * rt + r16, 4 * kt + g)] = u32x4{o[0], o[1], o[2], o[3]};
+      lds[swz(base_row + 16 * rt + r16, 4 * (2 * h + k2) + g)] = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
 }
@@ -116,9 +128,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  // weight work of this wave: block row n0/64 + (wave >> 1), row tiles 2 (wave & 1) + {0, 1}
+  // weight work of this wave: block row n0/64 + (wave >> 1), column half wave & 1
   const int br = (n0 >> 6) + (wave >> 1);
-  const int rt0 = 2 * (wave & 1);
+  const int hk = wave & 1;
   const int wrow = 64 * (wave >> 1);
 
   for (int bc = 0; bc < a.nbc; ++bc) {
@@ -142,18 +154,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const uint8_t* cb = a.codes + size_t(uniform(int(a.offs[blk]))) * 1024;
       const uint32_t* sb = a.sz + size_t(blk) * 64;
       switch (b) {
-        case 1: dequant_rows<1, 0>(cb, sb, rt0, lane, ws, wrow); break;
-        case 2: dequant_rows<2, 0>(cb, sb, rt0, lane, ws, wrow); break;
-        case 3: dequant_rows<2, 1>(cb, sb, rt0, lane, ws, wrow); break;
-        case 4: dequant_rows<4, 0>(cb, sb, rt0, lane, ws, wrow); break;
-        case 6: dequant_rows<4, 2>(cb, sb, rt0, lane, ws, wrow); break;
-        default: dequant_rows<4, 4>(cb, sb, rt0, lane, ws, wrow); break;
+        case 1: dequant_half<1, 0>(cb, sb, hk, lane, ws, wrow); break;
+        case 2: dequant_half<2, 0>(cb, sb, hk, lane, ws, wrow); break;
+        case 3: dequant_half<2, 1>(cb, sb, hk, lane, ws, wrow); break;
+        case 4: dequant_half<4, 0>(cb, sb, hk, lane, ws, wrow); break;
+        case 6: dequant_half<4, 2>(cb, sb, hk, lane, ws, wrow); break;
+        default: dequant_half<4, 4>(cb, sb, hk, lane, ws, wrow); break;
       }
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) ws[swz(wrow + 16 * (rt0 + h) + r16, 4 * kt + g)] = u32x4{0, 0, 0, 0};
+        for (int k2 = 0; k2 < 2; ++k2) ws[swz(wrow + 16 * rt + r16, 4 * (2 * hk + k2) + g)] = u32x4{0, 0, 0, 0};
     }
     __syncthreads();
 #pragma unroll

@@ -74,24 +74,26 @@ def block_image_size(bits: np.ndarray) -> int:
 def _plane_codes(plane: np.ndarray, w: int) -> np.ndarray:
     """Decode one plane for many blocks.
 
-    plane: uint8 [nb][w*1024].  Returns uint8 [nb][64][128] (row, column)."""
+    plane: uint8 [nb][w*1024].  Slot j (1 KiB) holds, for lane l, four little-
+    endian words c = 0..3; bit field i (width w) of the low half of word c is
+    the code of row 16*rt + l%16, column 32*kt + 8*(l//16) + 2*c, the same
+    field of the high half that of the next column, with j*(16//w) + i =
+    4*kt + rt.  Returns uint8 [nb][64][128] (row, column)."""
     nb = plane.shape[0]
-    dw = plane.view("<u4").reshape(nb, w, 64, 4)            # [blk][t][lane][c]
-    dw = dw.transpose(0, 2, 1, 3).reshape(nb, 64, 4 * w)    # [blk][lane][d]
+    words = plane.view("<u4").reshape(nb, w, 64, 4)          # [blk][slot][lane][c]
     npair = 16 // w
     mask = (1 << w) - 1
     out = np.empty((nb, 64, 128), np.uint8)
     lane = np.arange(64)
-    for d in range(4 * w):
-        word = dw[:, :, d].astype(np.uint64)
-        for i in range(npair):
-            P = d * npair + i
-            u, p = divmod(P, 4)
-            rt, kt = divmod(u, 4)
-            row = 16 * rt + lane % 16
-            col = 32 * kt + 8 * (lane // 16) + 2 * p
-            out[:, row, col] = ((word >> np.uint64(w * i)) & np.uint64(mask)).astype(np.uint8)
-            out[:, row, col + 1] = ((word >> np.uint64(16 + w * i)) & np.uint64(mask)).astype(np.uint8)
+    for j in range(w):
+        for c in range(4):
+            word = words[:, j, :, c].astype(np.uint64)
+            for i in range(npair):
+                kt, rt = divmod(j * npair + i, 4)
+                row = 16 * rt + lane % 16
+                col = 32 * kt + 8 * (lane // 16) + 2 * c
+                out[:, row, col] = ((word >> np.uint64(w * i)) & np.uint64(mask)).astype(np.uint8)
+                out[:, row, col + 1] = ((word >> np.uint64(16 + w * i)) & np.uint64(mask)).astype(np.uint8)
     return out
 
 

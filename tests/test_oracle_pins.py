@@ -289,21 +289,18 @@ def _slow_block_image(q, s16, z16, bits):
             shift = 0
             for w in planes[b]:
                 npair = 16 // w
-                for lane in range(64):
-                    for d in range(4 * w):
-                        t, c = divmod(d, 4)
-                        word = 0
-                        for i in range(npair):
-                            P = d * npair + i
-                            u, p = divmod(P, 4)
-                            rt, kt = divmod(u, 4)
-                            row = 64 * br + 16 * rt + lane % 16
-                            col = 128 * bc + 32 * kt + 8 * (lane // 16) + 2 * p
-                            ca = (int(q[row, col]) >> shift) & ((1 << w) - 1)
-                            cb = (int(q[row, col + 1]) >> shift) & ((1 << w) - 1)
-                            word |= (ca << (w * i)) | (cb << (16 + w * i))
-                        o = base + 1024 * t + 16 * lane + 4 * c
-                        buf[o:o + 4] = word.to_bytes(4, "little")
+                words = [0] * (256 * w)          # u32 words of the plane
+                # place each code: row tile rt, column tile kt, lane group g,
+                # word c, half h; tile 4 kt + rt is field i of slot j
+                for r in range(64):
+                    for k in range(128):
+                        rt, r16 = divmod(r, 16)
+                        kt, g, c, h = k // 32, (k % 32) // 8, (k % 8) // 2, k % 2
+                        j, i = divmod(4 * kt + rt, npair)
+                        code = (int(q[64 * br + r, 128 * bc + k]) >> shift) & ((1 << w) - 1)
+                        words[256 * j + 4 * (16 * g + r16) + c] |= code << (16 * h + w * i)
+                for n, word in enumerate(words):
+                    buf[base + 4 * n:base + 4 * n + 4] = word.to_bytes(4, "little")
                 base += 1024 * w
                 shift += w
             kib += b
