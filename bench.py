@@ -2,10 +2,13 @@
 
 Headline (one JSON line): decode (M = 1) weight GB/s over Llama-3-8B-shaped
 decoder layers -- q, k, v, o, gate, up, down at 64x128 blocks with bitwidths
-from {1,2,3,4,6,8} (mean 3.1) -- against the 8 TB/s HBM peak.  One step is
-one token through a stack of distinct layer copies whose packed weights
-(732 MB) exceed the 256 MiB Infinity Cache, so every weight byte comes from
-HBM.  The step is replayed from a HIP graph of its 56 launches.
+from {1,2,3,4,6,8} (mean 3.1) -- against the 8 TB/s HBM peak.  Projections
+that read the same input are packed as one matrix, as serving stacks do:
+q|k|v (6144 x 4096) and gate|up (28672 x 4096), so a layer is four launches
+(qkv, o, gate_up, down).  One step is one token through a stack of distinct
+layer copies whose packed weights (732 MB) exceed the 256 MiB Infinity
+Cache, so every weight byte comes from HBM.  The step is replayed from a HIP
+graph of its 32 launches.
 
 Also reported: M = 8 on the same layers, the 70B-shaped layer at M = 1, the
 M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
@@ -46,24 +49,30 @@ def weight_bytes(bits: np.ndarray) -> int:
     return 1024 * int(bits.astype(np.int64).sum()) + 256 * nblk + nblk + 4 * (nblk + 1)
 
 
+# launch groups of a decoder layer: projections that share their input are
+# stacked along the output rows into one packed matrix
+GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
 class DecodeLayerSet:
-    """R copies of one decoder layer's packed projections on the GPU, with
+    """R copies of one decoder layer's packed launch groups on the GPU, with
     their activations, outputs and one shared split-K workspace."""
 
     def __init__(self, torch, gbb, synth, gen, copies, M, dev):
         self.torch, self.gbb = torch, gbb
         self.M = M
-        self.projs = []
         host = []
-        for i in range(7):
-            p, W, bits = gen(i)
+        for name, idx in GROUPS:
+            parts = [gen(i) for i in idx]
+            W = np.concatenate([W for (_, W, _) in parts])
+            bits = np.concatenate([b for (_, _, b) in parts])
             img, _, _ = gbb.pack_blocks(W, bits)
-            host.append((p, img, bits))
-            del W
-        self.images = [[torch.from_numpy(img).to(dev) for (_, img, _) in host] for _ in range(copies)]
-        self.shapes = [(p.N, p.K) for (p, _, _) in host]
-        self.names = [p.name for (p, _, _) in host]
-        self.bytes = [weight_bytes(b) for (_, _, b) in host]
+            host.append((name, W.shape, img, bits))
+            del W, parts
+        self.images = [[torch.from_numpy(img).to(dev) for (_, _, img, _) in host] for _ in range(copies)]
+        self.shapes = [shape for (_, shape, _, _) in host]
+        self.names = [name for (name, _, _, _) in host]
+        self.bytes = [weight_bytes(b) for (_, _, _, b) in host]
         self.layer_bytes = sum(self.bytes)
         self.copies = copies
         g = np.random.default_rng(7)
@@ -139,6 +148,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads, no cpu baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB elementwise copy (read 256 MiB, write 256 MiB) five times, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the fused dequant-GEMM path has no multi-GPU component here "
@@ -155,8 +167,17 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} CUs={props.multi_processor_count}")
 
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("calibration copy: 5 x (read 268435456 B, write 268435456 B)")
+        del src, dst
+
     # ---------------- headline: Llama-3-8B layers, decode M = 1 ----------------
-    log("packing Llama-3-8B-shaped layer (7 projections)")
+    log("packing Llama-3-8B-shaped layer (qkv, o, gate_up, down)")
     L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
     log(f"layer weight bytes {L8.layer_bytes / 1e6:.1f} MB x {L8.copies} copies")
     h = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
@@ -167,8 +188,9 @@ def main():
     log(f"decode M=1: {sec * 1e6:.1f} us/step, {value:.0f} GB/s")
 
     # per-launch events over the same timed work (eager launches, one stream)
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)] for _ in range(L8.copies)]
-    durs = np.zeros((args.steps, L8.copies, 7))
+    ng = len(L8.shapes)
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ng)] for _ in range(L8.copies)]
+    durs = np.zeros((args.steps, L8.copies, ng))
     for _ in range(args.warmup):
         L8.step(h())
     torch.cuda.synchronize()
@@ -176,7 +198,7 @@ def main():
         L8.step(h(), ev)
         torch.cuda.synchronize()
         for r in range(L8.copies):
-            for i in range(7):
+            for i in range(ng):
                 durs[s, r, i] = ev[r][i][0].elapsed_time(ev[r][i][1]) * 1e3   # us
     mean_us = float(durs.mean())
     mean_bytes = float(np.mean(L8.bytes))
@@ -189,7 +211,7 @@ def main():
     achieved = mean_bytes / mean_us / 1e3
     log(f"decode kernel: mean {mean_us:.2f} us/launch, {achieved:.0f} GB/s; per projection {per_proj}")
 
-    extra = {"per_projection_m1": per_proj,
+    extra = {"per_launch_group_m1": per_proj,
              "kernel_sum_us_per_step": round(float(durs.sum(axis=(1, 2)).mean()), 1),
              "graph_step_us": round(sec * 1e6, 1), "host_wall_us_per_step": round(wall * 1e6, 1)}
 
@@ -208,8 +230,6 @@ def main():
         log(f"decode M=8: {total_bytes / s8 / 1e9:.0f} GB/s")
         del L8b
 
-    # keep the headline layers for the cpu baseline sample; free the device copies
-    host_layer = [(L8.shapes[i], L8.names[i]) for i in range(7)]
     del L8
     torch.cuda.empty_cache()
 
@@ -269,7 +289,7 @@ def main():
 
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
-        cpu = cpu_baseline(gbb, synth, host_layer)
+        cpu = cpu_baseline(gbb, synth)
 
     out = {
         "metric": "fused dequant-GEMM: weight GB/s (%HBM peak) at M=1; TFLOP/s (%MFMA) at M=2048",
@@ -285,13 +305,14 @@ def main():
         "dtype": "fp16",
         "data": "synthetic (seeded random weights and activations of Llama-3 layer shapes)",
         "config": {"workload": "llama3_8b_layer_decode_m1", "layers_per_step": LAYER_COPIES_8B,
-                   "projections": "q,k,v,o,gate,up,down", "M": 1, "block": "64x128",
+                   "projections": "q,k,v,o,gate,up,down", "launches_per_layer": "qkv,o,gate_up,down",
+                   "M": 1, "block": "64x128",
                    "bits": "{1,2,3,4,6,8} mean 3.10", "group": 128,
                    "weight_MB_per_step": round(total_bytes / 1e6, 1), "parallelism": "single GPU"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 3), "traffic": None,
-                     "kernel": "decode_kernel<1>", "mean_launch_us": round(mean_us, 3),
+                     "kernel": "decode1_kernel<4>", "mean_launch_us": round(mean_us, 3),
                      "mean_algorithmic_bytes_per_launch": round(mean_bytes)},
         "cpu_baseline": cpu,
         "extra": extra,
@@ -299,7 +320,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(gbb, synth, host_layer):
+def cpu_baseline(gbb, synth):
     """The oracle as it stands -- its own unpacker, exact fp32 dequant and an
     fp64 product -- over one copy of the headline layer (7 projections, M=1)."""
     from threadpoolctl import threadpool_info

@@ -21,13 +21,15 @@
 //  * The matrix cores form C = sum_k x_k q_k 2^(o - 24) per 16-row tile and
 //    X = sum_k x_k against an all-ones B operand; the epilogue adds
 //    s (2^(24 - o) C - z X) = s sum_k x_k (q_k - z) to fp32 accumulators.
-//  * Each wave streams its blocks through a 16-slot (32 for M > 16) LDS ring
-//    filled by global->LDS loads (global_load_lds_dword[x4]): per block one
-//    slot for the scale/zero record (and, for one token, the activations),
-//    the activation slots of larger batches and the b code slots.  Blocks are
-//    issued ahead while they fit, so the in-flight data costs no registers;
-//    the wait for a block is a vmcnt bound, and a block's slots are refilled
-//    as soon as its LDS reads have completed.
+//  * Each wave streams its blocks through LDS rings filled by global->LDS
+//    loads (global_load_lds_dword[x4]), so data in flight costs no
+//    registers.  For M > 1 one ring of 1 KiB slots (16, or 32 for M > 16)
+//    holds per block a scale/zero slot, ceil(M / 4) activation slots and the
+//    b code slots.  A single token has its own kernel with an 8-slot code ring
+//    and a 4-entry ring of 512-byte scale/zero + activation records: 10 KiB
+//    per wave, 16 waves per CU.  Blocks are issued ahead while they fit; the
+//    wait for a block is a vmcnt bound, and a block's slots are refilled as
+//    soon as its LDS reads have completed.
 //  * With K segments, partial sums cross workgroups (and XCDs) through
 //    device-scope (sc1) stores and loads, which need no cache writeback; the
 //    last workgroup of a block row (an atomic counter that resets itself)
@@ -53,7 +55,7 @@ struct DecodeArgs {
 };
 
 // Ring slots per wave (a power of two): a block takes 1 + nx + b slots
-// (nx = activation slots: 0 for one token, ceil(M / 4) otherwise).
+// (nx = ceil(M / 4) activation slots of four tokens each).
 template <int MT>
 struct Ring {
   static constexpr int kSlots = MT == 1 ? 16 : 32;
@@ -152,27 +154,20 @@ __device__ __forceinline__ constexpr float pow2(int e) {
 
 // One block of planes W0 (shift 0) and W1 (shift W0; 0 = none) whose records
 // start at ring byte offset sb: read them, let `refill` reuse the slots, then
-// acc += s (sum over planes of 2^(24 + shift - o) C - z X).  ONE: a single
-// token, whose activations share the scale/zero slot; all rows of A are that
-// token, so every row of an accumulator tile holds the same sums.
-template <int W0, int W1, int MT, bool ONE, class Refill>
+// acc += s (sum over planes of 2^(24 + shift - o) C - z X).
+template <int W0, int W1, int MT, class Refill>
 __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx, int M, f32x4 (&acc)[4][MT],
                                           Refill&& refill) {
   constexpr uint32_t MASK = Ring<MT>::kMask;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const u32x4 sz = ring[(sb >> 4) + r16];
   half8 xa[4][MT];
-  if constexpr (ONE) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) xa[kt][0] = __builtin_bit_cast(half8, ring[(sb >> 4) + 16 + 4 * kt + g]);
-  } else {
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(16 * mt + r16, M - 1);
+    const u32x4* xr = ring + (((sb + 1024 * (1 + (m >> 2))) & MASK) >> 4);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = min(16 * mt + r16, M - 1);
-      const u32x4* xr = ring + (((sb + 1024 * (1 + (m >> 2))) & MASK) >> 4);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
-    }
+    for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
   }
   u32x4 w0[W0], w1[W1 ? W1 : 1];
   {
@@ -200,7 +195,6 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx
   plane_mma<W0, MT>(w0, xa, c0);
   if constexpr (W1 != 0) plane_mma<W1, MT>(w1, xa, c1);
   // lane holds tokens 16 mt + 4 g + v
-  constexpr int NV = ONE ? 1 : 4;
   constexpr int W1g = W1 ? W1 : 1;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -212,7 +206,7 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
+      for (int v = 0; v < 4; ++v) {
         float t = c0[rt][mt][v] * k0[rt];
         if constexpr (W1 != 0) t = __builtin_fmaf(c1[rt][mt][v], k1[rt], t);
         acc[rt][mt][v] = __builtin_fmaf(s, __builtin_fmaf(-z, xsum[mt][v], t), acc[rt][mt][v]);
@@ -220,7 +214,7 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx
   }
 }
 
-template <int NW, int MT, bool ONE>
+template <int NW, int MT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int R = Ring<MT>::kSlots;
   constexpr uint32_t MASK = Ring<MT>::kMask;
@@ -234,9 +228,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
   const int w_begin = wg_begin + (wg_cols * wave) / NW;
   const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
-  const int M = ONE ? 1 : a.M;
-  const int nx = ONE ? 0 : (M + 3) / 4;   // activation slots per block
-  const int xd = ONE ? 1 : nx;            // activation loads per block
+  const int M = a.M;
+  const int nx = (M + 3) / 4;   // activation slots (and loads) per block
   // byte offset of lane's activation chunk in activation record xi
   uint32_t xoff[8];
 #pragma unroll
@@ -278,11 +271,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
         if (used + ns > R) break;
         dma4(szp, 4 * lane, ring_lds, sbn);
         szp += 64;
-        if constexpr (ONE) {
-          dma4(xp, 4 * lane, ring_lds, sbn + 256);
-        } else {
-          for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
-        }
+        for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
         xp += 128;
         uint32_t sc = sbn + 1024 * (1 + nx);
         for (int q = 0; q < bn; ++q) {
@@ -292,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
         }
         sbn = sc & MASK;
         used += ns;
-        issued += 1 + xd + bn;
+        issued += 1 + nx + bn;
         ++jn;
       }
     };
@@ -301,19 +290,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
     int done = 0;      // loads of blocks 0..j
     for (int j = 0; j < S; ++j) {
       const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
-      done += 1 + xd + bj;
+      done += 1 + nx + bj;
       wait_vmcnt_at_most(issued - done);
       auto refill = [&]() {
         used -= 1 + nx + bj;
         fill();
       };
       switch (bj) {
-        case 1: block_mma<1, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
-        case 2: block_mma<2, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
-        case 3: block_mma<2, 1, MT, ONE>(ring, sb, nx, M, acc, refill); break;
-        case 4: block_mma<4, 0, MT, ONE>(ring, sb, nx, M, acc, refill); break;
-        case 6: block_mma<4, 2, MT, ONE>(ring, sb, nx, M, acc, refill); break;
-        default: block_mma<4, 4, MT, ONE>(ring, sb, nx, M, acc, refill); break;
+        case 1: block_mma<1, 0, MT>(ring, sb, nx, M, acc, refill); break;
+        case 2: block_mma<2, 0, MT>(ring, sb, nx, M, acc, refill); break;
+        case 3: block_mma<2, 1, MT>(ring, sb, nx, M, acc, refill); break;
+        case 4: block_mma<4, 0, MT>(ring, sb, nx, M, acc, refill); break;
+        case 6: block_mma<4, 2, MT>(ring, sb, nx, M, acc, refill); break;
+        default: block_mma<4, 4, MT>(ring, sb, nx, M, acc, refill); break;
       }
       sb = (sb + 1024 * (1 + nx + bj)) & MASK;
     }
@@ -626,9 +615,9 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   if (M == 1)
     hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a);
   else if (M <= 16)
-    hipLaunchKernelGGL((decode_kernel<4, 1, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<4, 2, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
   return int(hipGetLastError());
 }
 
