@@ -250,6 +250,190 @@ __global__ __launch_bounds__(256) void w48_kernel(W48Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large batches: 128 tokens x 128 packed rows per workgroup.  Workgroups are
+// homogeneous: the first ceil(T8 / 8) row blocks hold 8-bit tiles, the rest
+// 4-bit tiles.  Per 128-column group everything the matrix cores read is
+// brought into LDS by global->LDS loads in MFMA fragment order -- activation
+// fragments gathered 16 tokens at a time, weight fragments as packed, the
+// group's weight scales and zero points -- so operand reads are conflict-free
+// lane-linear 16-byte reads and no staging registers are needed.  4-bit
+// fragments land raw and are expanded once per workgroup into int8 (q - z).
+// LDS is double-buffered: the next group's loads fly while the current group
+// runs; one wait and one barrier per group.  Wave (wm, wn) owns tokens
+// 64 wm + [0, 64) and rows 64 wn + [0, 64): 4 x 4 MFMA tiles, two k halves
+// per group.
+// ---------------------------------------------------------------------------
+constexpr int kTB = 128;   // tokens and packed rows per workgroup
+
+// LDS map (bytes): A[2] 16 KiB each, B[2] 16 KiB each, raw 4-bit staging
+// 8 KiB, weight scales[2] 256 B each, zero points 256 B
+constexpr int kLdsA = 0, kLdsB = 32768, kLdsRaw = 65536, kLdsS = 73728, kLdsZ = 74240, kLdsW48 = 74496;
+
+// global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
+// LDS address lds + 16 l (4 l).  No output registers: completion is waited
+// for with an explicit s_waitcnt vmcnt(0) before the barrier that publishes
+// the data.
+__device__ __forceinline__ void gdma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void gdma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+
+template <bool GA>   // GA: activation scales per (token, group), else per token
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void w48_tile_kernel(W48Args a) {
+  __shared__ u32x4 lds[kLdsW48 / 16];
+  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
+  const uint32_t lbase = lds_u32(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.x * kTB;
+  const int nb8 = (a.T8 + 7) / 8;
+  const bool q4 = int(blockIdx.y) >= nb8;
+  // first packed tile of this workgroup and the end of its row set
+  const int t0 = q4 ? a.T8 + (int(blockIdx.y) - nb8) * 8 : int(blockIdx.y) * 8;
+  const int tend = q4 ? a.T8 + a.T4 : a.T8;
+  const int G = a.K / 128, KT = a.K / 64;
+
+  // Loads of one group into buffer `buf`.  Wave w brings activation
+  // fragments f = w + 4 q (token tile f / 2, k half f % 2) and weight
+  // fragments f (row tile f / 2, k tile 2 grp + f % 2); wave 0 the scales,
+  // wave 1 the zero points.  Tokens and tiles past the end are clamped to the
+  // last valid one (read, then discarded).
+  auto issue = [&](int grp, int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = wave + 4 * q, i = f >> 1, h = f & 1;
+      const int m = min(m0 + 16 * i + r16, a.M - 1);
+      gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g,
+             lbase + kLdsA + buf * 16384 + f * 1024);
+      const int t = min(t0 + i, tend - 1), kt = 2 * grp + h;
+      if (!q4) {
+        gdma16(a.c8 + (size_t(t) * KT + kt) * 1024 + 16 * lane, lbase + kLdsB + buf * 16384 + f * 1024);
+      } else {
+        const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + kt) * 512;
+        gdma4(src + 4 * lane, lbase + kLdsRaw + f * 512);
+        gdma4(src + 256 + 4 * lane, lbase + kLdsRaw + f * 512 + 256);
+      }
+    }
+    if (wave == 0) {
+      const int t = min(t0 + (lane >> 3), tend - 1);
+      gdma4(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), lbase + kLdsS + buf * 256);
+    } else if (wave == 1 && q4) {
+      const int t = min(t0 + ((lane & 31) >> 2), tend - 1);
+      gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), lbase + kLdsZ);
+    }
+  };
+  // 4-bit: expand the raw fragments of this wave into int8 (q - z)
+  auto expand = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = wave + 4 * q, i = f >> 1;
+      const uint2 w = *reinterpret_cast<const uint2*>(base + kLdsRaw + f * 512 + 8 * lane);
+      const uint32_t z = base[kLdsZ + 16 * i + r16];
+      const i32x4 e = expand4(w, (128u - z) * 0x01010101u);
+      *reinterpret_cast<i32x4*>(base + kLdsB + buf * 16384 + f * 1024 + 16 * lane) = e;
+    }
+  };
+
+  f32x4 tot[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+  __syncthreads();
+  if (q4) {
+    expand(0);
+    __syncthreads();
+  }
+  for (int grp = 0; grp < G; ++grp) {
+    const int buf = grp & 1;
+    if (grp + 1 < G) issue(grp + 1, buf ^ 1);
+    const uint8_t* A = base + kLdsA + buf * 16384;
+    const uint8_t* B = base + kLdsB + buf * 16384;
+    const _Float16* S = reinterpret_cast<const _Float16*>(base + kLdsS + buf * 256);
+    i32x4 c[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[i][j] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[i] = *reinterpret_cast<const i32x4*>(A + (2 * (4 * wm + i) + h) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[j] = *reinterpret_cast<const i32x4*>(B + (2 * (4 * wn + j) + h) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[i][j] = mfma16_i8(av[i], bv[j], c[i][j]);
+    }
+    // step two: scale the exact group sums into the fp32 accumulators
+    float sw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sw[j] = (float)S[(4 * wn + j) * 16 + r16];
+    if constexpr (GA) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = min(m0 + 64 * wm + 16 * i + 4 * g + v, a.M - 1);
+          const float sa = (float)a.xs[size_t(m) * G + grp];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tot[i][j][v] = __builtin_fmaf(float(c[i][j][v]), sw[j] * sa, tot[i][j][v]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) tot[i][j][v] = __builtin_fmaf(float(c[i][j][v]), sw[j], tot[i][j][v]);
+    }
+    if (grp + 1 < G) {
+      // the next group's loads have landed (this wave's), then everyone's;
+      // the barrier also retires this group's reads of `buf`
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      __syncthreads();
+      if (q4) {
+        expand(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // per-token scale, fused scatter to the original rows
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 4 * wn + j;
+    if (t >= tend) continue;
+    const int n = a.rows[16 * t + r16];
+    if (n < 0) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
+        if (m >= a.M) continue;
+        const float sa = GA ? 1.0f : (float)a.xs[m];
+        a.y[size_t(m) * a.N + n] = (_Float16)(tot[i][j][v] * sa);
+      }
+  }
+}
+
 W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
                   int32_t* acc, int M) {
   W48Args a;
@@ -275,7 +459,14 @@ int launch(const W48Args& a, void* stream) {
   const int T = a.T8 + a.T4;
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.M <= 32) {
+  if (a.M > 64 && !a.acc_out) {
+    const unsigned by = unsigned((a.T8 + 7) / 8 + (a.T4 + 7) / 8);
+    const dim3 grid(unsigned((a.M + kTB - 1) / kTB), by);
+    if (a.ga == 128)
+      hipLaunchKernelGGL(w48_tile_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(w48_tile_kernel<false>, grid, dim3(256), 0, s, a);
+  } else if (a.M <= 32) {
     hipLaunchKernelGGL(w48_kernel<32>, dim3(unsigned((a.M + 31) / 32), gy), dim3(256), 0, s, a);
   } else if (a.M <= 64) {
     hipLaunchKernelGGL(w48_kernel<64>, dim3(unsigned((a.M + 63) / 64), gy), dim3(256), 0, s, a);
