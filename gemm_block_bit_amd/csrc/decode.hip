@@ -382,12 +382,16 @@ constexpr int kMetaSlots1 = 4;
 constexpr uint32_t kMetaMask1 = kMetaSlots1 * 512 - 1;
 constexpr int kWaveLds1 = kCodeSlots1 * 1024 + kMetaSlots1 * 512;   // bytes per wave
 
-// The b code loads of one block, code slot i at ring offset (c0 + 1024 i) & mask.
-template <int B>
-__device__ __forceinline__ void issue_codes1(const uint8_t* cp, const uint32_t (&voff)[8], uint32_t ring,
-                                             uint32_t c0) {
-#pragma unroll
-  for (int q = 0; q < B; ++q) dma16(cp, voff[q], ring, (c0 + 1024 * q) & kCodeMask1);
+// Wait until at most n (uniform, n >= 0) loads are in flight, rounded down to
+// 8, 4 or 0: two compares instead of a decision tree, at the price of waiting
+// for a few later loads.
+__device__ __forceinline__ void wait_vmcnt_coarse(int n) {
+  if (n >= 8)
+    wait_vmcnt<8>();
+  else if (n >= 4)
+    wait_vmcnt<4>();
+  else
+    wait_vmcnt<0>();
 }
 
 template <int W0, int W1, class Refill>
@@ -438,9 +442,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
   const int w_begin = wg_begin + (wg_cols * wave) / NW;
   const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
-  uint32_t voff[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) voff[q] = 16 * lane + 1024 * q;
+  const uint32_t voff = 16 * lane;   // lane's 16 bytes of a 1 KiB record
 
   __shared__ u32x4 lds[NW * kWaveLds1 / 16];   // per-wave rings; reused for the reduction
   const u32x4* code = lds + wave * (kWaveLds1 / 16);
@@ -469,14 +471,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
         if (bn > cfree || mfree == 0) break;
         dma4(szp, 4 * lane, meta_lds, mn);
         dma4(xp, 4 * lane, meta_lds, mn + 256);
-        switch (bn) {
-          case 1: issue_codes1<1>(cp, voff, code_lds, cn); break;
-          case 2: issue_codes1<2>(cp, voff, code_lds, cn); break;
-          case 3: issue_codes1<3>(cp, voff, code_lds, cn); break;
-          case 4: issue_codes1<4>(cp, voff, code_lds, cn); break;
-          case 6: issue_codes1<6>(cp, voff, code_lds, cn); break;
-          default: issue_codes1<8>(cp, voff, code_lds, cn); break;
-        }
+        for (int q = 0; q < bn; ++q) dma16(cp + 1024 * q, voff, code_lds, (cn + 1024 * q) & kCodeMask1);
         szp += 64;
         xp += 128;
         cp += 1024 * bn;
@@ -494,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     for (int j = 0; j < S; ++j) {
       const int bj = uniform(__builtin_amdgcn_readlane(bvec, j));
       done += 2 + bj;
-      wait_vmcnt_at_most(issued - done);
+      wait_vmcnt_coarse(issued - done);
       auto refill = [&]() {
         cfree += bj;
         mfree += 1;

@@ -324,11 +324,14 @@ def test_w48_group_acc_bit_exact(N, K, M, frac):
     assert np.array_equal(acc.astype(np.int64), ref)
 
 
-@pytest.mark.parametrize("N,K,M,ga", [(48, 256, 3, None), (200, 384, 40, None), (300, 1024, 130, None),
-                                      (300, 1024, 77, 128), (1000, 4096, 1, None)])
-def test_w48_parity(N, K, M, ga):
+@pytest.mark.parametrize("N,K,M,ga,frac", [(48, 256, 3, None, 0.1), (200, 384, 40, None, 0.1),
+                                           (300, 1024, 130, None, 0.1), (300, 1024, 77, 128, 0.1),
+                                           (1000, 4096, 1, None, 0.1),
+                                           # batches above 64 with no 8-bit rows / only 8-bit rows
+                                           (64, 256, 100, None, 0.0), (80, 256, 200, 128, 1.0)])
+def test_w48_parity(N, K, M, ga, frac):
     W = small(N, K, 3 * N + M)
-    rows8 = synth.salient_rows_by_l2(W, 0.1)
+    rows8 = synth.salient_rows_by_l2(W, frac)
     img, _, _ = gbb.pack_w48(W, rows8)
     x = rand_x(M, K, 2 * N)
     xq, xs = gbb.quant_act_i8(to_dev(x), ga)
