@@ -434,6 +434,133 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (M <= 64, per-token activation scales): the weights dominate,
+// so the kernel streams them.  A workgroup owns four packed tiles (64 rows,
+// homogeneous 8-bit or 4-bit) and walks K one 128-column group at a time
+// through a 4-stage LDS pipeline: per group each wave issues the same number
+// of global->LDS loads (its share of the activation fragments, its tile's
+// weight fragments, scales and zero points), so every wait is a fixed vmcnt.
+// One barrier per group publishes the shared activation fragments.
+// ---------------------------------------------------------------------------
+constexpr int kStages = 4;
+
+template <int TM>   // token tiles: M <= 16 TM
+struct StreamCfg {
+  static constexpr int NA = (2 * TM + 3) / 4;           // activation loads per wave per group
+  static constexpr int kA = 4 * NA * 1024;              // activation fragments per stage
+  static constexpr int kB = 4 * 2048;                   // weight fragments, 2 KiB per wave
+  static constexpr int kS = 4 * 256;                    // scales, 256 B per wave
+  static constexpr int kZ = 4 * 256;                    // zero points, 256 B per wave
+  static constexpr int kStage = kA + kB + kS + kZ;
+  static constexpr int kLoads8 = NA + 3;                // loads per wave per group, 8-bit rows
+  static constexpr int kLoads4 = NA + 6;                // 4-bit rows
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int TM>
+__global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
+  using C = StreamCfg<TM>;
+  __shared__ u32x4 lds[kStages * C::kStage / 16];
+  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
+  const uint32_t lbase = lds_u32(lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int nb8 = (a.T8 + 3) / 4;
+  const bool q4 = int(blockIdx.x) >= nb8;
+  const int t0 = q4 ? a.T8 + (int(blockIdx.x) - nb8) * 4 : int(blockIdx.x) * 4;
+  const int tend = q4 ? a.T8 + a.T4 : a.T8;
+  const int t = min(t0 + wave, tend - 1);   // this wave's tile (clamped; results discarded)
+  const int G = a.K / 128, KT = a.K / 64;
+
+  auto stage = [&](int grp) { return (grp % kStages) * C::kStage; };
+  auto issue = [&](int grp) {
+    const uint32_t st = lbase + stage(grp);
+#pragma unroll
+    for (int q = 0; q < C::NA; ++q) {
+      const int f = wave + 4 * q, i = min(f >> 1, TM - 1), h = f & 1;
+      const int m = min(16 * i + r16, a.M - 1);
+      gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g, st + f * 1024);
+    }
+    const uint32_t sb = st + C::kA + wave * 2048;
+    if (!q4) {
+      gdma16(a.c8 + (size_t(t) * KT + 2 * grp) * 1024 + 16 * lane, sb);
+      gdma16(a.c8 + (size_t(t) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
+    } else {
+      const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + 2 * grp) * 512;
+      gdma4(src + 4 * lane, sb);
+      gdma4(src + 256 + 4 * lane, sb + 256);
+      gdma4(src + 512 + 4 * lane, sb + 512);
+      gdma4(src + 768 + 4 * lane, sb + 768);
+    }
+    gdma4(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
+    if (q4) gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
+  };
+
+  f32x4 tot[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) tot[i] = f32x4{0, 0, 0, 0};
+
+  for (int p = 0; p < kStages - 1 && p < G; ++p) issue(p);
+  for (int grp = 0; grp < G; ++grp) {
+    // this wave's loads of group grp have landed once at most the loads of the
+    // (up to kStages - 2) later groups are in flight
+    const int later = min(G - 1 - grp, kStages - 2);
+    if (later == kStages - 2) {
+      if (q4) wait_vm<(kStages - 2) * C::kLoads4>(); else wait_vm<(kStages - 2) * C::kLoads8>();
+    } else if (later == 1) {
+      if (q4) wait_vm<C::kLoads4>(); else wait_vm<C::kLoads8>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();   // every wave's loads of grp landed; every wave is done with grp - 1
+    if (grp + kStages - 1 < G) issue(grp + kStages - 1);   // into grp - 1's stage
+    const uint8_t* st = base + stage(grp);
+    const uint8_t* B = st + C::kA + wave * 2048;
+    const float sw = (float)reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256)[r16];
+    i32x4 c[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) c[i] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 bv;
+      if (!q4) {
+        bv = *reinterpret_cast<const i32x4*>(B + h * 1024 + 16 * lane);
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(B + h * 512 + 8 * lane);
+        const uint32_t z = st[C::kA + C::kB + C::kS + wave * 256 + r16];
+        bv = expand4(w, (128u - z) * 0x01010101u);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x4 av = *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
+        c[i] = mfma16_i8(av, bv, c[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(c[i][v]), sw, tot[i][v]);
+  }
+
+  if (t0 + wave >= tend) return;
+  const int n = a.rows[16 * (t0 + wave) + r16];
+  if (n < 0) return;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * i + 4 * g + v;
+      if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(tot[i][v] * (float)a.xs[m]);
+    }
+}
+
 W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
                   int32_t* acc, int M) {
   W48Args a;
@@ -459,7 +586,15 @@ int launch(const W48Args& a, void* stream) {
   const int T = a.T8 + a.T4;
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.M > 64 && !a.acc_out) {
+  if (a.M <= 64 && a.ga != 128 && !a.acc_out) {
+    const dim3 grid(unsigned((a.T8 + 3) / 4 + (a.T4 + 3) / 4));
+    if (a.M <= 16)
+      hipLaunchKernelGGL(w48_stream_kernel<1>, grid, dim3(256), 0, s, a);
+    else if (a.M <= 32)
+      hipLaunchKernelGGL(w48_stream_kernel<2>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(w48_stream_kernel<4>, grid, dim3(256), 0, s, a);
+  } else if (a.M > 64 && !a.acc_out) {
     const unsigned by = unsigned((a.T8 + 7) / 8 + (a.T4 + 7) / 8);
     const dim3 grid(unsigned((a.M + kTB - 1) / kTB), by);
     if (a.ga == 128)
