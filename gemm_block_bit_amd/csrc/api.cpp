@@ -21,7 +21,7 @@ gbb_status device_status(int err, const char* what) {
 gbb_status check_block_args(const void* image, int N, int K, int M) {
   if (!image) return fail(GBB_E_ARG, "image is NULL");
   if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
-  if (size_t(N) > kCounterBytes / 4 * 64) return fail(GBB_E_SHAPE, "N=%d exceeds 1048576", N);
+  if (N > kMaxRows) return fail(GBB_E_SHAPE, "N=%d exceeds %d", N, kMaxRows);
   if (M < 0) return fail(GBB_E_ARG, "M must not be negative (M=%d)", M);
   if (N % kBlockRows || K % kGroup)
     return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);
@@ -79,7 +79,7 @@ extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
   if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % kGroup) return 0;
   if (M > 32) return 0;
   const DecodePlan p = decode_plan(N, K, M);
-  return p.ctr_bytes + p.part_bytes;
+  return p.ws_bytes;
 }
 
 extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t* x, uint16_t* y,
@@ -98,7 +98,7 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
   const bool decode = path == 1 || (path == 0 && M <= 32);
   if (decode) {
     const DecodePlan p = decode_plan(N, K, M);
-    const size_t need = p.ctr_bytes + p.part_bytes;
+    const size_t need = p.ws_bytes;
     if (need) {
       if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
       if (ws_bytes < need) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);

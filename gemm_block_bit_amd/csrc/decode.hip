@@ -30,10 +30,15 @@
 //    per wave, 16 waves per CU.  Blocks are issued ahead while they fit; the
 //    wait for a block is a vmcnt bound, and a block's slots are refilled as
 //    soon as its LDS reads have completed.
-//  * With K segments, partial sums cross workgroups (and XCDs) through
-//    device-scope (sc1) stores and loads, which need no cache writeback; the
-//    last workgroup of a block row (an atomic counter that resets itself)
-//    adds them in segment order, so results are deterministic.
+//  * With K segments, each workgroup hands its partial sums over with one
+//    device-scope 64-bit atomic add per output element: the partial, rounded
+//    to a multiple of 2^-28, in the high bits and a count in the low bits.
+//    The add that completes the count returns the whole sum, so the last
+//    contributor writes y and clears the word, one memory round trip after
+//    its partial is known.  Integer addition is exact and order-free, so
+//    results do not depend on which workgroup finishes first.  Partials too
+//    large for the fixed-point field (or not finite) go through an fp32
+//    atomic accumulator instead, published before their count.
 #include "device.h"
 #include "internal.h"
 #include "layout.h"
@@ -49,10 +54,43 @@ struct DecodeArgs {
   const uint8_t* codes;
   const _Float16* x;
   _Float16* y;
-  float* part;
-  uint32_t* ctr;
+  uint64_t* acc;   // split-K fixed-point accumulators [M][N] (zero between calls)
+  float* facc;     // split-K overflow accumulators [M][N] (zero between calls)
   int N, K, M, nbr, nbc, seg_cols, nseg;
 };
+
+// Split-K hand-off of one output element idx (of y and the accumulators).
+// The 64-bit word is  v * 2^12 + poisoned * 2^6 + count  with v the sum of
+// the partials rounded to multiples of 2^-28 (|partial| < 2^18, so 32 of
+// them fit the 52-bit field exactly), count the contributions so far and
+// poisoned those that went through the fp32 accumulator instead.  Every
+// lane of the wave calls this together; `active` lanes contribute.
+constexpr float kFixScale = 268435456.0f;   // 2^28
+constexpr float kFixLimit = 262144.0f;      // 2^18
+__device__ __forceinline__ void splitk_publish(const DecodeArgs& a, size_t idx, float p, bool active) {
+  const bool big = active && !(__builtin_fabsf(p) < kFixLimit);   // also NaN
+  uint64_t word = 1;
+  if (big) {
+    __hip_atomic_fetch_add(a.facc + idx, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    word += 64;
+  } else {
+    word += uint64_t(int64_t(__builtin_rintf(p * kFixScale))) << 12;
+  }
+  // the overflow adds are visible before the counts that announce them
+  if (__builtin_amdgcn_ballot_w64(big)) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (!active) return;
+  const uint64_t tot = __hip_atomic_fetch_add(a.acc + idx, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + word;
+  if (int(tot & 63) != a.nseg) return;
+  // last contribution: the word holds the complete sum
+  float r = float(double(int64_t(tot) >> 12) * (1.0 / 268435456.0));
+  if ((tot >> 6) & 63) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    r += __hip_atomic_load(a.facc + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.facc + idx, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  a.y[idx] = (_Float16)r;
+  __hip_atomic_store(a.acc + idx, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Ring slots per wave (a power of two): a block takes 1 + nx + b slots
 // (nx = ceil(M / 4) activation slots of four tokens each).
@@ -328,45 +366,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * mt + 4 * g + v;
-        if (m >= M) continue;
-        if (a.nseg == 1)
-          a.y[size_t(m) * a.N + n] = (_Float16)s[v];
-        else
-          __hip_atomic_store(a.part + (size_t(seg) * M + m) * a.N + n, s[v], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        const size_t idx = size_t(min(m, M - 1)) * a.N + n;
+        if (a.nseg == 1) {
+          if (m < M) a.y[idx] = (_Float16)s[v];
+        } else {
+          splitk_publish(a, idx, s[v], m < M);
+        }
       }
     }
-  }
-  if (a.nseg == 1) return;
-
-  // K segments: the barrier waits for every partial store of the workgroup;
-  // the workgroup that completes the block row's count sums the segments.
-  __shared__ int s_last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.ctr + br, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == uint32_t(a.nseg - 1);
-    if (last) __hip_atomic_store(a.ctr + br, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  const size_t stride = size_t(M) * a.N;
-  for (int o = threadIdx.x; o < 64 * M; o += NW * 64) {
-    const int m = o >> 6, n = br * 64 + (o & 63);
-    const float* pp = a.part + size_t(m) * a.N + n;
-    float s = 0.0f;
-    for (int s0 = 0; s0 < a.nseg; s0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = s0 + i < a.nseg
-                   ? __hip_atomic_load(pp + size_t(s0 + i) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[i];
-    }
-    a.y[size_t(m) * a.N + n] = (_Float16)s;
   }
 }
 
@@ -509,50 +516,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   }
   __syncthreads();
 
-  // waves meet in LDS; wave w < 4 adds row tile w over the waves in order
-  static_assert(NW * 4 * 64 * 4 + 4 <= NW * kWaveLds1, "reduction fits in the rings");
+  // waves meet in LDS; lane l of wave 0 adds row 16 (l / 16) + l % 16 of
+  // the block row over the waves in order
+  static_assert(NW * 4 * 64 * 4 <= NW * kWaveLds1, "reduction fits in the rings");
   float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(lds);
-  int* s_last = reinterpret_cast<int*>(lds) + NW * 4 * 64;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt];
   __syncthreads();
-  if (wave < 4 && g == 0) {
-    const int rt = wave;
-    const int n = br * 64 + 16 * rt + r16;
-    float s = red[0][rt][lane];
+  if (wave != 0) return;
+  float s = red[0][g][r16];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) s += red[w][rt][lane];
-    if (a.nseg == 1)
-      a.y[n] = (_Float16)s;
-    else
-      __hip_atomic_store(a.part + size_t(seg) * a.N + n, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (a.nseg == 1) return;
-
-  // K segments: the barrier waits for every partial store of the workgroup;
-  // the workgroup that completes the block row's count sums the segments.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.ctr + br, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == uint32_t(a.nseg - 1);
-    if (last) __hip_atomic_store(a.ctr + br, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = last;
-  }
-  __syncthreads();
-  if (!*s_last || threadIdx.x >= 64) return;
-  const int n = br * 64 + lane;
-  const float* pp = a.part + n;
-  float s = 0.0f;
-  for (int s0 = 0; s0 < a.nseg; s0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = s0 + i < a.nseg ? __hip_atomic_load(pp + size_t(s0 + i) * a.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s += v[i];
-  }
-  a.y[n] = (_Float16)s;
+  for (int w = 1; w < NW; ++w) s += red[w][g][r16];
+  const size_t n = size_t(br) * 64 + lane;
+  if (a.nseg == 1)
+    a.y[n] = (_Float16)s;
+  else
+    splitk_publish(a, n, s, true);
 }
 
 }  // namespace
@@ -561,29 +540,34 @@ DecodePlan decode_plan(int N, int K, int M) {
   DecodePlan p;
   const int nbr = N / 64, nbc = K / 128;
   p.nw = 4;
-  // 4-wave workgroups resident per CU: four for one token (40 KiB of LDS
-  // rings each), two for M <= 16 (64 KiB), one for larger M (128 KiB).
-  // One workgroup per block row when that fills the resident slots; else
-  // split K into as many segments as still fit in one resident wave of
-  // workgroups, with at least 2 columns per wave, capped by the partial-sum
-  // traffic (nseg * M * N * 8 bytes against ~N * K / 2).
-  const int resident = (M == 1 ? 4 : M <= 16 ? 2 : 1) * 256;
   int nseg = 1;
-  if (nbr < resident) {
-    nseg = resident / nbr;
-    nseg = min(nseg, max(1, nbc / (2 * p.nw)));
-    nseg = min(nseg, max(1, K / (64 * M)));
+  if (M == 1) {
+    // Single token: every wave takes k blocks of a block row (k = 4, 2 or
+    // 1), with the largest k that still gives at least 1024 workgroups (four
+    // per CU, the resident count) so the dispatcher can balance the CUs; k = 1
+    // when none reaches it.  Measured on Llama-3-8B/70B-shaped projections.
+    int k = 4;
+    while (k > 1 && nbr * ((nbc + 4 * k - 1) / (4 * k)) < 1024) k /= 2;
+    while ((nbc + 4 * k - 1) / (4 * k) > kMaxSegments) k *= 2;
+    nseg = (nbc + 4 * k - 1) / (4 * k);
+  } else {
+    // 4-wave workgroups resident per CU: two for M <= 16 (64 KiB of LDS
+    // rings each), one for larger M (128 KiB).  One workgroup per block row
+    // when that fills the resident slots; else split K into as many segments
+    // as still fit in one resident wave of workgroups, with at least 2
+    // columns per wave, capped by the hand-off traffic (nseg * M * N * 8
+    // bytes against ~N * K / 2).
+    const int resident = (M <= 16 ? 2 : 1) * 256;
+    if (nbr < resident) {
+      nseg = resident / nbr;
+      nseg = min(nseg, max(1, nbc / (2 * p.nw)));
+      nseg = min(nseg, max(1, K / (64 * M)));
+    }
   }
+  nseg = min(nseg, kMaxSegments);
   p.seg_cols = (nbc + nseg - 1) / nseg;
   p.nseg = (nbc + p.seg_cols - 1) / p.seg_cols;
-  if (p.nseg > 1) {
-    // counters live in a fixed region at the start of every workspace, so one
-    // zero-filled buffer serves calls of any shape
-    p.ctr_bytes = kCounterBytes;
-    p.part_bytes = size_t(p.nseg) * size_t(M) * size_t(N) * 4;
-  } else {
-    p.ctr_bytes = p.part_bytes = 0;
-  }
+  p.ws_bytes = p.nseg > 1 ? size_t(M) * size_t(N) * 12 : 0;
   return p;
 }
 
@@ -596,8 +580,8 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   a.codes = im.codes;
   a.x = reinterpret_cast<const _Float16*>(x);
   a.y = reinterpret_cast<_Float16*>(y);
-  a.ctr = static_cast<uint32_t*>(workspace);
-  a.part = plan.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ctr_bytes) : nullptr;
+  a.acc = plan.nseg > 1 ? static_cast<uint64_t*>(workspace) : nullptr;
+  a.facc = plan.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + size_t(M) * im.N * 8) : nullptr;
   a.N = im.N;
   a.K = im.K;
   a.M = M;

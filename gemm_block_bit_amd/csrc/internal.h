@@ -25,12 +25,14 @@ struct BlockImageView {
 };
 
 // Decode (M <= 32) launch plan: one workgroup of nw waves per block row and
-// K segment.  Split-K calls keep one u32 counter per block row in the first
-// kCounterBytes of the workspace (N up to 1 048 576 rows).
-constexpr size_t kCounterBytes = 65536;
+// K segment.  Split-K calls keep, per output element, one 64-bit fixed-point
+// accumulator (first M * N * 8 bytes of the workspace) and one fp32 overflow
+// accumulator (next M * N * 4 bytes); both return to zero when a call ends.
+constexpr int kMaxRows = 1 << 20;   // N limit of the block format's entry points
+constexpr int kMaxSegments = 32;    // K segments per block row (fits the count field)
 struct DecodePlan {
   int nw, nseg, seg_cols;
-  size_t part_bytes, ctr_bytes;
+  size_t ws_bytes;
 };
 DecodePlan decode_plan(int N, int K, int M);
 

@@ -166,6 +166,50 @@ def test_split_k_deterministic_over_many_calls(M):
     assert bq.rel_inf_err(first.float().numpy()[:, rows], bq.reference_rows(rand_x(M, K, 77), W, bits, rows)) <= TOL
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_split_k_large_partials(M):
+    """Segment partial sums beyond the fixed-point range of the split-K
+    hand-off (|partial| >= 2^18) take the fp32 overflow accumulator: two block
+    columns at opposite ends of K carry identical weights against activations
+    of +-30000, so their huge partials cancel in y."""
+    N, K = 1024, 4096
+    g = np.random.default_rng(91)
+    W = g.standard_normal((N, K)).astype(np.float16)
+    W[:, K - 128:] = W[:, :128]
+    bits = synth.random_bitmap(N, K, ALLOWED, 91)
+    bits[:, 0] = bits[:, -1] = 8
+    x = (100.0 * g.standard_normal((M, K))).astype(np.float16)
+    x[:, :128] = 30000.0
+    x[:, K - 128:] = -30000.0
+    assert gbb.gemm_mixed_w_workspace(N, K, M) > 0
+    ws = torch.zeros(gbb.gemm_mixed_w_workspace(N, K, M), dtype=torch.uint8, device=dev())
+    img = packed(W, bits)
+    ref = bq.reference_gemm(x, W, bits)
+    for _ in range(3):   # the accumulators are clean again after each call
+        y = gbb.gemm_mixed_w_path(img, N, K, to_dev(x), 1, workspace=ws)
+        assert rel_err(y, ref) <= TOL
+    assert not torch.any(ws)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_split_k_nan_then_clean(M):
+    """A NaN activation reaches every output through the overflow
+    accumulator; the next call on the same workspace is unaffected."""
+    N, K = 1024, 4096
+    W = small(N, K, 92)
+    bits = synth.random_bitmap(N, K, ALLOWED, 92)
+    img = packed(W, bits)
+    ws = torch.zeros(gbb.gemm_mixed_w_workspace(N, K, M), dtype=torch.uint8, device=dev())
+    xn = rand_x(M, K, 92)
+    xn[:, 5] = np.nan
+    y = gbb.gemm_mixed_w_path(img, N, K, to_dev(xn), 1, workspace=ws)
+    assert torch.isnan(y.float()).all()
+    x = rand_x(M, K, 93)
+    y = gbb.gemm_mixed_w_path(img, N, K, to_dev(x), 1, workspace=ws)
+    assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
+    assert not torch.any(ws)
+
+
 def test_graph_replay_matches_eager():
     """The decode and prefill launches captured in a HIP graph: every replay,
     with eager work in between, reproduces the eager result bit for bit."""
