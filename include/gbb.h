@@ -97,10 +97,11 @@ gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits,
 /* Check a host copy of an image header against N and K (GBB_E_FORMAT). */
 gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 
-/* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M); may be 0.  The
- * workspace must be zero-filled once before its first use; every call leaves
- * it zero-filled again.  Calls that run at the same time need separate
- * workspaces. */
+/* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M); may be 0 (it is
+ * M * N * 12 when K is split across workgroups: per output element an int64
+ * fixed-point and an fp32 accumulator).  The workspace must be zero-filled
+ * once before its first use; every call leaves it zero-filled again.  Calls
+ * that run at the same time need separate workspaces. */
 size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
 
 /* y = x . dequant(W)^T over a packed block image (ScaleBITS explainer page,
