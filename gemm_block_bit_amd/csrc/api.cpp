@@ -106,6 +106,8 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
     }
     return device_status(launch_decode(v, x, y, M, workspace, p, stream), "decode launch");
   }
+  if (size_t(M) * size_t(K) >= (size_t(1) << 31))
+    return fail(GBB_E_SHAPE, "the prefill kernel takes M * K < 2^31 (M=%d K=%d)", M, K);
   return device_status(launch_prefill(v, x, y, M, stream), "prefill launch");
 }
 

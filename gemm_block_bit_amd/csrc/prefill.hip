@@ -4,17 +4,26 @@
 // hidden under the matrix math (MixLLM page, section 2.2 on batched serving
 // and section 3.3 on overlapping dequantization with the matrix product).
 //
-// gfx950 design: a workgroup computes a 128 (tokens) x 128 (output rows) tile
-// of y and walks K one 128-column block column at a time.  Per step its four
-// waves (a) copy the 128x128 fp16 activation tile into LDS and (b) dequantize
-// the two 64x128 weight blocks of the tile into LDS: a lane unpacks the codes
-// it loaded (one coalesced 16-byte load per KiB of codes), forms 1024 + q with
-// the fp16 magic, subtracts 1024 + z and multiplies by s with packed fp16
-// arithmetic -- exactly fp16((q - z) * s), since q - z is an exact small
-// integer and the product is rounded once.  Then each wave runs
-// v_mfma_f32_16x16x32_f16 on its 64x64 sub-tile from LDS.  Both LDS tiles are
-// XOR-swizzled on 16-byte chunks so that the 16 rows a lane group touches at
-// one column fall in distinct banks.  Workgroups are mapped XCD by XCD to
+// gfx950 design: a workgroup of eight waves (two per SIMD, one workgroup per
+// CU) computes a 128 (tokens) x 512 (output rows) tile of y; wave w owns
+// block row 8 t + w, all 128 tokens.  The block image stores each 1 KiB of
+// codes so that the 16 bytes a lane loads are, field by field, exactly its
+// v_mfma_f32_16x16x32_f16 B operands (16 rows x 32 columns per tile).  So a
+// wave turns the codes of one 64x128 block into B operands in registers, one
+// 32-column tile at a time -- fp16((q - z) s) per element: OR the code into
+// the mantissa of 1024.0, subtract 1024 + z (exact, a small integer) and
+// multiply by s (rounded once) -- and uses each of them for the eight
+// 16-token tiles (128 MFMAs per block and wave).  The dequantization of the
+// next column tile is independent of the current tile's MFMAs, and the other
+// wave on the SIMD fills the matrix cores while one does vector work.  The
+// plane widths, slots and shifts are uniform per block, so one branch-free
+// code path serves all bitwidths and the accumulators never move.  Codes and
+// scale/zero records reach a per-wave LDS stage by global->LDS loads issued
+// as soon as the previous block's last code slot has been read; the shared
+// activation tile (128 tokens x 128 columns per K step) reaches LDS one step
+// ahead, double buffered, in MFMA fragment order (one 1 KiB fragment per 16
+// tokens x 32 columns, lane l's 16 bytes at 16 l), so every A read is one
+// conflict-free 16-byte LDS read.  Workgroups are mapped XCD by XCD to
 // contiguous, grouped stretches of tiles so that each XCD's L2 sees the reuse
 // of activation rows and weight blocks.
 #include "device.h"
@@ -25,8 +34,10 @@ namespace gbb {
 
 namespace {
 
-constexpr int kBM = 128;  // tokens per tile
-constexpr int kBN = 128;  // output rows per tile (two block rows)
+constexpr int kBM = 128;                 // tokens per tile
+constexpr int kWaves = 8;                // waves per workgroup, one block row each
+constexpr int kBN = 64 * kWaves;         // output rows per tile
+constexpr int kMT = kBM / 16;            // 16-token tiles per tile
 constexpr int kGroupM = 8;
 
 struct PrefillArgs {
@@ -39,77 +50,95 @@ struct PrefillArgs {
   int N, K, M, nbr, nbc, tiles_m, tiles_n, per_xcd;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Code pairs of the column half h (column tiles kt = 2h, 2h + 1) of one plane
-// of width W: tile 4 kt + rt is field (4 kt + rt) % (16 / W) of slot
-// (4 kt + rt) / (16 / W), so the half lives in the slots [8h / NP, ..] and,
-// for W = 1, in the byte of each half word selected by h.
-template <int W>
-struct PlaneHalf {
-  static constexpr int NP = 16 / W;
-  static constexpr int NS = W == 1 ? 1 : 8 / NP;  // slots of one half
-  uint32_t w[NS][4];
-  __device__ __forceinline__ void load(const uint8_t* cb, int h) {
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const u32x4 v = ld16(reinterpret_cast<const uint32_t*>(cb + 1024 * ((8 * h) / NP + t)));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[t][c] = W == 1 ? v[c] >> (8 * h) : v[c];
-    }
-  }
-  // pair of word c of local tile ul = 4 (kt - 2h) + rt
-  __device__ __forceinline__ uint32_t pair(int ul, int c) const {
-    return (w[ul / NP][c] >> (W * (ul % NP))) & (((1u << W) - 1u) * 0x00010001u);
-  }
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
 
-// Dequantize the column half h of one block into LDS rows base_row + 0..63:
-// exactly fp16((q - z) s), as (1024 + q) - (1024 + z) is an exact small
-// integer in fp16 and the product is rounded once.
-template <int W0, int W1>
-__device__ __forceinline__ void dequant_half(const uint8_t* __restrict__ blk_codes, const uint32_t* __restrict__ blk_sz,
-                                             int h, int lane, u32x4* __restrict__ lds, int base_row) {
-  const int g = lane >> 4, r16 = lane & 15;
-  const uint8_t* cb = blk_codes + 16 * lane;
-  PlaneHalf<W0> p0;
-  PlaneHalf<W1 ? W1 : 1> p1;
-  p0.load(cb, h);
-  if constexpr (W1 != 0) p1.load(cb + 1024 * W0, h);
-  // entry 4 r16 + rt of the block's scale/zero record is row 16 rt + r16
-  const u32x4 sz = ld16(blk_sz + 4 * r16);
+// One global->LDS load of 16 bytes per lane from sbase + voff: lane l's bytes
+// land at LDS address lds + 16 l.  No output registers; completion is
+// awaited with an explicit vmcnt wait before the LDS is read.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_all_loads() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One K step of one wave for a block of bitwidth b (planes W0 + W1): the
+// B operands of column tile kt + 1 are formed while the 8 x 4 MFMAs of column
+// tile kt run.  Tile 4 kt + rt is field (4 kt + rt) % (16 / W) of slot
+// (4 kt + rt) / (16 / W) of a plane of width W -- one slot per column tile
+// and plane -- and the second plane holds the high bits.  The plane widths,
+// slots and shifts are uniform per block, so one branch-free code path
+// serves every bitwidth (a missing second plane has an empty mask) and the
+// accumulators stay in the matrix-core registers.
+template <class Refill>
+__device__ __forceinline__ void kstep(int b, const u32x4* __restrict__ st, const u32x4* __restrict__ xb, int lane,
+                                      f32x4 (&acc)[kMT][4], Refill&& refill) {
+  const int W0 = b == 3 ? 2 : (b >= 4 ? 4 : b);
+  const int W1 = b == 3 ? 1 : (b == 6 ? 2 : (b == 8 ? 4 : 0));
+  const int L0 = W0 == 4 ? 2 : (W0 == 2 ? 3 : 4);   // log2(16 / W0)
+  const int L1 = W1 == 4 ? 2 : (W1 == 2 ? 3 : 4);
+  const uint32_t M0 = ((1u << W0) - 1u) * 0x00010001u;
+  const uint32_t M1 = (((1u << W1) - 1u) * 0x00010001u) << W0;
+  const u32x4 sz = st[512 + lane];
+  half2v s2[4], z2[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const uint32_t e = sz[rt];
-    const half2v s2 = as_half2((e & 0xffffu) * 0x00010001u);
-    const _Float16 zf = __builtin_bit_cast(_Float16, (unsigned short)(e >> 16));
-    const _Float16 nz = -((_Float16)1024.0f + zf);  // exact: an integer below 2048
-    const half2v z2 = {nz, nz};
+    s2[rt] = as_half2((e & 0xffffu) * 0x00010001u);
+    const _Float16 nz = -((_Float16)1024.0f + __builtin_bit_cast(_Float16, (unsigned short)(e >> 16)));
+    z2[rt] = half2v{nz, nz};   // exact: an integer below 2048
+  }
+  auto deq = [&](int kt, u32x4 (&B)[4]) {
+    const u32x4 c0 = st[64 * ((4 * kt) >> L0) + lane];
+    const u32x4 c1 = st[64 * (W0 + ((4 * kt) >> L1)) + lane];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int ul = 4 * k2 + rt;
+    for (int rt = 0; rt < 4; ++rt) {
+      const int u = 4 * kt + rt;
+      const uint32_t s0 = uint32_t(W0 * (u & ((1 << L0) - 1)));
+      const uint32_t r1 = uint32_t(W1 * (u & ((1 << L1) - 1)) - W0) & 31u;   // rotate the field to bit W0
       uint32_t o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t q = p0.pair(ul, c);
-        if constexpr (W1 != 0) q |= p1.pair(ul, c) << W0;
-        const half2v v = (as_half2(q | kMagicPair) + z2) * s2;
-        o[c] = as_u32(v);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = ((c0[k] >> s0) & M0) | kMagicPair;
+        const uint32_t q = (__builtin_amdgcn_alignbit(c1[k], c1[k], r1) & M1) | lo;
+        o[k] = as_u32((as_half2(q) + z2[rt]) * s2[rt]);
       }
-      lds[swz(base_row + 16 * rt + r16, 4 * (2 * h + k2) + g)] = u32x4{o[0], o[1], o[2], o[3]};
+      B[rt] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+  u32x4 B[2][4];
+  deq(0, B[0]);
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    if (kt < 3) deq(kt + 1, B[(kt + 1) & 1]);
+    if (kt == 2) refill();   // every code slot of the block has been read
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      const half8 A = __builtin_bit_cast(half8, xb[(4 * mt + kt) * 64 + lane]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = mfma16(A, __builtin_bit_cast(half8, B[kt & 1][rt]), acc[mt][rt]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  __shared__ u32x4 xs[kBM * 16];
-  __shared__ u32x4 ws[kBN * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
+  // activation tiles, double buffered: fragment (mt, kt) at 1 KiB (4 mt + kt)
+  __shared__ u32x4 xs[2][kMT * 4 * 64];
+  // per wave: a block's codes (up to 8 KiB) and its scale/zero entries (1 KiB)
+  __shared__ u32x4 stage[kWaves][9 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
 
   // XCD-aware tile order: the hardware deals workgroups round robin to the 8
   // XCDs, so workgroup i runs on XCD i % 8; give each XCD a contiguous range
-  // of tiles, walked in groups of kGroupM row tiles.
+  // of tiles, walked in groups of kGroupM token tiles.
   const int bid = blockIdx.x;
   const int t = (bid & 7) * a.per_xcd + (bid >> 3);
   const int ntiles = a.tiles_m * a.tiles_n;
@@ -119,84 +148,88 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int gm = min(kGroupM, a.tiles_m - first_m);
   const int tm = first_m + (t % gsize) % gm;
   const int tn = (t % gsize) / gm;
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = tm * kBM;
+  const bool has_rows = tn * kWaves + wave < a.nbr;
+  // waves past the last block row repeat it (their outputs are not stored),
+  // so the step loop has no branch around the matrix-core work
+  const int br = min(tn * kWaves + wave, a.nbr - 1);   // this wave's block row
 
-  f32x4 acc[4][4];
+  // wave w loads the activation fragments (mt, kt) = (2 w + f / 4, f % 4);
+  // token rows past M repeat row M - 1 (their outputs are not stored)
+  constexpr int kFrag = kMT * 4 / kWaves;
+  uint32_t xoff[kFrag];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int f = 0; f < kFrag; ++f) {
+    const int fr = kFrag * wave + f, mt = fr >> 2, kt = fr & 3;
+    const int m = min(m0 + 16 * mt + r16, a.M - 1);
+    xoff[f] = uint32_t((size_t(m) * a.K + 32 * kt + 8 * g) * 2);
+  }
+  const uint32_t xs_lds = lds_addr(&xs[0][0]);
+  auto load_x = [&](int bc, int buf) {
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+      dma16(a.x, xoff[f] + uint32_t(bc) * 256,
+            xs_lds + uint32_t(buf) * (kMT * 4 * 1024) + uint32_t(kFrag * wave + f) * 1024);
+  };
+
+  // this wave's block row: bitwidths and code offsets 64 columns at a time
+  const size_t row_blk = size_t(br) * a.nbc;
+  int bvec = 0, ovec = 0;
+  auto load_meta = [&](int col0) {
+    const int c = min(col0 + lane, a.nbc - 1);
+    bvec = int(a.bits[row_blk + c]);
+    ovec = int(a.offs[row_blk + c]);
+  };
+  const uint32_t st_lds = uint32_t(uniform(int(lds_addr(&stage[wave][0]))));
+  auto load_block = [&](int bc) {   // codes and scale/zero of block (br, bc) into the stage
+    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
+    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc & 63))) * 1024;
+    for (int q = 0; q < bj; ++q) dma16(cb + 1024 * q, 16 * lane, st_lds + 1024 * q);
+    dma16(a.sz + (row_blk + bc) * 64, 16 * r16, st_lds + 8192);
+  };
+
+  f32x4 acc[kMT][4];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  // weight work of this wave: block row n0/64 + (wave >> 1), column half wave & 1
-  const int br = (n0 >> 6) + (wave >> 1);
-  const int hk = wave & 1;
-  const int wrow = 64 * (wave >> 1);
-
+  load_meta(0);
+  load_x(0, 0);
+  load_block(0);
   for (int bc = 0; bc < a.nbc; ++bc) {
-    u32x4 xr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = j * 256 + tid, row = idx >> 4, c = idx & 15;
-      const int m = m0 + row;
-      xr[j] = u32x4{0, 0, 0, 0};
-      if (m < a.M) xr[j] = ld16(a.x + size_t(m) * a.K + size_t(bc) * 128 + 8 * c);
+    const int buf = bc & 1;
+    wait_all_loads();   // this wave's fragments and block of step bc
+    __syncthreads();    // every wave's fragments of step bc are in LDS; step bc - 1's reads are done
+    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));   // before the next 64 columns' metadata
+    const bool more = bc + 1 < a.nbc;
+    if (more) {
+      load_x(bc + 1, buf ^ 1);
+      if (((bc + 1) & 63) == 0) load_meta(bc + 1);
     }
-    __syncthreads();  // the previous step's MFMA reads are done
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = j * 256 + tid, row = idx >> 4, c = idx & 15;
-      xs[swz(row, c)] = xr[j];
-    }
-    if (br < a.nbr) {
-      const int blk = br * a.nbc + bc;
-      const int b = uniform(a.bits[blk]);
-      const uint8_t* cb = a.codes + size_t(uniform(int(a.offs[blk]))) * 1024;
-      const uint32_t* sb = a.sz + size_t(blk) * 64;
-      switch (b) {
-        case 1: dequant_half<1, 0>(cb, sb, hk, lane, ws, wrow); break;
-        case 2: dequant_half<2, 0>(cb, sb, hk, lane, ws, wrow); break;
-        case 3: dequant_half<2, 1>(cb, sb, hk, lane, ws, wrow); break;
-        case 4: dequant_half<4, 0>(cb, sb, hk, lane, ws, wrow); break;
-        case 6: dequant_half<4, 2>(cb, sb, hk, lane, ws, wrow); break;
-        default: dequant_half<4, 4>(cb, sb, hk, lane, ws, wrow); break;
+    // the next block's codes go into the stage as soon as this block's last
+    // code slot has been read (inside the step, before its last MFMAs)
+    auto refill = [&]() {
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        load_block(bc + 1);
       }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) ws[swz(wrow + 16 * rt + r16, 4 * (2 * hk + k2) + g)] = u32x4{0, 0, 0, 0};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      half8 A[4], B[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A[i] = __builtin_bit_cast(half8, xs[swz(wm * 64 + i * 16 + r16, 4 * ks + g)]);
-        B[i] = __builtin_bit_cast(half8, ws[swz(wn * 64 + i * 16 + r16, 4 * ks + g)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
-    }
+    };
+    kstep(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
   }
+  if (!has_rows) return;
 
   // lane holds D[token 4 g + v][row r16] of each 16x16 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * 64 + i * 16 + 4 * g + v;
+      const int m = m0 + 16 * mt + 4 * g + v;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + r16;
-        if (n < a.N) a.y[size_t(m) * a.N + n] = (_Float16)acc[i][j][v];
-      }
+      for (int rt = 0; rt < 4; ++rt) a.y[size_t(m) * a.N + br * 64 + 16 * rt + r16] = (_Float16)acc[mt][rt][v];
     }
-  }
 }
 
 }  // namespace
@@ -218,7 +251,7 @@ int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int
   a.tiles_n = (im.nbr * 64 + kBN - 1) / kBN;
   const int ntiles = a.tiles_m * a.tiles_n;
   a.per_xcd = (ntiles + 7) / 8;
-  const dim3 grid(unsigned(8 * a.per_xcd)), block(256);
+  const dim3 grid(unsigned(8 * a.per_xcd)), block(kWaves * 64);
   hipLaunchKernelGGL(prefill_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }
