@@ -257,18 +257,19 @@ __global__ __launch_bounds__(256) void w48_kernel(W48Args a) {
 // brought into LDS by global->LDS loads in MFMA fragment order -- activation
 // fragments gathered 16 tokens at a time, weight fragments as packed, the
 // group's weight scales and zero points -- so operand reads are conflict-free
-// lane-linear 16-byte reads and no staging registers are needed.  4-bit
-// fragments land raw and are expanded once per workgroup into int8 (q - z).
-// LDS is double-buffered: the next group's loads fly while the current group
-// runs; one wait and one barrier per group.  Wave (wm, wn) owns tokens
-// 64 wm + [0, 64) and rows 64 wn + [0, 64): 4 x 4 MFMA tiles, two k halves
-// per group.
+// lane-linear reads and no staging registers are needed.  4-bit fragments
+// land raw (512 B) and each wave expands the ones it multiplies into int8
+// (q - z) in registers right before its MFMAs.  LDS is double-buffered: the
+// next group's loads fly while the current group runs; one wait and one
+// barrier per group.  Wave (wm, wn) owns tokens 64 wm + [0, 64) and rows
+// 64 wn + [0, 64): 4 x 4 MFMA tiles, two k halves per group.
 // ---------------------------------------------------------------------------
 constexpr int kTB = 128;   // tokens and packed rows per workgroup
 
-// LDS map (bytes): A[2] 16 KiB each, B[2] 16 KiB each, raw 4-bit staging
-// 8 KiB, weight scales[2] 256 B each, zero points 256 B
-constexpr int kLdsA = 0, kLdsB = 32768, kLdsRaw = 65536, kLdsS = 73728, kLdsZ = 74240, kLdsW48 = 74496;
+// LDS map (bytes): A[2] 16 KiB each, B[2] 16 KiB each (8-bit fragments, or
+// the raw 4-bit fragments in the first 8 KiB), weight scales[2] 256 B each,
+// zero points[2] 256 B each
+constexpr int kLdsA = 0, kLdsB = 32768, kLdsS = 65536, kLdsZ = 66048, kLdsW48 = 66560;
 
 // global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
 // LDS address lds + 16 l (4 l).  No output registers: completion is waited
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         gdma16(a.c8 + (size_t(t) * KT + kt) * 1024 + 16 * lane, lbase + kLdsB + buf * 16384 + f * 1024);
       } else {
         const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + kt) * 512;
-        gdma4(src + 4 * lane, lbase + kLdsRaw + f * 512);
-        gdma4(src + 256 + 4 * lane, lbase + kLdsRaw + f * 512 + 256);
+        gdma4(src + 4 * lane, lbase + kLdsB + buf * 16384 + f * 512);
+        gdma4(src + 256 + 4 * lane, lbase + kLdsB + buf * 16384 + f * 512 + 256);
       }
     }
     if (wave == 0) {
@@ -328,18 +329,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       gdma4(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), lbase + kLdsS + buf * 256);
     } else if (wave == 1 && q4) {
       const int t = min(t0 + ((lane & 31) >> 2), tend - 1);
-      gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), lbase + kLdsZ);
-    }
-  };
-  // 4-bit: expand the raw fragments of this wave into int8 (q - z)
-  auto expand = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f = wave + 4 * q, i = f >> 1;
-      const uint2 w = *reinterpret_cast<const uint2*>(base + kLdsRaw + f * 512 + 8 * lane);
-      const uint32_t z = base[kLdsZ + 16 * i + r16];
-      const i32x4 e = expand4(w, (128u - z) * 0x01010101u);
-      *reinterpret_cast<i32x4*>(base + kLdsB + buf * 16384 + f * 1024 + 16 * lane) = e;
+      gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), lbase + kLdsZ + buf * 256);
     }
   };
 
@@ -352,10 +342,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
   __syncthreads();
-  if (q4) {
-    expand(0);
-    __syncthreads();
-  }
   for (int grp = 0; grp < G; ++grp) {
     const int buf = grp & 1;
     if (grp + 1 < G) issue(grp + 1, buf ^ 1);
@@ -373,9 +359,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         av[i] = *reinterpret_cast<const i32x4*>(A + (2 * (4 * wm + i) + h) * 1024 + 16 * lane);
+      if (q4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[j] = *reinterpret_cast<const i32x4*>(B + (2 * (4 * wn + j) + h) * 1024 + 16 * lane);
+        for (int j = 0; j < 4; ++j) {
+          const int f = 2 * (4 * wn + j) + h;
+          const uint2 w = *reinterpret_cast<const uint2*>(B + f * 512 + 8 * lane);
+          const uint32_t z = base[kLdsZ + buf * 256 + 16 * (4 * wn + j) + r16];
+          bv[j] = expand4(w, (128u - z) * 0x01010101u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bv[j] = *reinterpret_cast<const i32x4*>(B + (2 * (4 * wn + j) + h) * 1024 + 16 * lane);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -408,10 +404,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // the barrier also retires this group's reads of `buf`
       __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
       __syncthreads();
-      if (q4) {
-        expand(buf ^ 1);
-        __syncthreads();
-      }
     }
   }
 
