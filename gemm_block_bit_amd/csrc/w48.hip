@@ -281,6 +281,14 @@ __device__ __forceinline__ void gdma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void gdma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// Non-temporal forms for data a launch reads once (the weight streams of the
+// small-M kernel): the caches give those lines up first.
+__device__ __forceinline__ void gdma16_once(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void gdma4_once(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -482,17 +490,17 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
     }
     const uint32_t sb = st + C::kA + wave * 2048;
     if (!q4) {
-      gdma16(a.c8 + (size_t(t) * KT + 2 * grp) * 1024 + 16 * lane, sb);
-      gdma16(a.c8 + (size_t(t) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
+      gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp) * 1024 + 16 * lane, sb);
+      gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
     } else {
       const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + 2 * grp) * 512;
-      gdma4(src + 4 * lane, sb);
-      gdma4(src + 256 + 4 * lane, sb + 256);
-      gdma4(src + 512 + 4 * lane, sb + 512);
-      gdma4(src + 768 + 4 * lane, sb + 768);
+      gdma4_once(src + 4 * lane, sb);
+      gdma4_once(src + 256 + 4 * lane, sb + 256);
+      gdma4_once(src + 512 + 4 * lane, sb + 512);
+      gdma4_once(src + 768 + 4 * lane, sb + 768);
     }
-    gdma4(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
-    if (q4) gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
+    gdma4_once(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
+    if (q4) gdma4_once(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
   };
 
   f32x4 tot[TM];
