@@ -558,9 +558,14 @@ DecodePlan decode_plan(int N, int K, int M) {
     // Single token: every wave takes k blocks of a block row (k = 4, 2 or
     // 1), with the largest k that still gives at least 1024 workgroups (four
     // per CU, the resident count) so the dispatcher can balance the CUs; k = 1
-    // when none reaches it.  Measured on Llama-3-8B/70B-shaped projections.
+    // when none reaches it.  At 768 or more workgroups a smaller k is not
+    // taken when it would split K into more than 16 segments: the hand-off
+    // atomics per output then cost more than the balance gains (Llama-3-8B
+    // down projection, 4096 x 14336: 9.0 against 10.0 us).  Measured on
+    // Llama-3-8B/70B-shaped projections.
+    auto segs = [&](int kk) { return (nbc + 4 * kk - 1) / (4 * kk); };
     int k = 4;
-    while (k > 1 && nbr * ((nbc + 4 * k - 1) / (4 * k)) < 1024) k /= 2;
+    while (k > 1 && nbr * segs(k) < 1024 && !(nbr * segs(k) >= 768 && segs(k / 2) > 16)) k /= 2;
     while ((nbc + 4 * k - 1) / (4 * k) > kMaxSegments) k *= 2;
     nseg = (nbc + 4 * k - 1) / (4 * k);
   } else {
