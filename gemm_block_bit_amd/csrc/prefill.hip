@@ -26,6 +26,8 @@
 // conflict-free 16-byte LDS read.  Workgroups are mapped XCD by XCD to
 // contiguous, grouped stretches of tiles so that each XCD's L2 sees the reuse
 // of activation rows and weight blocks.
+#include <atomic>
+
 #include "device.h"
 #include "internal.h"
 #include "layout.h"
@@ -47,7 +49,7 @@ struct PrefillArgs {
   const uint8_t* codes;
   const _Float16* x;
   _Float16* y;
-  int N, K, M, nbr, nbc, tiles_m, tiles_n, per_xcd;
+  int N, K, M, nbr, nbc, tiles_m, tiles_n, per_xcd, cus_xcd;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -77,9 +79,9 @@ __device__ __forceinline__ void wait_all_loads() {
 // slots and shifts are uniform per block, so one branch-free code path
 // serves every bitwidth (a missing second plane has an empty mask) and the
 // accumulators stay in the matrix-core registers.
-template <class Refill>
+template <int MT, class Refill>
 __device__ __forceinline__ void kstep(int b, const u32x4* __restrict__ st, const u32x4* __restrict__ xb, int lane,
-                                      f32x4 (&acc)[kMT][4], Refill&& refill) {
+                                      f32x4 (&acc)[MT][4], Refill&& refill) {
   const int W0 = b == 3 ? 2 : (b >= 4 ? 4 : b);
   const int W1 = b == 3 ? 1 : (b == 6 ? 2 : (b == 8 ? 4 : 0));
   const int L0 = W0 == 4 ? 2 : (W0 == 2 ? 3 : 4);   // log2(16 / W0)
@@ -120,7 +122,7 @@ __device__ __forceinline__ void kstep(int b, const u32x4* __restrict__ st, const
     if (kt < 3) deq(kt + 1, B[(kt + 1) & 1]);
     if (kt == 2) refill();   // every code slot of the block has been read
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const half8 A = __builtin_bit_cast(half8, xb[(4 * mt + kt) * 64 + lane]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = mfma16(A, __builtin_bit_cast(half8, B[kt & 1][rt]), acc[mt][rt]);
@@ -128,35 +130,39 @@ __device__ __forceinline__ void kstep(int b, const u32x4* __restrict__ st, const
   }
 }
 
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
-  // activation tiles, double buffered: fragment (mt, kt) at 1 KiB (4 mt + kt)
-  __shared__ u32x4 xs[2][kMT * 4 * 64];
-  // per wave: a block's codes (up to 8 KiB) and its scale/zero entries (1 KiB)
-  __shared__ u32x4 stage[kWaves][9 * 64];
+// Tiles of XCD x are [first, first + count).  When they fill whole rounds
+// of the XCD's CUs (one workgroup per CU) and leave a last round at most half
+// full, the last `split` tiles run as two 64-token halves each, so that last
+// round keeps every CU busy for half as long instead of half the CUs for a
+// whole tile.  The halves need no reduction: they own disjoint outputs.
+struct XcdWork {
+  int first, count, split;
+};
+__host__ __device__ inline XcdWork xcd_work(int ntiles, int per_xcd, int cus_xcd, int x) {
+  XcdWork w;
+  w.first = x * per_xcd;
+  w.count = max(0, min(per_xcd, ntiles - w.first));
+  const int r = w.count % cus_xcd;
+  w.split = (w.count >= cus_xcd && r > 0 && 2 * r <= cus_xcd) ? r : 0;
+  return w;
+}
+
+// One tile of MT 16-token tiles (tokens m0 ...) x 512 rows (block rows
+// 8 tn ...): wave w owns block row 8 tn + w.
+template <int MT>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int tn, u32x4 (*xs)[kMT * 4 * 64],
+                                             u32x4 (*stage)[9 * 64]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-
-  // XCD-aware tile order: the hardware deals workgroups round robin to the 8
-  // XCDs, so workgroup i runs on XCD i % 8; give each XCD a contiguous range
-  // of tiles, walked in groups of kGroupM token tiles.
-  const int bid = blockIdx.x;
-  const int t = (bid & 7) * a.per_xcd + (bid >> 3);
-  const int ntiles = a.tiles_m * a.tiles_n;
-  if (t >= ntiles) return;
-  const int gsize = kGroupM * a.tiles_n;
-  const int first_m = (t / gsize) * kGroupM;
-  const int gm = min(kGroupM, a.tiles_m - first_m);
-  const int tm = first_m + (t % gsize) % gm;
-  const int tn = (t % gsize) / gm;
-  const int m0 = tm * kBM;
   const bool has_rows = tn * kWaves + wave < a.nbr;
   // waves past the last block row repeat it (their outputs are not stored),
   // so the step loop has no branch around the matrix-core work
   const int br = min(tn * kWaves + wave, a.nbr - 1);   // this wave's block row
 
-  // wave w loads the activation fragments (mt, kt) = (2 w + f / 4, f % 4);
-  // token rows past M repeat row M - 1 (their outputs are not stored)
-  constexpr int kFrag = kMT * 4 / kWaves;
+  // wave w loads the activation fragments (mt, kt) = (f' / 4, f' % 4) with
+  // f' = kFrag w + f; token rows past M repeat row M - 1 (their outputs are
+  // not stored)
+  constexpr int kFrag = MT * 4 / kWaves;
   uint32_t xoff[kFrag];
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) {
@@ -188,9 +194,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     dma16(a.sz + (row_blk + bc) * 64, 16 * r16, st_lds + 8192);
   };
 
-  f32x4 acc[kMT][4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
@@ -216,13 +222,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         load_block(bc + 1);
       }
     };
-    kstep(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
+    kstep<MT>(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
   }
   if (!has_rows) return;
 
   // lane holds D[token 4 g + v][row r16] of each 16x16 tile
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = m0 + 16 * mt + 4 * g + v;
@@ -230,6 +236,57 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) a.y[size_t(m) * a.N + br * 64 + 16 * rt + r16] = (_Float16)acc[mt][rt][v];
     }
+}
+
+
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillArgs a) {
+  // activation tiles, double buffered: fragment (mt, kt) at 1 KiB (4 mt + kt)
+  __shared__ u32x4 xs[2][kMT * 4 * 64];
+  // per wave: a block's codes (up to 8 KiB) and its scale/zero entries (1 KiB)
+  __shared__ u32x4 stage[kWaves][9 * 64];
+
+  // XCD-aware tile order: the hardware deals workgroups round robin to the 8
+  // XCDs, so workgroup i runs on XCD i % 8; give each XCD a contiguous range
+  // of tiles, walked in groups of kGroupM token tiles, whole tiles first and
+  // the split halves (if any) last.
+  const int bid = blockIdx.x;
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, bid & 7);
+  const int j = bid >> 3, whole = w.count - w.split;
+  int t, half = -1;
+  if (j < whole) {
+    t = w.first + j;
+  } else {
+    const int v = j - whole;
+    if (v >= 2 * w.split) return;
+    t = w.first + whole + (v >> 1);
+    half = v & 1;
+  }
+  const int gsize = kGroupM * a.tiles_n;
+  const int first_m = (t / gsize) * kGroupM;
+  const int gm = min(kGroupM, a.tiles_m - first_m);
+  const int tm = first_m + (t % gsize) % gm;
+  const int tn = (t % gsize) / gm;
+  if (half < 0) {
+    prefill_tile<kMT>(a, tm * kBM, tn, xs, stage);
+  } else {
+    const int m0 = tm * kBM + half * (kBM / 2);
+    if (m0 >= a.M) return;
+    prefill_tile<kMT / 2>(a, m0, tn, xs, stage);
+  }
+}
+
+// Compute units of the current device, looked up once per device.
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 }  // namespace
@@ -251,7 +308,13 @@ int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int
   a.tiles_n = (im.nbr * 64 + kBN - 1) / kBN;
   const int ntiles = a.tiles_m * a.tiles_n;
   a.per_xcd = (ntiles + 7) / 8;
-  const dim3 grid(unsigned(8 * a.per_xcd)), block(kWaves * 64);
+  a.cus_xcd = max(1, compute_units() / 8);
+  int items = 0;
+  for (int x = 0; x < 8; ++x) {
+    const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, x);
+    items = max(items, w.count + w.split);
+  }
+  const dim3 grid(unsigned(8 * items)), block(kWaves * 64);
   hipLaunchKernelGGL(prefill_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }

@@ -122,7 +122,11 @@ def test_decode_parity(N, K, M):
         assert rel_err(y, ref) <= TOL
 
 
-PREFILL_CASES = [(64, 128, 33), (192, 384, 100), (128, 1280, 257), (320, 512, 129), (256, 4096, 600)]
+# the last two have 384 tiles of 128 tokens x 512 rows: 48 per XCD, so each
+# XCD's last 16 tiles run as 64-token halves (with M = 1436 some second halves
+# start past the last token)
+PREFILL_CASES = [(64, 128, 33), (192, 384, 100), (128, 1280, 257), (320, 512, 129), (256, 4096, 600),
+                 (16384, 256, 1536), (16384, 256, 1436)]
 
 
 @pytest.mark.parametrize("N,K,M", PREFILL_CASES)
