@@ -298,11 +298,13 @@ def main():
             x = torch.from_numpy(synth.prefill_x(2048, p.K, i)).to(dev)
             y = torch.empty((2048, p.N), dtype=torch.float16, device=dev)
             fl = 2.0 * 2048 * p.N * p.K
-            sp = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, x, out=y), 12, 6)
+            # matrix-core-bound launches reach steady clocks only after some
+            # tens of milliseconds of such work: warm up for ~30 launches
+            sp = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, x, out=y), 30, 30)
             del rot
             w32, w16 = gbb.dequant(imgd, p.N, p.K)
             del w32
-            sl = time_eager(torch, lambda: torch.matmul(x, w16.t(), out=y), 10, 3)
+            sl = time_eager(torch, lambda: torch.matmul(x, w16.t(), out=y), 30, 30)
             pre[p.name] = {"N": p.N, "K": p.K, "ms": round(sp * 1e3, 3), "TFLOPs": round(fl / sp / 1e12, 1),
                            "frac_fp16_peak": round(fl / sp / 1e12 / FP16_PEAK_TFLOPS, 3),
                            "fp16_library_gemm_on_dequantized_TFLOPs": round(fl / sl / 1e12, 1)}
@@ -324,7 +326,9 @@ def main():
             x = torch.from_numpy(synth.activations(M, 8192, synth.WL_W44A8, 0)).to(dev)
             xq, xs = gbb.quant_act_i8(x)
             y = torch.empty((M, 28672), dtype=torch.float16, device=dev)
-            sw = time_eager(torch, lambda: gbb.gemm_w48a8(rot.next(), 28672, 8192, rows8.size, xq, xs, out=y), 20, 4)
+            # warm up for ~30 ms of launches (at least 4, at most 200)
+            sw = time_eager(torch, lambda: gbb.gemm_w48a8(rot.next(), 28672, 8192, rows8.size, xq, xs, out=y), 30,
+                            min(200, max(4, int(30e-3 / (2.0 * M * 28672 * 8192 / 1e15)))))
             ops = 2.0 * M * 28672 * 8192
             w48[f"M{M}"] = {"us": round(sw * 1e6, 1), "TOPs": round(ops / sw / 1e12, 1),
                             "frac_int8_peak": round(ops / sw / 1e12 / INT8_PEAK_TOPS, 3),

@@ -29,8 +29,10 @@ CXX_FLAGS = ["-O2", "-Wall", "-Wextra", "-fno-fast-math"] + COMMON
 
 HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip"]
 # per-source extra flags: the decode kernel reads its MFMA results with VALU
-# code right away, so it keeps them in VGPRs rather than accumulation registers
-HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# code right away, so it keeps them in VGPRs rather than accumulation
+# registers; its single-token kernel takes its arguments preloaded into
+# scalar registers
+HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 CXX_SOURCES = ["pack.cpp", "api.cpp"]
 
 

@@ -454,7 +454,36 @@ __device__ __forceinline__ void block1(const u32x4* code, const u32x4* meta, uin
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode1_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode1_body(const DecodeArgs& a);
+// The arguments are passed one by one, those needed first leading, so the
+// dispatcher can place them in scalar registers before the first instruction
+// (kernel argument preloading) instead of every wave loading them from
+// memory: with one round of short workgroups that load is on the critical
+// path (Llama-3-8B layer set: 8.25 -> 8.07 us per launch).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode1_kernel(
+    const uint8_t* bits, const uint32_t* offs, const uint32_t* sz, const uint8_t* codes, const _Float16* x, int nbc,
+    int seg_cols, int nseg, _Float16* y, uint64_t* acc, float* facc, int N, int K, int M, int nbr) {
+  DecodeArgs a;
+  a.bits = bits;
+  a.offs = offs;
+  a.sz = sz;
+  a.codes = codes;
+  a.x = x;
+  a.y = y;
+  a.acc = acc;
+  a.facc = facc;
+  a.N = N;
+  a.K = K;
+  a.M = M;
+  a.nbr = nbr;
+  a.nbc = nbc;
+  a.seg_cols = seg_cols;
+  a.nseg = nseg;
+  decode1_body<NW>(a);
+}
+template <int NW>
+__device__ __forceinline__ void decode1_body(const DecodeArgs& a) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int br = blockIdx.x / a.nseg, seg = blockIdx.x - br * a.nseg;
@@ -610,7 +639,8 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   const dim3 grid(unsigned(im.nbr * plan.nseg));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M == 1)
-    hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a.bits, a.offs, a.sz, a.codes, a.x, a.nbc,
+                       a.seg_cols, a.nseg, a.y, a.acc, a.facc, a.N, a.K, a.M, a.nbr);
   else if (M <= 16)
     hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
   else
