@@ -438,15 +438,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Small batches (M <= 64, per-token activation scales): the weights dominate,
 // so the kernel streams them.  A workgroup owns four packed tiles (64 rows,
 // homogeneous 8-bit or 4-bit) and walks K one 128-column group at a time
-// through a 4-stage LDS pipeline: per group each wave issues the same number
+// through a 5-stage (M > 32: 4-stage) LDS pipeline: per group each wave issues the same number
 // of global->LDS loads (its share of the activation fragments, its tile's
 // weight fragments, scales and zero points), so every wait is a fixed vmcnt.
 // One barrier per group publishes the shared activation fragments.
 // ---------------------------------------------------------------------------
-constexpr int kStages = 4;
-
 template <int TM>   // token tiles: M <= 16 TM
 struct StreamCfg {
+  // The kernel is bound by how many bytes each CU keeps in flight (stages - 1
+  // groups per workgroup, two workgroups per CU): five stages still fit two
+  // workgroups in the LDS for M <= 32, four for M <= 64.
+  static constexpr int kStages = TM <= 2 ? 5 : 4;
   static constexpr int NA = (2 * TM + 3) / 4;           // activation loads per wave per group
   static constexpr int kA = 4 * NA * 1024;              // activation fragments per stage
   static constexpr int kB = 4 * 2048;                   // weight fragments, 2 KiB per wave
@@ -454,7 +456,7 @@ struct StreamCfg {
   static constexpr int kZ = 4 * 256;                    // zero points, 256 B per wave
   static constexpr int kStage = kA + kB + kS + kZ;
   static constexpr int kLoads8 = NA + 3;                // loads per wave per group, 8-bit rows
-  static constexpr int kLoads4 = NA + 6;                // 4-bit rows
+  static constexpr int kLoads4 = NA + 3;                // 4-bit rows
 };
 
 template <int N>
@@ -464,18 +466,15 @@ __device__ __forceinline__ void wait_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int TM>
-__global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
+// One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.
+template <int TM, bool Q4>
+__device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend) {
   using C = StreamCfg<TM>;
-  __shared__ u32x4 lds[kStages * C::kStage / 16];
-  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
-  const uint32_t lbase = lds_u32(lds);
+  constexpr int kStages = C::kStages;
+  constexpr int kLoads = Q4 ? C::kLoads4 : C::kLoads8;
+  const uint32_t lbase = lds_u32(base);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int nb8 = (a.T8 + 3) / 4;
-  const bool q4 = int(blockIdx.x) >= nb8;
-  const int t0 = q4 ? a.T8 + (int(blockIdx.x) - nb8) * 4 : int(blockIdx.x) * 4;
-  const int tend = q4 ? a.T8 + a.T4 : a.T8;
   const int t = min(t0 + wave, tend - 1);   // this wave's tile (clamped; results discarded)
   const int G = a.K / 128, KT = a.K / 64;
 
@@ -489,65 +488,84 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
       gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g, st + f * 1024);
     }
     const uint32_t sb = st + C::kA + wave * 2048;
-    if (!q4) {
+    if constexpr (!Q4) {
       gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp) * 1024 + 16 * lane, sb);
       gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
     } else {
-      const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + 2 * grp) * 512;
-      gdma4_once(src + 4 * lane, sb);
-      gdma4_once(src + 256 + 4 * lane, sb + 256);
-      gdma4_once(src + 512 + 4 * lane, sb + 512);
-      gdma4_once(src + 768 + 4 * lane, sb + 768);
+      // the group's two 512-byte fragments are contiguous: one 1 KiB load
+      gdma16_once(a.c4 + (size_t(t - a.T8) * KT + 2 * grp) * 512 + 16 * lane, sb);
     }
     gdma4_once(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
-    if (q4) gdma4_once(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
+    if constexpr (Q4)
+      gdma4_once(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
   };
 
   f32x4 tot[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) tot[i] = f32x4{0, 0, 0, 0};
+  // the previous group's int32 sums and weight scale: they are scaled into
+  // tot while the current group's MFMAs run, so no step waits for its own
+  // matrix-core results
+  i32x4 cp[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) cp[i] = i32x4{0, 0, 0, 0};
+  float swp = 0.0f;
 
   for (int p = 0; p < kStages - 1 && p < G; ++p) issue(p);
   for (int grp = 0; grp < G; ++grp) {
     // this wave's loads of group grp have landed once at most the loads of the
     // (up to kStages - 2) later groups are in flight
+    static_assert(kStages - 2 <= 3, "wait cases");
     const int later = min(G - 1 - grp, kStages - 2);
-    if (later == kStages - 2) {
-      if (q4) wait_vm<(kStages - 2) * C::kLoads4>(); else wait_vm<(kStages - 2) * C::kLoads8>();
-    } else if (later == 1) {
-      if (q4) wait_vm<C::kLoads4>(); else wait_vm<C::kLoads8>();
-    } else {
+    if (later >= 3)
+      wait_vm<3 * kLoads>();
+    else if (later == 2)
+      wait_vm<2 * kLoads>();
+    else if (later == 1)
+      wait_vm<kLoads>();
+    else
       wait_vm<0>();
-    }
     __syncthreads();   // every wave's loads of grp landed; every wave is done with grp - 1
     if (grp + kStages - 1 < G) issue(grp + kStages - 1);   // into grp - 1's stage
+    // every LDS read of the step first, then one wait
     const uint8_t* st = base + stage(grp);
     const uint8_t* B = st + C::kA + wave * 2048;
+    i32x4 av[TM][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) av[i][h] = *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
     const float sw = (float)reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256)[r16];
+    i32x4 bv[2];
+    if constexpr (!Q4) {
+      bv[0] = *reinterpret_cast<const i32x4*>(B + 16 * lane);
+      bv[1] = *reinterpret_cast<const i32x4*>(B + 1024 + 16 * lane);
+    } else {
+      const uint2 w0 = *reinterpret_cast<const uint2*>(B + 8 * lane);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(B + 512 + 8 * lane);
+      const uint32_t z = st[C::kA + C::kB + C::kS + wave * 256 + r16];
+      const uint32_t zb = (128u - z) * 0x01010101u;
+      bv[0] = expand4(w0, zb);
+      bv[1] = expand4(w1, zb);
+    }
     i32x4 c[TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) c[i] = i32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      i32x4 bv;
-      if (!q4) {
-        bv = *reinterpret_cast<const i32x4*>(B + h * 1024 + 16 * lane);
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(B + h * 512 + 8 * lane);
-        const uint32_t z = st[C::kA + C::kB + C::kS + wave * 256 + r16];
-        bv = expand4(w, (128u - z) * 0x01010101u);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const i32x4 av = *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
-        c[i] = mfma16_i8(av, bv, c[i]);
-      }
+    for (int i = 0; i < TM; ++i) {
+      c[i] = mfma16_i8(av[i][0], bv[0], i32x4{0, 0, 0, 0});
+      c[i] = mfma16_i8(av[i][1], bv[1], c[i]);
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(c[i][v]), sw, tot[i][v]);
+      for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), swp, tot[i][v]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) cp[i] = c[i];
+    swp = sw;
   }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), swp, tot[i][v]);
 
   if (t0 + wave >= tend) return;
   const int n = a.rows[16 * (t0 + wave) + r16];
@@ -559,6 +577,19 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
       const int m = 16 * i + 4 * g + v;
       if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(tot[i][v] * (float)a.xs[m]);
     }
+}
+
+template <int TM>
+__global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
+  using C = StreamCfg<TM>;
+  static_assert(2 * C::kStages * C::kStage <= 160 * 1024, "two workgroups per CU");
+  __shared__ u32x4 lds[C::kStages * C::kStage / 16];
+  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
+  const int nb8 = (a.T8 + 3) / 4;
+  if (int(blockIdx.x) < nb8)
+    stream_tiles<TM, false>(a, base, int(blockIdx.x) * 4, a.T8);
+  else
+    stream_tiles<TM, true>(a, base, a.T8 + (int(blockIdx.x) - nb8) * 4, a.T8 + a.T4);
 }
 
 W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,

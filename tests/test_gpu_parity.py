@@ -374,7 +374,8 @@ def test_w48_group_acc_bit_exact(N, K, M, frac):
 
 @pytest.mark.parametrize("N,K,M,ga,frac", [(48, 256, 3, None, 0.1), (200, 384, 40, None, 0.1),
                                            (300, 1024, 130, None, 0.1), (300, 1024, 77, 128, 0.1),
-                                           (1000, 4096, 1, None, 0.1),
+                                           (1000, 4096, 1, None, 0.1), (256, 1024, 64, None, 0.1),
+                                           (128, 640, 17, None, 0.3),
                                            # batches above 64 with no 8-bit rows / only 8-bit rows
                                            (64, 256, 100, None, 0.0), (80, 256, 200, 128, 1.0)])
 def test_w48_parity(N, K, M, ga, frac):
