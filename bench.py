@@ -10,8 +10,9 @@ layer copies whose packed weights (732 MB) exceed the 256 MiB Infinity
 Cache, so every weight byte comes from HBM.  The step is replayed from a HIP
 graph of its 32 launches.
 
-Also reported: M = 8 on the same layers, the 70B-shaped layer at M = 1, the
-M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
+Also reported: M = 8 on the same layers, the same shapes with uniform 3- and
+4-bit bitmaps (the cost of mixing bitwidths), the 70B-shaped layer at
+M = 1, 8 and 32, the M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
 an fp16 library GEMM on the dequantized weights for context, the W4.4A8 layer
 (M = 32, 512, 4096) and the oracle timed on the host cores (cpu_baseline).
 
@@ -98,6 +99,8 @@ class DecodeLayerSet:
         self.names = [name for (name, _, _, _) in host]
         self.bytes = [weight_bytes(b) for (_, _, _, b) in host]
         self.layer_bytes = sum(self.bytes)
+        nblk = sum(b.size for (_, _, _, b) in host)
+        self.mean_bits = float(sum(int(b.astype(np.int64).sum()) for (_, _, _, b) in host)) / nblk
         self.copies = copies
         g = np.random.default_rng(7)
         self.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
@@ -106,6 +109,21 @@ class DecodeLayerSet:
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         # raw arguments for direct C calls (no per-call Python marshalling)
         self.fn = gbb.lib().gbb_gemm_mixed_w
+
+    def with_batch(self, M, seed):
+        """The same packed layers with new activations, outputs and workspace
+        for a batch of M tokens (the images are shared, not copied)."""
+        torch, gbb = self.torch, self.gbb
+        other = DecodeLayerSet.__new__(DecodeLayerSet)
+        other.__dict__.update(self.__dict__)
+        other.M = M
+        dev = self.images[0][0].device
+        g = np.random.default_rng(seed)
+        other.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
+        other.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (N, _) in self.shapes]
+        ws = max(gbb.gemm_mixed_w_workspace(N, K, M) for (N, K) in self.shapes)
+        other.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        return other
 
     def launches(self):
         for r in range(self.copies):
@@ -257,18 +275,33 @@ def main():
 
     if not args.quick:
         # ---------------- same layers at M = 8 ----------------
-        L8b = DecodeLayerSet.__new__(DecodeLayerSet)
-        L8b.__dict__.update(L8.__dict__)
-        L8b.M = 8
-        g = np.random.default_rng(8)
-        L8b.x = [torch.from_numpy(g.standard_normal((8, K)).astype(np.float16)).to(dev) for (_, K) in L8.shapes]
-        L8b.y = [torch.empty((8, N), dtype=torch.float16, device=dev) for (N, _) in L8.shapes]
-        ws = max(gbb.gemm_mixed_w_workspace(N, K, 8) for (N, K) in L8.shapes)
-        L8b.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        L8b = L8.with_batch(8, 8)
         s8, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)
         extra["llama3_8b_decode_m8_GBps"] = round(total_bytes / s8 / 1e9, 1)
         log(f"decode M=8: {total_bytes / s8 / 1e9:.0f} GB/s")
         del L8b
+
+        # ------- the same shapes with uniform 3- and 4-bit bitmaps, M = 1 -------
+        # The mixed layers' GB/s against uniform layers' GB/s interpolated to
+        # the same mean bitwidth: the cost of mixing bitwidths in one launch.
+        uni = {}
+        for b in (3, 4):
+            def gen_uniform(i, b=b):
+                p, W, _ = synth.llama3_8b_proj(i)
+                return p, W, synth.uniform_bitmap(p.N, p.K, b)
+            log(f"packing Llama-3-8B-shaped layer with uniform {b}-bit blocks")
+            Lu = DecodeLayerSet(torch, gbb, synth, gen_uniform, LAYER_COPIES_8B, 1, dev)
+            su, _, _ = time_graph(torch, lambda: Lu.step(h()), args.steps, args.warmup)
+            uni[b] = Lu.layer_bytes * Lu.copies / su / 1e9
+            log(f"uniform {b}-bit decode M=1: {uni[b]:.0f} GB/s")
+            del Lu
+            torch.cuda.empty_cache()
+        ref = uni[3] + (L8.mean_bits - 3.0) * (uni[4] - uni[3])
+        extra["mixed_vs_uniform_8b_m1"] = {
+            "uniform3_GBps": round(uni[3], 1), "uniform4_GBps": round(uni[4], 1),
+            "mixed_GBps": round(value, 1), "mixed_mean_bits": round(L8.mean_bits, 3),
+            "mixed_over_uniform_at_same_bits": round(value / ref, 3)}
+        log(f"mixed / uniform at {L8.mean_bits:.2f} bits: {value / ref:.3f}")
 
     del L8
     torch.cuda.empty_cache()
@@ -282,6 +315,12 @@ def main():
         extra["llama3_70b_decode_m1_GBps"] = round(b70 / s70 / 1e9, 1)
         extra["llama3_70b_layer_MB"] = round(L70.layer_bytes / 1e6, 1)
         log(f"70B decode M=1: {b70 / s70 / 1e9:.0f} GB/s")
+        for M in (8, 32):
+            Lm = L70.with_batch(M, M)
+            sm, _, _ = time_graph(torch, lambda: Lm.step(h()), max(10, args.steps // 2), args.warmup)
+            extra[f"llama3_70b_decode_m{M}_GBps"] = round(b70 / sm / 1e9, 1)
+            log(f"70B decode M={M}: {b70 / sm / 1e9:.0f} GB/s")
+            del Lm
         del L70
         torch.cuda.empty_cache()
 
