@@ -10,8 +10,9 @@ layer copies whose packed weights (732 MB) exceed the 256 MiB Infinity
 Cache, so every weight byte comes from HBM.  The step is replayed from a HIP
 graph of its 32 launches.
 
-Also reported: M = 8 on the same layers, the same shapes with uniform 3- and
-4-bit bitmaps (the cost of mixing bitwidths), the 70B-shaped layer at
+Also reported: p10/p50/p90 of single step replays, M = 8 on the same
+layers, the same shapes with uniform 3- and 4-bit bitmaps (the cost of
+mixing bitwidths), one 4096 x 4096 matrix at M = 1, the 70B-shaped layer at
 M = 1, 8 and 32, the M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
 an fp16 library GEMM on the dequantized weights for context, the W4.4A8 layer
 (M = 32, 512, 4096) and the oracle timed on the host cores (cpu_baseline).
@@ -169,6 +170,19 @@ def time_graph(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3 / steps, wall / steps, graph
 
 
+def replay_percentiles(torch, graph, n):
+    """p10 / p50 / p90 (microseconds) of n single replays of a captured graph,
+    each between its own pair of events."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return [round(float(v), 1) for v in np.percentile(t, [10, 50, 90])]
+
+
 class Rotation:
     """Cycles through equal copies of a device image, one per call."""
 
@@ -235,10 +249,12 @@ def main():
     log(f"layer weight bytes {L8.layer_bytes / 1e6:.1f} MB x {L8.copies} copies")
     h = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
 
-    sec, wall, _ = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
+    sec, wall, g8 = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
     total_bytes = L8.layer_bytes * L8.copies
     value = total_bytes / sec / 1e9
     log(f"decode M=1: {sec * 1e6:.1f} us/step, {value:.0f} GB/s")
+    step_pct = replay_percentiles(torch, g8, args.steps)
+    del g8
 
     # per-launch events over the same timed work (eager launches, one stream)
     ng = len(L8.shapes)
@@ -271,7 +287,8 @@ def main():
 
     extra = {"per_launch_group_m1_eager_events": per_proj,
              "kernel_sum_us_per_step": round(float(durs.sum(axis=(1, 2)).mean()), 1),
-             "graph_step_us": round(sec * 1e6, 1), "host_wall_us_per_step": round(wall * 1e6, 1)}
+             "graph_step_us": round(sec * 1e6, 1), "graph_step_us_p10_p50_p90": step_pct,
+             "host_wall_us_per_step": round(wall * 1e6, 1)}
 
     if not args.quick:
         # ---------------- same layers at M = 8 ----------------
@@ -307,6 +324,29 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
+        # ---------------- one 4096 x 4096 matrix, M = 1 ----------------
+        W, bits, x1 = synth.linear_4096()
+        img, _, _ = gbb.pack_blocks(W, bits)
+        del W
+        d = torch.from_numpy(img).to(dev)
+        lin = [d] + [d.clone() for _ in range(79)]   # 80 x 7.0 MB > 512 MiB
+        xd = torch.from_numpy(x1).to(dev)
+        yd = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+        wsl = torch.zeros(max(gbb.gemm_mixed_w_workspace(4096, 4096, 1), 256), dtype=torch.uint8, device=dev)
+        fn = gbb.lib().gbb_gemm_mixed_w
+
+        def lin_step():
+            for im in lin:
+                if fn(im.data_ptr(), 4096, 4096, xd.data_ptr(), yd.data_ptr(), 1, wsl.data_ptr(), wsl.numel(), h()):
+                    raise RuntimeError(gbb.lib().gbb_last_error().decode())
+        sl1, _, _ = time_graph(torch, lin_step, max(10, args.steps // 2), args.warmup)
+        lb = weight_bytes(bits) * len(lin)
+        extra["linear_4096_m1"] = {"us_per_launch": round(sl1 * 1e6 / len(lin), 2), "GBps": round(lb / sl1 / 1e9, 1),
+                                   "weight_MB": round(weight_bytes(bits) / 1e6, 2)}
+        log(f"4096x4096 M=1: {sl1 * 1e6 / len(lin):.2f} us/launch, {lb / sl1 / 1e9:.0f} GB/s")
+        del lin, d
+        torch.cuda.empty_cache()
+
         # ---------------- Llama-3-70B layer, decode M = 1 ----------------
         log("packing Llama-3-70B-shaped layer")
         L70 = DecodeLayerSet(torch, gbb, synth, synth.llama3_70b_proj, LAYER_COPIES_70B, 1, dev)
