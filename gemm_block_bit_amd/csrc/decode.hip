@@ -206,28 +206,27 @@ __device__ __forceinline__ constexpr float pow2(int e) {
 // One block of planes W0 (shift 0) and W1 (shift W0; 0 = none) whose records
 // start at ring byte offset sb: read them, let `refill` reuse the slots, then
 // acc += s (sum over planes of 2^(24 + shift - o) C - z X).
+// The ring offsets are those of its scale/zero slot (sz), first activation
+// slot (xb) and first code slot (cb).
 template <int W0, int W1, int MT, class Refill>
-__device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t sb, int nx, int M, f32x4 (&acc)[4][MT],
-                                          Refill&& refill) {
+__device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint32_t xb, uint32_t cb, int M,
+                                          f32x4 (&acc)[4][MT], Refill&& refill) {
   constexpr uint32_t MASK = Ring<MT>::kMask;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const u32x4 sz = ring[(sb >> 4) + r16];
+  const u32x4 sz = ring[((szb & MASK) >> 4) + r16];
   half8 xa[4][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(16 * mt + r16, M - 1);
-    const u32x4* xr = ring + (((sb + 1024 * (1 + (m >> 2))) & MASK) >> 4);
+    const u32x4* xr = ring + (((xb + 1024 * (m >> 2)) & MASK) >> 4);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
   }
   u32x4 w0[W0], w1[W1 ? W1 : 1];
-  {
-    const uint32_t cb = sb + 1024 * (1 + nx);
 #pragma unroll
-    for (int q = 0; q < W0; ++q) w0[q] = ring[(((cb + 1024 * q) & MASK) >> 4) + lane];
+  for (int q = 0; q < W0; ++q) w0[q] = ring[(((cb + 1024 * q) & MASK) >> 4) + lane];
 #pragma unroll
-    for (int q = 0; q < W1; ++q) w1[q] = ring[(((cb + 1024 * (W0 + q)) & MASK) >> 4) + lane];
-  }
+  for (int q = 0; q < W1; ++q) w1[q] = ring[(((cb + 1024 * (W0 + q)) & MASK) >> 4) + lane];
   wait_lds();
   refill();
 
@@ -347,13 +346,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
         used -= 1 + nx + bj;
         fill();
       };
+      const uint32_t xb = sb + 1024, cb = sb + 1024 * (1 + nx);
       switch (bj) {
-        case 1: block_mma<1, 0, MT>(ring, sb, nx, M, acc, refill); break;
-        case 2: block_mma<2, 0, MT>(ring, sb, nx, M, acc, refill); break;
-        case 3: block_mma<2, 1, MT>(ring, sb, nx, M, acc, refill); break;
-        case 4: block_mma<4, 0, MT>(ring, sb, nx, M, acc, refill); break;
-        case 6: block_mma<4, 2, MT>(ring, sb, nx, M, acc, refill); break;
-        default: block_mma<4, 4, MT>(ring, sb, nx, M, acc, refill); break;
+        case 1: block_mma<1, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        case 2: block_mma<2, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        case 3: block_mma<2, 1, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        case 4: block_mma<4, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        case 6: block_mma<4, 2, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        default: block_mma<4, 4, MT>(ring, sb, xb, cb, M, acc, refill); break;
       }
       sb = (sb + 1024 * (1 + nx + bj)) & MASK;
     }
@@ -376,6 +376,163 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
       f32x4 s = red[0][rt][mt][lane];
 #pragma unroll
       for (int w = 1; w < NW; ++w) s += red[w][rt][mt][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * mt + 4 * g + v;
+        const size_t idx = size_t(min(m, M - 1)) * a.N + n;
+        if (a.nseg == 1) {
+          if (m < M) a.y[idx] = (_Float16)s[v];
+        } else {
+          splitk_publish(a, idx, s[v], m < M);
+        }
+      }
+    }
+  }
+}
+
+// Two block rows per wave (17 <= M <= 32): at that batch a block column's
+// activations take eight 1 KiB slots against ~2-3 KiB of codes, so the ring
+// mostly holds activations and keeps only about three blocks in flight.  A
+// workgroup owns two consecutive block rows; for each column a wave loads the
+// activations once and the two rows' blocks behind them, and runs both
+// blocks on them: [sz A | activations | codes A | sz B | codes B].
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode2_kernel(DecodeArgs a) {
+  constexpr int NW = 4;
+  constexpr int R = Ring<MT>::kSlots;
+  constexpr uint32_t MASK = Ring<MT>::kMask;
+  static_assert(2 + 4 * MT + 16 <= R, "a column's records of two rows fit in the ring");
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int rp = blockIdx.x / a.nseg, seg = blockIdx.x - rp * a.nseg;
+  const int brA = 2 * rp;
+  const bool hasB = brA + 1 < a.nbr;   // else row B repeats row A, unstored
+  const int brB = hasB ? brA + 1 : brA;
+  const int wg_begin = seg * a.seg_cols;
+  const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
+  const int w_begin = wg_begin + (wg_cols * wave) / NW;
+  const int w_end = wg_begin + (wg_cols * (wave + 1)) / NW;
+  const int M = a.M;
+  const int nx = (M + 3) / 4;
+  uint32_t xoff[8];
+#pragma unroll
+  for (int xi = 0; xi < 8; ++xi) xoff[xi] = uint32_t(min(4 * xi + g, M - 1)) * uint32_t(2 * a.K) + 16 * r16;
+
+  __shared__ u32x4 lds[NW * R * 64];   // per-wave rings; reused for the reduction
+  const u32x4* ring = lds + wave * R * 64;
+  const uint32_t ring_lds = lds_addr(ring);
+
+  f32x4 acc[2][4][MT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[r][rt][mt] = f32x4{0, 0, 0, 0};
+
+  for (int col0 = w_begin; col0 < w_end; col0 += 64) {
+    const int S = min(64, w_end - col0);
+    const bool in = lane < S;
+    const size_t blkA = size_t(brA) * a.nbc + col0, blkB = size_t(brB) * a.nbc + col0;
+    const int bvecA = in ? int(a.bits[blkA + lane]) : 0;
+    const int bvecB = in ? int(a.bits[blkB + lane]) : 0;
+    const int oA = int(a.offs[blkA]), oB = int(a.offs[blkB]);
+    wait_vmcnt<0>();   // the compiler tracks only these loads
+    const uint32_t* szpA = a.sz + blkA * 64;
+    const uint32_t* szpB = a.sz + blkB * 64;
+    const _Float16* xp = a.x + size_t(col0) * 128;
+    const uint8_t* cpA = a.codes + size_t(uniform(oA)) * 1024;
+    const uint8_t* cpB = a.codes + size_t(uniform(oB)) * 1024;
+    int jn = 0, used = 0, issued = 0;
+    uint32_t sbn = 0;
+    auto fill = [&]() {
+      while (jn < S) {
+        const int bA = uniform(__builtin_amdgcn_readlane(bvecA, jn));
+        const int bB = uniform(__builtin_amdgcn_readlane(bvecB, jn));
+        const int ns = 2 + nx + bA + bB;
+        if (used + ns > R) break;
+        dma4_once(szpA, 4 * lane, ring_lds, sbn);
+        for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
+        uint32_t sc = sbn + 1024 * (1 + nx);
+        for (int q = 0; q < bA; ++q) {
+          dma16_once(cpA, 16 * lane, ring_lds, sc & MASK);
+          cpA += 1024;
+          sc += 1024;
+        }
+        dma4_once(szpB, 4 * lane, ring_lds, sc & MASK);
+        sc += 1024;
+        for (int q = 0; q < bB; ++q) {
+          dma16_once(cpB, 16 * lane, ring_lds, sc & MASK);
+          cpB += 1024;
+          sc += 1024;
+        }
+        szpA += 64;
+        szpB += 64;
+        xp += 128;
+        sbn = sc & MASK;
+        used += ns;
+        issued += ns;
+        ++jn;
+      }
+    };
+    fill();
+    uint32_t sb = 0;
+    int done = 0;
+    for (int j = 0; j < S; ++j) {
+      const int bA = uniform(__builtin_amdgcn_readlane(bvecA, j));
+      const int bB = uniform(__builtin_amdgcn_readlane(bvecB, j));
+      done += 2 + nx + bA + bB;
+      wait_vmcnt_at_most(issued - done);
+      // row A's block shares the activations with row B's: the slots of the
+      // column are released only after row B's reads
+      auto keep = []() {};
+      auto refill = [&]() {
+        used -= 2 + nx + bA + bB;
+        fill();
+      };
+      const uint32_t xb = sb + 1024, cbA = sb + 1024 * (1 + nx);
+      const uint32_t sbB = cbA + 1024 * bA, cbB = sbB + 1024;
+      switch (bA) {
+        case 1: block_mma<1, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        case 2: block_mma<2, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        case 3: block_mma<2, 1, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        case 4: block_mma<4, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        case 6: block_mma<4, 2, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        default: block_mma<4, 4, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+      }
+      switch (bB) {
+        case 1: block_mma<1, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        case 2: block_mma<2, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        case 3: block_mma<2, 1, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        case 4: block_mma<4, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        case 6: block_mma<4, 2, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        default: block_mma<4, 4, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+      }
+      sb = (sb + 1024 * (2 + nx + bA + bB)) & MASK;
+    }
+  }
+  __syncthreads();
+
+  // waves meet in LDS; wave w adds row tile w of both rows over the waves
+  static_assert(NW * 2 * 4 * MT <= NW * R, "reduction fits in the rings");
+  f32x4 (*red)[2][4][MT][64] = reinterpret_cast<f32x4 (*)[2][4][MT][64]>(lds);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[wave][r][rt][mt][lane] = acc[r][rt][mt];
+  __syncthreads();
+  const int rt = wave;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !hasB) break;
+    const int n = (r ? brB : brA) * 64 + 16 * rt + r16;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 s = red[0][r][rt][mt][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s += red[w][r][rt][mt][lane];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * mt + 4 * g + v;
@@ -582,6 +739,7 @@ DecodePlan decode_plan(int N, int K, int M) {
   DecodePlan p;
   const int nbr = N / 64, nbc = K / 128;
   p.nw = 4;
+  p.rows = 1;
   int nseg = 1;
   if (M == 1) {
     // Single token: every wave takes k blocks of a block row (k = 4, 2 or
@@ -599,16 +757,21 @@ DecodePlan decode_plan(int N, int K, int M) {
     nseg = (nbc + 4 * k - 1) / (4 * k);
   } else {
     // 4-wave workgroups resident per CU: two for M <= 16 (64 KiB of LDS
-    // rings each), one for larger M (128 KiB).  One workgroup per block row
-    // when that fills the resident slots; else split K into as many segments
-    // as still fit in one resident wave of workgroups, with at least 2
-    // columns per wave, capped by the hand-off traffic (nseg * M * N * 8
-    // bytes against ~N * K / 2).
+    // rings each), one for larger M (128 KiB).  A workgroup owns one block
+    // row, or two for M > 16 on matrices of at least 2^26 weights (smaller
+    // ones lose more to the halved workgroup count than they gain: Llama-3
+    // sweeps at M = 20 and 32).  One workgroup per row unit when that fills
+    // the resident slots; else split K into as many segments as still fit
+    // in one resident wave of workgroups, with at least 2 columns per wave,
+    // capped by the hand-off traffic (nseg * M * N * 8 bytes against
+    // ~N * K / 2; twice that for M > 16, where the sweeps favour the split).
     const int resident = (M <= 16 ? 2 : 1) * 256;
-    if (nbr < resident) {
-      nseg = resident / nbr;
+    if (M > 16 && size_t(N) * size_t(K) >= (size_t(1) << 26)) p.rows = 2;
+    const int units = (nbr + p.rows - 1) / p.rows;
+    if (units < resident) {
+      nseg = resident / units;
       nseg = min(nseg, max(1, nbc / (2 * p.nw)));
-      nseg = min(nseg, max(1, K / (64 * M)));
+      nseg = min(nseg, max(1, K / ((M > 16 ? 32 : 64) * M)));
     }
   }
   nseg = min(nseg, kMaxSegments);
@@ -636,15 +799,18 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   a.nbc = im.nbc;
   a.seg_cols = plan.seg_cols;
   a.nseg = plan.nseg;
-  const dim3 grid(unsigned(im.nbr * plan.nseg));
+  const int units = (im.nbr + plan.rows - 1) / plan.rows;
+  const dim3 grid(unsigned(units * plan.nseg));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M == 1)
     hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a.bits, a.offs, a.sz, a.codes, a.x, a.nbc,
                        a.seg_cols, a.nseg, a.y, a.acc, a.facc, a.N, a.K, a.M, a.nbr);
   else if (M <= 16)
     hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
-  else
+  else if (plan.rows == 1)
     hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode2_kernel<2>), grid, dim3(256), 0, s, a);
   return int(hipGetLastError());
 }
 

@@ -32,6 +32,7 @@ constexpr int kMaxRows = 1 << 20;   // N limit of the block format's entry point
 constexpr int kMaxSegments = 32;    // K segments per block row (fits the count field)
 struct DecodePlan {
   int nw, nseg, seg_cols;
+  int rows;   // block rows per workgroup (1, or 2 for large matrices at M > 16)
   size_t ws_bytes;
 };
 DecodePlan decode_plan(int N, int K, int M);

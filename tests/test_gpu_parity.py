@@ -195,6 +195,37 @@ def test_split_k_large_partials(M):
     assert not torch.any(ws)
 
 
+@pytest.mark.parametrize("M", [17, 32])
+def test_two_row_workgroups(M):
+    """At M > 16 a matrix of at least 2^26 weights runs two block rows per
+    workgroup; 129 block rows leave the last workgroup a single one.  The
+    K segments' partials include huge cancelling ones (fp32 overflow
+    accumulator) and outputs must repeat bit for bit over calls on one
+    workspace, which is clean after each."""
+    N, K = 129 * 64, 8192
+    g = np.random.default_rng(94)
+    W = g.standard_normal((N, K)).astype(np.float16)
+    W[:, K - 128:] = W[:, :128]
+    bits = synth.random_bitmap(N, K, ALLOWED, 94)
+    bits[:, 0] = bits[:, -1] = 8
+    x = g.standard_normal((M, K)).astype(np.float16)
+    x[0, :128] = 30000.0
+    x[0, K - 128:] = -30000.0
+    ws = torch.zeros(gbb.gemm_mixed_w_workspace(N, K, M), dtype=torch.uint8, device=dev())
+    assert ws.numel() > 0
+    img = packed(W, bits)
+    ref = bq.reference_gemm(x, W, bits)
+    first = None
+    for _ in range(3):
+        y = gbb.gemm_mixed_w_path(img, N, K, to_dev(x), 1, workspace=ws)
+        assert rel_err(y, ref) <= TOL
+        assert not torch.any(ws)
+        if first is None:
+            first = y.cpu()
+        else:
+            assert torch.equal(y.cpu().view(torch.int16), first.view(torch.int16))
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_split_k_nan_then_clean(M):
     """A NaN activation reaches every output through the overflow
