@@ -8,6 +8,8 @@ no CPU fallback -- if the library is missing every call raises.
 """
 from .binding import (  # noqa: F401
     GbbError,
+    allocate_bits,
+    channel_order,
     check_image,
     dequant,
     gemm_mixed_w,

@@ -37,6 +37,8 @@ _SIGS = {
     "gbb_packed_bytes": (_sz, [_vp, _i, _i]),
     "gbb_pack_blocks": (_i, [_vp, _i, _i, _vp, _vp, _vp, _u, _vp, _sz]),
     "gbb_check_image": (_i, [_vp, _sz, _i, _i]),
+    "gbb_allocate_bits": (_i, [_vp, _i, _i, ctypes.c_double, ctypes.c_double, _vp]),
+    "gbb_channel_order": (_i, [_vp, _i, _i, _vp, _vp]),
     "gbb_gemm_mixed_w_workspace": (_sz, [_i, _i, _i]),
     "gbb_gemm_mixed_w": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_gemm_mixed_w_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
@@ -104,6 +106,27 @@ def packed_bytes(bits: np.ndarray, N: int, K: int) -> int:
         _check(lib().gbb_pack_blocks(None, N, K, _np_ptr(bits), None, None, 0, None, 0))
         _check(-1)
     return n
+
+
+def allocate_bits(W: np.ndarray, target_bits: float, gamma: float = 0.05) -> np.ndarray:
+    """Per-block bitwidths uint8 [N/64][K/128] of mean <= target_bits for fp16
+    W [N][K] (host; see gbb_allocate_bits)."""
+    Wu = _as_u16(W)
+    N, K = Wu.shape
+    bits = np.empty((N // 64, K // 128), np.uint8)
+    _check(lib().gbb_allocate_bits(_np_ptr(Wu), N, K, float(target_bits), float(gamma), _np_ptr(bits)))
+    return bits
+
+
+def channel_order(W: np.ndarray):
+    """(row_order int32 [N], col_order int32 [K]) by descending L1 norm of fp16
+    W [N][K] (host; see gbb_channel_order)."""
+    Wu = _as_u16(W)
+    N, K = Wu.shape
+    rows = np.empty(N, np.int32)
+    cols = np.empty(K, np.int32)
+    _check(lib().gbb_channel_order(_np_ptr(Wu), N, K, _np_ptr(rows), _np_ptr(cols)))
+    return rows, cols
 
 
 def pack_blocks(W: np.ndarray, bits: np.ndarray, scale: np.ndarray | None = None,

@@ -418,3 +418,169 @@ extern "C" gbb_status gbb_pack_w48(const uint16_t* W, int N, int K, const int32_
   });
   return GBB_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Offline bitwidth allocation and channel reordering (ScaleBITS explainer,
+// sections 1.2.1, 2.2 and 4.2), with a weight-magnitude proxy in place of the
+// gradient sensitivity, which needs a model and calibration data.
+//
+// Objective of block i at bitwidth b: S_i * e_i(b), with S_i = sum |w| over
+// the block (exact in binary64: fp16 values are multiples of 2^-24 and a
+// block sums to less than 2^29) and e_i(b) = sum (w - w'_b)^2 under this
+// file's group quantizer, summed in binary64 in row-major order.  Every
+// block starts at 3 bits and moves one step of {1,2,3,4,6,8} at a time.
+// A round: over the budget, lower the k = max(1, floor(gamma nblk + 1/2))
+// blocks of least per-bit cost; within it, raise the blocks of largest
+// per-bit gain whose step still fits (at most k); when none fits, trade the
+// max(1, k / 2) best raises for as many cheapest lowerings if that lowers the
+// objective and keeps the budget, else stop; at most 64 + floor(4 / gamma)
+// rounds.  Ties go to the lower block index.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kAllowed[6] = {1, 2, 3, 4, 6, 8};
+int bit_index(int b) { return b <= 4 ? b - 1 : (b == 6 ? 4 : 5); }
+int step_up(int b) { return b == 4 ? 6 : (b == 6 ? 8 : b + 1); }
+int step_down(int b) { return b == 6 ? 4 : (b == 8 ? 6 : b - 1); }
+
+struct Ranked {
+  double key;
+  int idx;
+};
+
+}  // namespace
+
+extern "C" gbb_status gbb_allocate_bits(const uint16_t* W, int N, int K, double target_bits, double gamma,
+                                        uint8_t* bits) {
+  if (!W || !bits) return fail(GBB_E_ARG, "W and bits must not be NULL");
+  if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive");
+  if (N % kBlockRows || K % kGroup) return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128");
+  if (!(target_bits >= 1.0 && target_bits <= 8.0)) return fail(GBB_E_ARG, "target_bits must lie in [1, 8]");
+  if (!(gamma > 0.0 && gamma <= 1.0)) return fail(GBB_E_ARG, "gamma must lie in (0, 1]");
+  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+  const int nbr = N / kBlockRows, nbc = K / kGroup, n = nbr * nbc;
+
+  // block statistics: S[i] and E[i][bit_index(b)]
+  std::vector<double> S(n), E(size_t(n) * 6);
+  parallel_for(n, [&](long i) {
+    const int br = int(i / nbc), bc = int(i % nbc);
+    double v[kGroup], s = 0;
+    for (int r = 0; r < kBlockRows; ++r)
+      for (int c = 0; c < kGroup; ++c)
+        s += std::fabs(half_to_double(W[size_t(br * kBlockRows + r) * K + size_t(bc) * kGroup + c]));
+    S[i] = s;
+    for (int t = 0; t < 6; ++t) {
+      const double levels = double((1 << kAllowed[t]) - 1);
+      double e = 0;
+      for (int r = 0; r < kBlockRows; ++r) {
+        const uint16_t* src = W + size_t(br * kBlockRows + r) * K + size_t(bc) * kGroup;
+        for (int c = 0; c < kGroup; ++c) v[c] = half_to_double(src[c]);
+        const GroupQ gq = asym_scale_zero(v, kGroup, levels);
+        for (int c = 0; c < kGroup; ++c) {
+          const float qz = float(asym_code(v[c], gq, levels)) - float(gq.z);
+          const double d = v[c] - double(qz * float(gq.s));
+          e += d * d;
+        }
+      }
+      E[size_t(i) * 6 + t] = e;
+    }
+  });
+
+  std::vector<int> b(n, 3);
+  const int k = std::max(1, int(std::floor(gamma * n + 0.5)));
+  const double budget = target_bits * n;
+  auto err = [&](int i, int bw) { return E[size_t(i) * 6 + bit_index(bw)]; };
+  auto up = [&](int i) {
+    const int b2 = step_up(b[i]);
+    return S[i] * (err(i, b[i]) - err(i, b2)) / double(b2 - b[i]);
+  };
+  auto down = [&](int i) {
+    const int b2 = step_down(b[i]);
+    return S[i] * (err(i, b2) - err(i, b[i])) / double(b[i] - b2);
+  };
+  // ascending key, ties to the lower index
+  auto by_key = [](const Ranked& x, const Ranked& y) { return x.key < y.key || (x.key == y.key && x.idx < y.idx); };
+  std::vector<Ranked> rk;
+  rk.reserve(n);
+  const int rounds = 64 + int(std::floor(4.0 / gamma));
+  for (int round = 0; round < rounds; ++round) {
+    long total = 0;
+    for (int i = 0; i < n; ++i) total += b[i];
+    if (double(total) > budget) {
+      rk.clear();
+      for (int i = 0; i < n; ++i)
+        if (b[i] > 1) rk.push_back({down(i), i});
+      std::sort(rk.begin(), rk.end(), by_key);
+      for (int j = 0; j < k && j < int(rk.size()); ++j) b[rk[j].idx] = step_down(b[rk[j].idx]);
+      continue;
+    }
+    double slack = budget - double(total);
+    rk.clear();
+    for (int i = 0; i < n; ++i)
+      if (b[i] < 8) rk.push_back({-up(i), i});
+    std::sort(rk.begin(), rk.end(), by_key);
+    const std::vector<Ranked> ups = rk;
+    int raised = 0;
+    for (const Ranked& u : ups) {
+      if (raised == k) break;
+      const int step = step_up(b[u.idx]) - b[u.idx];
+      if (double(step) <= slack) {
+        b[u.idx] = step_up(b[u.idx]);
+        slack -= double(step);
+        ++raised;
+      }
+    }
+    if (raised) continue;
+    const int h = std::max(1, k / 2);
+    std::vector<int> chosen;
+    for (int j = 0; j < h && j < int(ups.size()); ++j) chosen.push_back(ups[j].idx);
+    // pay for the raises with the cheapest lowerings of other blocks until
+    // the bits freed cover the overshoot of the budget
+    long need_bits = total;
+    for (int i : chosen) need_bits += step_up(b[i]) - b[i];
+    const double need = double(need_bits) - budget;
+    rk.clear();
+    for (int i = 0; i < n; ++i)
+      if (b[i] > 1) rk.push_back({down(i), i});
+    std::sort(rk.begin(), rk.end(), by_key);
+    std::vector<int> downs;
+    long freed = 0;
+    for (const Ranked& d : rk) {
+      if (double(freed) >= need) break;
+      if (std::find(chosen.begin(), chosen.end(), d.idx) != chosen.end()) continue;
+      downs.push_back(d.idx);
+      freed += b[d.idx] - step_down(b[d.idx]);
+    }
+    double gain = 0, cost = 0;
+    for (int i : chosen) gain += S[i] * (err(i, b[i]) - err(i, step_up(b[i])));
+    for (int i : downs) cost += S[i] * (err(i, step_down(b[i])) - err(i, b[i]));
+    if (chosen.empty() || double(freed) < need || !(gain > cost)) break;
+    for (int i : chosen) b[i] = step_up(b[i]);
+    for (int i : downs) b[i] = step_down(b[i]);
+  }
+  for (int i = 0; i < n; ++i) bits[i] = uint8_t(b[i]);
+  return GBB_OK;
+}
+
+extern "C" gbb_status gbb_channel_order(const uint16_t* W, int N, int K, int32_t* row_order, int32_t* col_order) {
+  if (!W || !row_order || !col_order) return fail(GBB_E_ARG, "W, row_order and col_order must not be NULL");
+  if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive");
+  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+  // exact L1 norms in units of 2^-24 (the fp16 quantum)
+  std::vector<int64_t> rl(N, 0), cl(K, 0);
+  for (int r = 0; r < N; ++r)
+    for (int c = 0; c < K; ++c) {
+      const int64_t a = int64_t(std::ldexp(std::fabs(half_to_double(W[size_t(r) * K + c])), 24));
+      rl[r] += a;
+      cl[c] += a;
+    }
+  auto order = [](const std::vector<int64_t>& l1, int32_t* out) {
+    std::vector<int32_t> idx(l1.size());
+    for (size_t i = 0; i < idx.size(); ++i) idx[i] = int32_t(i);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return l1[a] > l1[b]; });
+    std::copy(idx.begin(), idx.end(), out);
+  };
+  order(rl, row_order);
+  order(cl, col_order);
+  return GBB_OK;
+}

@@ -94,6 +94,38 @@ gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits,
                            uint16_t* scale, uint16_t* zero, unsigned flags,
                            void* image, size_t image_cap);
 
+/* Offline bitwidth allocation (host, synchronous, deterministic): one
+ * bitwidth from {1,2,3,4,6,8} per 64x128 block with a mean of at most
+ * target_bits, by the batched greedy of the ScaleBITS explainer page
+ * (section 2.2: gamma * nblk blocks per round, gamma = 0.05 there; section
+ * 4.2: the bitwidth set and the 3-bit start).  The pages' gradient
+ * sensitivity needs a model and calibration data; here block i's cost at
+ * bitwidth b is S_i * e_i(b), S_i = sum |w| over the block, e_i(b) = sum
+ * (w - w')^2 under gbb_pack_blocks' quantizer.  Rounds lower the cheapest
+ * blocks while over budget, raise the most beneficial ones that fit while
+ * under it, then trade the most beneficial raises for the cheapest
+ * lowerings that pay for them while that lowers the summed cost; ties go to
+ * the lower block index.
+ *   W            fp16 [N][K], finite; N % 64 == 0, K % 128 == 0.
+ *   target_bits  mean bitwidth budget in [1, 8].
+ *   gamma        fraction of the blocks moved per round, in (0, 1].
+ *   bits         host output [N/64][K/128], row-major.
+ * Errors: GBB_E_ARG (NULL, non-finite W, target or gamma out of range),
+ * GBB_E_SHAPE. */
+gbb_status gbb_allocate_bits(const uint16_t* W, int N, int K, double target_bits, double gamma,
+                             uint8_t* bits);
+
+/* Bidirectional channel reordering (ScaleBITS explainer page, section
+ * 1.2.1) with |W| as the sensitivity: rows and columns by descending L1
+ * norm (exact), ties to the lower index.  Packing W[row_order][:, col_order]
+ * gathers the large weights in the top-left blocks; the caller permutes the
+ * activations (x[:, col_order]) and un-permutes the outputs accordingly.
+ *   W          fp16 [N][K], finite, any N, K > 0.
+ *   row_order  host output [N] (a permutation of 0 ... N-1).
+ *   col_order  host output [K].
+ * Errors: GBB_E_ARG. */
+gbb_status gbb_channel_order(const uint16_t* W, int N, int K, int32_t* row_order, int32_t* col_order);
+
 /* Check a host copy of an image header against N and K (GBB_E_FORMAT). */
 gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 

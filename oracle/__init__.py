@@ -16,6 +16,8 @@ image       an independent reader for the packed block image, written from the
 w48         output-feature mixed W8(sym)/W4(asym) x A8(sym) reference: row
             split, weight and activation quantizers, two-step group GEMM.
 model       the arithmetic-intensity formula of the MixLLM page.
+alloc       offline bitwidth allocation (batched greedy) and bidirectional
+            channel reordering, with a weight-magnitude sensitivity proxy.
 
 Precision: quantization decisions for weights are taken in fp64; the
 activation quantizer takes them in fp32 (the precision of the GPU kernel
@@ -23,4 +25,4 @@ that produces the int8 activations); reference products are fp64.
 Every function names the passage it follows.  Functions without an
 independent pin say "parity unpinned" -- none currently.
 """
-from . import blockquant, image, model, w48  # noqa: F401
+from . import alloc, blockquant, image, model, w48  # noqa: F401

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import alloc
 from oracle import blockquant as bq
 from oracle import w48 as ow48
 
@@ -366,6 +367,30 @@ def test_prefill_70b_mlp_m2048(i):
     rows = sample_rows(p.N, 20 + i, 12)
     ref = bq.reference_rows(x, W, bits, rows)
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+def test_reordered_allocated_layer():
+    """Offline chain: channel order, bit allocation on the reordered weight,
+    packing, then the kernels on the permuted activations; the outputs,
+    scattered back by the row order, approximate W x."""
+    N, K = 1024, 2048
+    W = synth.weight_heavy_rows(N, K, synth.WL_LLAMA3_8B, 1)
+    r, c = gbb.channel_order(W)
+    Wr = np.ascontiguousarray(W[r][:, c])
+    bits = gbb.allocate_bits(Wr, 3.0)
+    assert np.array_equal(bits, alloc.allocate(Wr, 3.0))
+    assert synth.mean_bits(bits) <= 3.0 and np.unique(bits).size > 1
+    img = packed(Wr, bits)
+    for M in (1, 8, 64):
+        x = rand_x(M, K, 77 + M)
+        xr = np.ascontiguousarray(x[:, c])
+        y = gbb.gemm_mixed_w(img, N, K, to_dev(xr)).cpu().numpy().astype(np.float64)
+        ref = bq.reference_rows(xr, Wr, bits, np.arange(N))
+        assert bq.rel_inf_err(y, ref) <= TOL
+        full = np.empty_like(y)
+        full[:, r] = y
+        exact = x.astype(np.float64) @ W.astype(np.float64).T
+        assert bq.rel_inf_err(full, exact) <= 0.25
 
 
 # ----------------------------------------------------------------------------
