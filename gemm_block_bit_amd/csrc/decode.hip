@@ -203,18 +203,21 @@ __device__ __forceinline__ constexpr float pow2(int e) {
   return e >= 0 ? float(1ull << e) : 1.0f / float(1ull << -e);
 }
 
-// One block of planes W0 (shift 0) and W1 (shift W0; 0 = none) whose records
-// start at ring byte offset sb: read them, let `refill` reuse the slots, then
-// acc += s (sum over planes of 2^(24 + shift - o) C - z X).
-// The ring offsets are those of its scale/zero slot (sz), first activation
-// slot (xb) and first code slot (cb).
-template <int W0, int W1, int MT, class Refill>
-__device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint32_t xb, uint32_t cb, int M,
-                                          f32x4 (&acc)[4][MT], Refill&& refill) {
+// Byte offset off (below 2 RS KiB) wrapped into a ring of RS 1 KiB slots.
+template <int RS>
+__device__ __forceinline__ uint32_t wrap(uint32_t off) {
+  if constexpr ((RS & (RS - 1)) == 0)
+    return off & (RS * 1024u - 1u);
+  else
+    return off >= RS * 1024u ? off - RS * 1024u : off;
+}
+
+// A block column's activation fragments from the ring: lane holds tokens
+// 16 mt + r16 (rows past M repeat row M - 1), columns 32 kt + 8 g ... + 7.
+template <int MT>
+__device__ __forceinline__ void read_x(const u32x4* ring, uint32_t xb, int M, half8 (&xa)[4][MT]) {
   constexpr uint32_t MASK = Ring<MT>::kMask;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const u32x4 sz = ring[((szb & MASK) >> 4) + r16];
-  half8 xa[4][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(16 * mt + r16, M - 1);
@@ -222,46 +225,78 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint3
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
   }
+}
+
+// One block of planes W0 (shift 0) and W1 (shift W0; 0 = none) on the
+// activation fragments xa: read its scale/zero slot (ring byte offset szb)
+// and code slots (cb), let `refill` reuse the slots, then
+// acc += s (sum over planes of 2^(24 + shift - o) C - z X), where X (xsum)
+// is the sum of the block column's activations per token -- formed here by
+// MFMAs on a ones operand when SumX, else passed in from the block of the
+// same column in another row.  The plane weight 2^(24 - o) of the first
+// plane is folded into s and z once per row tile (exact: powers of two), so
+// each output takes one fewer vector instruction with the same roundings.
+template <int W0, int W1, int MT, bool SumX, int RS = Ring<MT>::kSlots, class Refill>
+__device__ __forceinline__ void block_core(const u32x4* ring, uint32_t szb, uint32_t cb, const half8 (&xa)[4][MT],
+                                           f32x4 (&xsum)[MT], f32x4 (&acc)[4][MT], Refill&& refill) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15;
+  const u32x4 sz = ring[(wrap<RS>(szb) >> 4) + r16];
   u32x4 w0[W0], w1[W1 ? W1 : 1];
 #pragma unroll
-  for (int q = 0; q < W0; ++q) w0[q] = ring[(((cb + 1024 * q) & MASK) >> 4) + lane];
+  for (int q = 0; q < W0; ++q) w0[q] = ring[(wrap<RS>(cb + 1024 * q) >> 4) + lane];
 #pragma unroll
-  for (int q = 0; q < W1; ++q) w1[q] = ring[(((cb + 1024 * (W0 + q)) & MASK) >> 4) + lane];
+  for (int q = 0; q < W1; ++q) w1[q] = ring[(wrap<RS>(cb + 1024 * (W0 + q)) >> 4) + lane];
   wait_lds();
   refill();
 
-  const half8 ones = as_half8(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
-  f32x4 xsum[MT], c0[4][MT], c1[4][MT];
+  f32x4 c0[4][MT], c1[4][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    xsum[mt] = f32x4{0, 0, 0, 0};
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) c0[rt][mt] = c1[rt][mt] = f32x4{0, 0, 0, 0};
+  if constexpr (SumX) {
+    const half8 ones = as_half8(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xsum[mt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xsum[mt] = mfma16(xa[kt][mt], ones, xsum[mt]);
   }
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xsum[mt] = mfma16(xa[kt][mt], ones, xsum[mt]);
   plane_mma<W0, MT>(w0, xa, c0);
   if constexpr (W1 != 0) plane_mma<W1, MT>(w1, xa, c1);
   // lane holds tokens 16 mt + 4 g + v
   constexpr int W1g = W1 ? W1 : 1;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const float s = lo_half(sz[rt]), z = hi_half(sz[rt]);
-    constexpr float k0[4] = {pow2(24 - PlaneGeom<W0>::off(0)), pow2(24 - PlaneGeom<W0>::off(1)),
-                             pow2(24 - PlaneGeom<W0>::off(2)), pow2(24 - PlaneGeom<W0>::off(3))};
-    constexpr float k1[4] = {pow2(24 + W0 - PlaneGeom<W1g>::off(0)), pow2(24 + W0 - PlaneGeom<W1g>::off(1)),
-                             pow2(24 + W0 - PlaneGeom<W1g>::off(2)), pow2(24 + W0 - PlaneGeom<W1g>::off(3))};
+    constexpr int o0[4] = {PlaneGeom<W0>::off(0), PlaneGeom<W0>::off(1), PlaneGeom<W0>::off(2),
+                           PlaneGeom<W0>::off(3)};
+    constexpr int o1[4] = {PlaneGeom<W1g>::off(0), PlaneGeom<W1g>::off(1), PlaneGeom<W1g>::off(2),
+                           PlaneGeom<W1g>::off(3)};
+    const float s = lo_half(sz[rt]) * pow2(24 - o0[rt]);
+    const float z = hi_half(sz[rt]) * pow2(o0[rt] - 24);
+    constexpr float k10[4] = {pow2(W0 - o1[0] + o0[0]), pow2(W0 - o1[1] + o0[1]), pow2(W0 - o1[2] + o0[2]),
+                              pow2(W0 - o1[3] + o0[3])};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float t = c0[rt][mt][v] * k0[rt];
-        if constexpr (W1 != 0) t = __builtin_fmaf(c1[rt][mt][v], k1[rt], t);
+        float t = c0[rt][mt][v];
+        if constexpr (W1 != 0) t = __builtin_fmaf(c1[rt][mt][v], k10[rt], t);
         acc[rt][mt][v] = __builtin_fmaf(s, __builtin_fmaf(-z, xsum[mt][v], t), acc[rt][mt][v]);
       }
   }
+}
+
+// One block whose records start at ring byte offsets sz (scale/zero slot),
+// xb (first activation slot) and cb (first code slot).
+template <int W0, int W1, int MT, class Refill>
+__device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint32_t xb, uint32_t cb, int M,
+                                          f32x4 (&acc)[4][MT], Refill&& refill) {
+  half8 xa[4][MT];
+  read_x<MT>(ring, xb, M, xa);
+  f32x4 xsum[MT];
+  block_core<W0, W1, MT, true>(ring, szb, cb, xa, xsum, acc, refill);
 }
 
 template <int NW, int MT>
@@ -390,18 +425,50 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
   }
 }
 
-// Two block rows per wave (17 <= M <= 32): at that batch a block column's
-// activations take eight 1 KiB slots against ~2-3 KiB of codes, so the ring
-// mostly holds activations and keeps only about three blocks in flight.  A
-// workgroup owns two consecutive block rows; for each column a wave loads the
-// activations once and the two rows' blocks behind them, and runs both
-// blocks on them: [sz A | activations | codes A | sz B | codes B].
+// Two block rows per wave (17 <= M <= 32).  At that batch a block column's
+// activations are eight 1 KiB slots against ~2-3 KiB of codes per block.
+// A workgroup owns two consecutive block rows; for each column a wave reads
+// the activations into registers once and runs both rows' blocks on them.
+// The activations have a one-column buffer of their own, refilled with the
+// next column as soon as the current one is in registers, so the code ring
+// holds only scale/zero records and codes: [sz A | codes A], [sz B | codes B]
+// records in column order, each released as soon as its block has read it.
+// Twelve slots take any record (at most 1 + 8), so each wave needs 20 KiB
+// of LDS and two four-wave workgroups share a CU: two waves per SIMD, which
+// hide each other's LDS and matrix-core latencies.
+constexpr int kRing2 = 12;   // code ring slots per wave
+constexpr int kXs2 = 8;      // activation slots per wave (4 tokens each)
+
+// Sequence numbers of the last load of the next six records in the ring, a
+// shift register indexed only by constants (no private-memory array).
+struct RecordEnds {
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0, q4 = 0, q5 = 0;
+  __device__ void set(int pos, int v) {
+    switch (pos) {
+      case 0: q0 = v; break;
+      case 1: q1 = v; break;
+      case 2: q2 = v; break;
+      case 3: q3 = v; break;
+      case 4: q4 = v; break;
+      default: q5 = v; break;
+    }
+  }
+  __device__ void pop() {
+    q0 = q1;
+    q1 = q2;
+    q2 = q3;
+    q3 = q4;
+    q4 = q5;
+  }
+};
+
 template <int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode2_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode2_kernel(DecodeArgs a) {
   constexpr int NW = 4;
-  constexpr int R = Ring<MT>::kSlots;
-  constexpr uint32_t MASK = Ring<MT>::kMask;
-  static_assert(2 + 4 * MT + 16 <= R, "a column's records of two rows fit in the ring");
+  constexpr int R = kRing2;
+  static_assert(1 + 8 <= R, "any block's records fit in the ring");
+  static_assert(R / 2 <= 6, "records take two slots or more, so at most six sit in the ring");
+  static_assert(4 * MT <= kXs2, "a column's activations fit in the activation slots");
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int rp = blockIdx.x / a.nseg, seg = blockIdx.x - rp * a.nseg;
@@ -418,9 +485,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
   for (int xi = 0; xi < 8; ++xi) xoff[xi] = uint32_t(min(4 * xi + g, M - 1)) * uint32_t(2 * a.K) + 16 * r16;
 
-  __shared__ u32x4 lds[NW * R * 64];   // per-wave rings; reused for the reduction
-  const u32x4* ring = lds + wave * R * 64;
+  // per wave: the code ring, then the activation slots; reused for the reduction
+  __shared__ u32x4 lds[NW * (R + kXs2) * 64];
+  const u32x4* ring = lds + wave * (R + kXs2) * 64;
+  const u32x4* xbuf = ring + R * 64;
   const uint32_t ring_lds = lds_addr(ring);
+  constexpr uint32_t kXbuf = R * 1024;   // activation slots, relative to the ring
 
   f32x4 acc[2][4][MT];
 #pragma unroll
@@ -443,78 +513,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const _Float16* xp = a.x + size_t(col0) * 128;
     const uint8_t* cpA = a.codes + size_t(uniform(oA)) * 1024;
     const uint8_t* cpB = a.codes + size_t(uniform(oB)) * 1024;
-    int jn = 0, used = 0, issued = 0;
-    uint32_t sbn = 0;
+    int issued = 0;      // loads issued
+    int ri = 0, rc = 0;  // records issued / consumed: A0, B0, A1, B1, ...
+    int used = 0;        // ring slots of issued records not yet released
+    uint32_t sbn = 0;    // ring byte offset of the next record to issue
+    RecordEnds ends;
+    for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, kXbuf + 1024 * xi);
+    issued += nx;
+    int xend = issued;   // loads up to the current column's activations
     auto fill = [&]() {
-      while (jn < S) {
-        const int bA = uniform(__builtin_amdgcn_readlane(bvecA, jn));
-        const int bB = uniform(__builtin_amdgcn_readlane(bvecB, jn));
-        const int ns = 2 + nx + bA + bB;
-        if (used + ns > R) break;
-        dma4_once(szpA, 4 * lane, ring_lds, sbn);
-        for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
-        uint32_t sc = sbn + 1024 * (1 + nx);
-        for (int q = 0; q < bA; ++q) {
-          dma16_once(cpA, 16 * lane, ring_lds, sc & MASK);
-          cpA += 1024;
-          sc += 1024;
+      while (ri < 2 * S) {
+        const int col = ri >> 1;
+        const bool rowB = (ri & 1) != 0;
+        const int b = uniform(__builtin_amdgcn_readlane(rowB ? bvecB : bvecA, col));
+        if (used + 1 + b > R) break;
+        if (!rowB) {
+          dma4_once(szpA, 4 * lane, ring_lds, sbn);
+          szpA += 64;
+          for (int q = 0; q < b; ++q) {
+            dma16_once(cpA, 16 * lane, ring_lds, wrap<R>(sbn + 1024 * (1 + q)));
+            cpA += 1024;
+          }
+        } else {
+          dma4_once(szpB, 4 * lane, ring_lds, sbn);
+          szpB += 64;
+          for (int q = 0; q < b; ++q) {
+            dma16_once(cpB, 16 * lane, ring_lds, wrap<R>(sbn + 1024 * (1 + q)));
+            cpB += 1024;
+          }
         }
-        dma4_once(szpB, 4 * lane, ring_lds, sc & MASK);
-        sc += 1024;
-        for (int q = 0; q < bB; ++q) {
-          dma16_once(cpB, 16 * lane, ring_lds, sc & MASK);
-          cpB += 1024;
-          sc += 1024;
-        }
-        szpA += 64;
-        szpB += 64;
-        xp += 128;
-        sbn = sc & MASK;
-        used += ns;
-        issued += ns;
-        ++jn;
+        sbn = wrap<R>(sbn + 1024 * (1 + b));
+        used += 1 + b;
+        issued += 1 + b;
+        ends.set(ri - rc, issued);
+        ++ri;
       }
     };
     fill();
-    uint32_t sb = 0;
-    int done = 0;
+    uint32_t sb = 0;   // ring byte offset of the next record to consume
     for (int j = 0; j < S; ++j) {
       const int bA = uniform(__builtin_amdgcn_readlane(bvecA, j));
       const int bB = uniform(__builtin_amdgcn_readlane(bvecB, j));
-      done += 2 + nx + bA + bB;
-      wait_vmcnt_at_most(issued - done);
-      // row A's block shares the activations with row B's: the slots of the
-      // column are released only after row B's reads
-      auto keep = []() {};
-      auto refill = [&]() {
-        used -= 2 + nx + bA + bB;
+      // row A's record and the column's activations
+      wait_vmcnt_at_most(issued - max(ends.q0, xend));
+      half8 xa[4][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = min(16 * mt + r16, M - 1);
+        const u32x4* xr = xbuf + 64 * (m >> 2);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
+      }
+      f32x4 xsum[MT];
+      // after row A's reads: release its record, bring the next column's
+      // activations into the (now read) activation slots, refill the ring
+      auto afterA = [&]() {
+        used -= 1 + bA;
+        ends.pop();
+        ++rc;
+        if (j + 1 < S) {
+          xp += 128;
+          for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, kXbuf + 1024 * xi);
+          issued += nx;
+          xend = issued;
+        }
         fill();
       };
-      const uint32_t xb = sb + 1024, cbA = sb + 1024 * (1 + nx);
-      const uint32_t sbB = cbA + 1024 * bA, cbB = sbB + 1024;
+      const uint32_t cbA = wrap<R>(sb + 1024);
       switch (bA) {
-        case 1: block_mma<1, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
-        case 2: block_mma<2, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
-        case 3: block_mma<2, 1, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
-        case 4: block_mma<4, 0, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
-        case 6: block_mma<4, 2, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
-        default: block_mma<4, 4, MT>(ring, sb, xb, cbA, M, acc[0], keep); break;
+        case 1: block_core<1, 0, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
+        case 2: block_core<2, 0, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
+        case 3: block_core<2, 1, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
+        case 4: block_core<4, 0, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
+        case 6: block_core<4, 2, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
+        default: block_core<4, 4, MT, true, R>(ring, sb, cbA, xa, xsum, acc[0], afterA); break;
       }
+      sb = wrap<R>(sb + 1024 * (1 + bA));
+      // row B's record (issued at the latest by afterA's refill)
+      wait_vmcnt_at_most(issued - ends.q0);
+      auto afterB = [&]() {
+        used -= 1 + bB;
+        ends.pop();
+        ++rc;
+        fill();
+      };
+      const uint32_t cbB = wrap<R>(sb + 1024);
       switch (bB) {
-        case 1: block_mma<1, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
-        case 2: block_mma<2, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
-        case 3: block_mma<2, 1, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
-        case 4: block_mma<4, 0, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
-        case 6: block_mma<4, 2, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
-        default: block_mma<4, 4, MT>(ring, sbB, xb, cbB, M, acc[1], refill); break;
+        case 1: block_core<1, 0, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
+        case 2: block_core<2, 0, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
+        case 3: block_core<2, 1, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
+        case 4: block_core<4, 0, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
+        case 6: block_core<4, 2, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
+        default: block_core<4, 4, MT, false, R>(ring, sb, cbB, xa, xsum, acc[1], afterB); break;
       }
-      sb = (sb + 1024 * (2 + nx + bA + bB)) & MASK;
+      sb = wrap<R>(sb + 1024 * (1 + bB));
     }
   }
   __syncthreads();
 
   // waves meet in LDS; wave w adds row tile w of both rows over the waves
-  static_assert(NW * 2 * 4 * MT <= NW * R, "reduction fits in the rings");
+  static_assert(NW * 2 * 4 * MT <= NW * (R + kXs2), "reduction fits in the rings");
   f32x4 (*red)[2][4][MT][64] = reinterpret_cast<f32x4 (*)[2][4][MT][64]>(lds);
 #pragma unroll
   for (int r = 0; r < 2; ++r)
@@ -757,16 +855,17 @@ DecodePlan decode_plan(int N, int K, int M) {
     nseg = (nbc + 4 * k - 1) / (4 * k);
   } else {
     // 4-wave workgroups resident per CU: two for M <= 16 (64 KiB of LDS
-    // rings each), one for larger M (128 KiB).  A workgroup owns one block
-    // row, or two for M > 16 on matrices of at least 2^26 weights (smaller
-    // ones lose more to the halved workgroup count than they gain: Llama-3
-    // sweeps at M = 20 and 32).  One workgroup per row unit when that fills
+    // rings each) and for the two-row kernel (80 KiB), one for one row at
+    // M > 16 (128 KiB).  A workgroup owns one block row, or two for M > 16 on
+    // matrices of at least 2^26 weights (smaller ones lose more to the halved
+    // workgroup count than they gain: Llama-3 sweeps at M = 20 and 32).  One
+    // workgroup per row unit when that fills
     // the resident slots; else split K into as many segments as still fit
     // in one resident wave of workgroups, with at least 2 columns per wave,
     // capped by the hand-off traffic (nseg * M * N * 8 bytes against
     // ~N * K / 2; twice that for M > 16, where the sweeps favour the split).
-    const int resident = (M <= 16 ? 2 : 1) * 256;
     if (M > 16 && size_t(N) * size_t(K) >= (size_t(1) << 26)) p.rows = 2;
+    const int resident = (M <= 16 || p.rows == 2 ? 2 : 1) * 256;
     const int units = (nbr + p.rows - 1) / p.rows;
     if (units < resident) {
       nseg = resident / units;
