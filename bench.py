@@ -17,7 +17,7 @@ M = 1, 8 and 32, the M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16
 an fp16 library GEMM on the dequantized weights for context, the W4.4A8 layer
 (M = 32, 512, 4096) and the oracle timed on the host cores (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--extras a,b,...]
 """
 from __future__ import annotations
 
@@ -61,6 +61,10 @@ def measured_traffic():
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+# extra workloads after the headline, in run order
+EXTRAS = ("llama3_8b_m8", "mixed_vs_uniform", "linear_4096", "llama3_70b", "prefill", "w44a8")
 
 
 def log(msg):
@@ -215,10 +219,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline only (no extra workloads, no cpu baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated extra workloads to run after the headline (default: all of "
+                         + ", ".join(EXTRAS) + ")")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB elementwise copy (read 256 MiB, write 256 MiB) five times, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
     args = ap.parse_args()
+    want = set(w for w in args.extras.split(",") if w)
+    if want - set(EXTRAS):
+        ap.error("unknown extra workload(s): " + ", ".join(sorted(want - set(EXTRAS))))
+    if args.quick:
+        want = set()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the fused dequant-GEMM path has no multi-GPU component here "
               "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -290,7 +302,7 @@ def main():
              "graph_step_us": round(sec * 1e6, 1), "graph_step_us_p10_p50_p90": step_pct,
              "host_wall_us_per_step": round(wall * 1e6, 1)}
 
-    if not args.quick:
+    if "llama3_8b_m8" in want:
         # ---------------- same layers at M = 8 ----------------
         L8b = L8.with_batch(8, 8)
         s8, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)
@@ -298,6 +310,7 @@ def main():
         log(f"decode M=8: {total_bytes / s8 / 1e9:.0f} GB/s")
         del L8b
 
+    if "mixed_vs_uniform" in want:
         # ------- the same shapes with uniform 3- and 4-bit bitmaps, M = 1 -------
         # The mixed layers' GB/s against uniform layers' GB/s interpolated to
         # the same mean bitwidth: the cost of mixing bitwidths in one launch.
@@ -323,7 +336,7 @@ def main():
     del L8
     torch.cuda.empty_cache()
 
-    if not args.quick:
+    if "linear_4096" in want:
         # ---------------- one 4096 x 4096 matrix, M = 1 ----------------
         W, bits, x1 = synth.linear_4096()
         img, _, _ = gbb.pack_blocks(W, bits)
@@ -347,6 +360,7 @@ def main():
         del lin, d
         torch.cuda.empty_cache()
 
+    if "llama3_70b" in want:
         # ---------------- Llama-3-70B layer, decode M = 1 ----------------
         log("packing Llama-3-70B-shaped layer")
         L70 = DecodeLayerSet(torch, gbb, synth, synth.llama3_70b_proj, LAYER_COPIES_70B, 1, dev)
@@ -364,6 +378,7 @@ def main():
         del L70
         torch.cuda.empty_cache()
 
+    if "prefill" in want:
         # ---------------- prefill M = 2048 on the 70B MLP ----------------
         pre = {}
         for i in range(2):
@@ -392,6 +407,7 @@ def main():
             torch.cuda.empty_cache()
         extra["prefill_m2048_70b_mlp"] = pre
 
+    if "w44a8" in want:
         # ---------------- W4.4A8 28672 x 8192 ----------------
         W, rows8 = synth.w44a8_28672x8192()
         img, _, _ = gbb.pack_w48(W, rows8)
