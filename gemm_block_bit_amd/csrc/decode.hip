@@ -214,14 +214,13 @@ __device__ __forceinline__ uint32_t wrap(uint32_t off) {
 
 // A block column's activation fragments from the ring: lane holds tokens
 // 16 mt + r16 (rows past M repeat row M - 1), columns 32 kt + 8 g ... + 7.
-template <int MT>
+template <int MT, int RS = Ring<MT>::kSlots>
 __device__ __forceinline__ void read_x(const u32x4* ring, uint32_t xb, int M, half8 (&xa)[4][MT]) {
-  constexpr uint32_t MASK = Ring<MT>::kMask;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(16 * mt + r16, M - 1);
-    const u32x4* xr = ring + (((xb + 1024 * (m >> 2)) & MASK) >> 4);
+    const u32x4* xr = ring + (wrap<RS>(xb + 1024 * (m >> 2)) >> 4);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) xa[kt][mt] = __builtin_bit_cast(half8, xr[16 * (m & 3) + 4 * kt + g]);
   }
@@ -290,19 +289,25 @@ __device__ __forceinline__ void block_core(const u32x4* ring, uint32_t szb, uint
 
 // One block whose records start at ring byte offsets sz (scale/zero slot),
 // xb (first activation slot) and cb (first code slot).
-template <int W0, int W1, int MT, class Refill>
+template <int W0, int W1, int MT, int RS, class Refill>
 __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint32_t xb, uint32_t cb, int M,
                                           f32x4 (&acc)[4][MT], Refill&& refill) {
   half8 xa[4][MT];
-  read_x<MT>(ring, xb, M, xa);
+  read_x<MT, RS>(ring, xb, M, xa);
   f32x4 xsum[MT];
-  block_core<W0, W1, MT, true>(ring, szb, cb, xa, xsum, acc, refill);
+  block_core<W0, W1, MT, true, RS>(ring, szb, cb, xa, xsum, acc, refill);
 }
 
-template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(DecodeArgs a) {
-  constexpr int R = Ring<MT>::kSlots;
-  constexpr uint32_t MASK = Ring<MT>::kMask;
+// Ring slots per wave for M <= 8: a block's records (scale/zero, at most two
+// activation slots, at most eight code slots) fit in twelve, so the rings of
+// a four-wave workgroup take 48 KiB and three workgroups share a CU (three
+// waves per SIMD).  Llama-3-70B projections at M = 2..8: 6-10 % faster on
+// gate|up and down than 16 slots with two workgroups per CU.
+constexpr int kRing8 = 12;
+
+template <int NW, int MT, int RS = Ring<MT>::kSlots>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3))) void decode_kernel(DecodeArgs a) {
+  constexpr int R = RS;
   // wave-uniform values go through readfirstlane so the compiler keeps them
   // in scalar registers and branches on them with scalar branches
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -356,15 +361,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
         if (used + ns > R) break;
         dma4_once(szp, 4 * lane, ring_lds, sbn);
         szp += 64;
-        for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, (sbn + 1024 * (1 + xi)) & MASK);
+        for (int xi = 0; xi < nx; ++xi) dma16(xp, xoff[xi], ring_lds, wrap<R>(sbn + 1024 * (1 + xi)));
         xp += 128;
         uint32_t sc = sbn + 1024 * (1 + nx);
         for (int q = 0; q < bn; ++q) {
-          dma16_once(cp, 16 * lane, ring_lds, sc & MASK);
+          dma16_once(cp, 16 * lane, ring_lds, wrap<R>(sc));
           cp += 1024;
           sc += 1024;
         }
-        sbn = sc & MASK;
+        sbn = wrap<R>(sc);
         used += ns;
         issued += 1 + nx + bn;
         ++jn;
@@ -383,14 +388,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
       };
       const uint32_t xb = sb + 1024, cb = sb + 1024 * (1 + nx);
       switch (bj) {
-        case 1: block_mma<1, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
-        case 2: block_mma<2, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
-        case 3: block_mma<2, 1, MT>(ring, sb, xb, cb, M, acc, refill); break;
-        case 4: block_mma<4, 0, MT>(ring, sb, xb, cb, M, acc, refill); break;
-        case 6: block_mma<4, 2, MT>(ring, sb, xb, cb, M, acc, refill); break;
-        default: block_mma<4, 4, MT>(ring, sb, xb, cb, M, acc, refill); break;
+        case 1: block_mma<1, 0, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
+        case 2: block_mma<2, 0, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
+        case 3: block_mma<2, 1, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
+        case 4: block_mma<4, 0, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
+        case 6: block_mma<4, 2, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
+        default: block_mma<4, 4, MT, R>(ring, sb, xb, cb, M, acc, refill); break;
       }
-      sb = (sb + 1024 * (1 + nx + bj)) & MASK;
+      sb = wrap<R>(sb + 1024 * (1 + nx + bj));
     }
   }
   __syncthreads();
@@ -854,9 +859,9 @@ DecodePlan decode_plan(int N, int K, int M) {
     while ((nbc + 4 * k - 1) / (4 * k) > kMaxSegments) k *= 2;
     nseg = (nbc + 4 * k - 1) / (4 * k);
   } else {
-    // 4-wave workgroups resident per CU: two for M <= 16 (64 KiB of LDS
-    // rings each) and for the two-row kernel (80 KiB), one for one row at
-    // M > 16 (128 KiB).  A workgroup owns one block row, or two for M > 16 on
+    // 4-wave workgroups resident per CU: three for M <= 8 (48 KiB of LDS
+    // rings each), two for M <= 16 (64 KiB) and for the two-row kernel
+    // (80 KiB), one for one row at M > 16 (128 KiB).  A workgroup owns one block row, or two for M > 16 on
     // matrices of at least 2^26 weights (smaller ones lose more to the halved
     // workgroup count than they gain: Llama-3 sweeps at M = 20 and 32).  One
     // workgroup per row unit when that fills
@@ -865,7 +870,7 @@ DecodePlan decode_plan(int N, int K, int M) {
     // capped by the hand-off traffic (nseg * M * N * 8 bytes against
     // ~N * K / 2; twice that for M > 16, where the sweeps favour the split).
     if (M > 16 && size_t(N) * size_t(K) >= (size_t(1) << 26)) p.rows = 2;
-    const int resident = (M <= 16 || p.rows == 2 ? 2 : 1) * 256;
+    const int resident = (M <= 8 ? 3 : (M <= 16 || p.rows == 2 ? 2 : 1)) * 256;
     const int units = (nbr + p.rows - 1) / p.rows;
     if (units < resident) {
       nseg = resident / units;
@@ -904,6 +909,8 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   if (M == 1)
     hipLaunchKernelGGL((decode1_kernel<4>), grid, dim3(256), 0, s, a.bits, a.offs, a.sz, a.codes, a.x, a.nbc,
                        a.seg_cols, a.nseg, a.y, a.acc, a.facc, a.N, a.K, a.M, a.nbr);
+  else if (M <= 8)   // a block's records (1 + ceil(M / 4) + 8 slots) fit in 12 slots
+    hipLaunchKernelGGL((decode_kernel<4, 1, kRing8>), grid, dim3(256), 0, s, a);
   else if (M <= 16)
     hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
   else if (plan.rows == 1)

@@ -130,6 +130,24 @@ PREFILL_CASES = [(64, 128, 33), (192, 384, 100), (128, 1280, 257), (320, 512, 12
                  (16384, 256, 1536), (16384, 256, 1436)]
 
 
+@pytest.mark.parametrize("b", [1, 8])
+@pytest.mark.parametrize("M", [2, 5, 8, 12, 16, 17, 32])
+def test_uniform_extreme_bitwidths(b, M):
+    """Every block at 8 bits fills a ring with one block's records; every
+    block at 1 bit puts the most records in it.  An odd block-row count and
+    a matrix of 2^26 weights (two rows per workgroup for M > 16) cover every
+    decode kernel's ring."""
+    for N, K in [(64 * 9, 128 * 12), (8192, 8192)]:
+        W = small(N, K, N + b + M)
+        bits = np.full((N // 64, K // 128), b, np.uint8)
+        img = packed(W, bits)
+        x = rand_x(M, K, b + M)
+        rows = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+        y = gbb.gemm_mixed_w(img, N, K, to_dev(x)).cpu().numpy()
+        ref = bq.reference_rows(x, W, bits, rows)
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL, (N, K)
+
+
 @pytest.mark.parametrize("N,K,M", PREFILL_CASES)
 def test_prefill_parity(N, K, M):
     W = small(N, K, N * 7 + K)
