@@ -298,12 +298,14 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint3
   block_core<W0, W1, MT, true, RS>(ring, szb, cb, xa, xsum, acc, refill);
 }
 
-// Ring slots per wave for M <= 8: a block's records (scale/zero, at most two
-// activation slots, at most eight code slots) fit in twelve, so the rings of
-// a four-wave workgroup take 48 KiB and three workgroups share a CU (three
-// waves per SIMD).  Llama-3-70B projections at M = 2..8: 6-10 % faster on
-// gate|up and down than 16 slots with two workgroups per CU.
+// Ring slots per wave for 2 <= M <= 16: a block's records (scale/zero,
+// ceil(M / 4) activation slots, at most eight code slots) fit in twelve for
+// M <= 8 and in thirteen for M <= 16, so the rings of a four-wave workgroup
+// take 48 or 52 KiB and three workgroups share a CU (three waves per SIMD).
+// Llama-3-70B projections: 6-11 % faster on gate|up and down than 16 slots
+// with two workgroups per CU; the 8B shapes are within a few per cent.
 constexpr int kRing8 = 12;
+constexpr int kRing16 = 13;
 
 template <int NW, int MT, int RS = Ring<MT>::kSlots>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3))) void decode_kernel(DecodeArgs a) {
@@ -859,9 +861,9 @@ DecodePlan decode_plan(int N, int K, int M) {
     while ((nbc + 4 * k - 1) / (4 * k) > kMaxSegments) k *= 2;
     nseg = (nbc + 4 * k - 1) / (4 * k);
   } else {
-    // 4-wave workgroups resident per CU: three for M <= 8 (48 KiB of LDS
-    // rings each), two for M <= 16 (64 KiB) and for the two-row kernel
-    // (80 KiB), one for one row at M > 16 (128 KiB).  A workgroup owns one block row, or two for M > 16 on
+    // 4-wave workgroups resident per CU: three for M <= 16 (48 or 52 KiB of
+    // LDS rings each), two for the two-row kernel (80 KiB), one for one row
+    // at M > 16 (128 KiB).  A workgroup owns one block row, or two for M > 16 on
     // matrices of at least 2^26 weights (smaller ones lose more to the halved
     // workgroup count than they gain: Llama-3 sweeps at M = 20 and 32).  One
     // workgroup per row unit when that fills
@@ -870,7 +872,7 @@ DecodePlan decode_plan(int N, int K, int M) {
     // capped by the hand-off traffic (nseg * M * N * 8 bytes against
     // ~N * K / 2; twice that for M > 16, where the sweeps favour the split).
     if (M > 16 && size_t(N) * size_t(K) >= (size_t(1) << 26)) p.rows = 2;
-    const int resident = (M <= 8 ? 3 : (M <= 16 || p.rows == 2 ? 2 : 1)) * 256;
+    const int resident = (M <= 16 ? 3 : (p.rows == 2 ? 2 : 1)) * 256;
     const int units = (nbr + p.rows - 1) / p.rows;
     if (units < resident) {
       nseg = resident / units;
@@ -911,8 +913,8 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
                        a.seg_cols, a.nseg, a.y, a.acc, a.facc, a.N, a.K, a.M, a.nbr);
   else if (M <= 8)   // a block's records (1 + ceil(M / 4) + 8 slots) fit in 12 slots
     hipLaunchKernelGGL((decode_kernel<4, 1, kRing8>), grid, dim3(256), 0, s, a);
-  else if (M <= 16)
-    hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(256), 0, s, a);
+  else if (M <= 16)   // 1 + 4 + 8 slots fit in 13
+    hipLaunchKernelGGL((decode_kernel<4, 1, kRing16>), grid, dim3(256), 0, s, a);
   else if (plan.rows == 1)
     hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
   else
