@@ -268,6 +268,21 @@ def main():
     step_pct = replay_percentiles(torch, g8, args.steps)
     del g8
 
+    # the same step as one library graph (gbb_graph_create over the 32 calls)
+    lg = gbb.Graph([(L8.images[r][i], N, K, L8.x[i], L8.y[i]) for r, i, N, K in L8.launches()])
+    for _ in range(args.warmup):
+        lg.launch()
+    torch.cuda.synchronize()
+    le0, le1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    le0.record()
+    for _ in range(args.steps):
+        lg.launch()
+    le1.record()
+    torch.cuda.synchronize()
+    lib_graph_us = le0.elapsed_time(le1) * 1e3 / args.steps
+    lg.close()
+    log(f"the same step as one library graph: {lib_graph_us:.1f} us")
+
     # per-launch events over the same timed work (eager launches, one stream)
     ng = len(L8.shapes)
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ng)] for _ in range(L8.copies)]
@@ -300,6 +315,7 @@ def main():
     extra = {"per_launch_group_m1_eager_events": per_proj,
              "kernel_sum_us_per_step": round(float(durs.sum(axis=(1, 2)).mean()), 1),
              "graph_step_us": round(sec * 1e6, 1), "graph_step_us_p10_p50_p90": step_pct,
+             "library_graph_step_us": round(lib_graph_us, 1),
              "host_wall_us_per_step": round(wall * 1e6, 1)}
 
     if "llama3_8b_m8" in want:

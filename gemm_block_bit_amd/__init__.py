@@ -8,6 +8,7 @@ no CPU fallback -- if the library is missing every call raises.
 """
 from .binding import (  # noqa: F401
     GbbError,
+    Graph,
     allocate_bits,
     channel_order,
     check_image,

@@ -42,6 +42,9 @@ _SIGS = {
     "gbb_gemm_mixed_w_workspace": (_sz, [_i, _i, _i]),
     "gbb_gemm_mixed_w": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_gemm_mixed_w_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
+    "gbb_graph_create": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "gbb_graph_launch": (_i, [_vp, _vp]),
+    "gbb_graph_destroy": (_i, [_vp]),
     "gbb_unpack_codes": (_i, [_vp, _i, _i, _vp, _vp]),
     "gbb_dequant": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "gbb_w48_packed_bytes": (_sz, [_i, _i, _i]),
@@ -245,6 +248,55 @@ def gemm_mixed_w_path(image, N: int, K: int, x, path: int, out=None, workspace=N
 def gemm_mixed_w(image, N: int, K: int, x, out=None, workspace=None):
     """y = x . dequant(W)^T (fp16 [M][N]) on torch's current stream."""
     return gemm_mixed_w_path(image, N, K, x, 0, out, workspace)
+
+
+class Graph:
+    """gemm_mixed_w calls captured into one HIP graph (gbb_graph_create) and
+    replayed by launch().  calls: (image, N, K, x, y) with every x [M][K] and
+    y [M][N] on one device and one M.  The tensors are kept referenced here
+    and must keep their storage and shapes; the inputs are read and the
+    outputs written at each launch."""
+
+    def __init__(self, calls, workspace=None):
+        torch = _torch()
+        if not calls:
+            raise ValueError("no calls")
+        M = calls[0][3].shape[0]
+        for (img, N, K, x, y) in calls:
+            if x.dim() != 2 or tuple(x.shape) != (M, K) or tuple(y.shape) != (M, N):
+                raise ValueError(f"x must be [{M}][{K}] and y [{M}][{N}]")
+        need = max(gemm_mixed_w_workspace(N, K, M) for (_, N, K, _, _) in calls)
+        dev = calls[0][3].device
+        self._ws = workspace if workspace is not None else torch.zeros(max(need, 256), dtype=torch.uint8,
+                                                                       device=dev)
+        n = len(calls)
+        images = (ctypes.c_void_p * n)(*[_dev_ptr(c[0], torch.uint8, "image") for c in calls])
+        Ns = (ctypes.c_int * n)(*[c[1] for c in calls])
+        Ks = (ctypes.c_int * n)(*[c[2] for c in calls])
+        xs = (ctypes.c_void_p * n)(*[_dev_ptr(c[3], torch.float16, "x") for c in calls])
+        ys = (ctypes.c_void_p * n)(*[_dev_ptr(c[4], torch.float16, "y") for c in calls])
+        out = ctypes.c_void_p()
+        self._g = None
+        _check(lib().gbb_graph_create(n, images, Ns, Ks, xs, ys, M, self._ws.data_ptr(), self._ws.numel(),
+                                      ctypes.byref(out)))
+        self._g = out
+        self._calls = list(calls)
+
+    def launch(self):
+        """Replay on torch's current stream of the calls' device."""
+        torch = _torch()
+        _check(lib().gbb_graph_launch(self._g, torch.cuda.current_stream(self._ws.device).cuda_stream))
+
+    def close(self):
+        if self._g is not None:
+            g, self._g = self._g, None
+            _check(lib().gbb_graph_destroy(g))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def unpack_codes(image, N: int, K: int):

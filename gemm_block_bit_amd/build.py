@@ -27,7 +27,8 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + COMMON
 CXX_FLAGS = ["-O2", "-Wall", "-Wextra", "-fno-fast-math"] + COMMON
 
-HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip"]
+# graph.cpp is host code on the HIP runtime (stream capture), so hipcc builds it too
+HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip", "graph.cpp"]
 # per-source extra flags: the decode kernel reads its MFMA results with VALU
 # code right away, so it keeps them in VGPRs rather than accumulation
 # registers; its single-token kernel takes its arguments preloaded into

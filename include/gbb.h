@@ -150,6 +150,35 @@ gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
                             uint16_t* y, int M, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/* Whole-layer execution (ScaleBITS explainer page, section 3.2: an execution
+ * plan generated for a given bit configuration; MixLLM page, section 3.3:
+ * the kernels of a step replayed from a captured graph).  Captures n
+ * gbb_gemm_mixed_w calls, in order, into one HIP graph: call i multiplies
+ * x[i] (device fp16 [M][K[i]]) by images[i] (device, N[i] x K[i]) into y[i]
+ * (device fp16 [M][N[i]]).  Every pointer is recorded as is and must stay
+ * valid, with the same shapes, for the graph's life; each call is checked as
+ * gbb_gemm_mixed_w checks it, and the first failing call's status is
+ * returned.  The calls share one workspace (device, zero-filled once before
+ * the first launch, ws_bytes >= the largest gbb_gemm_mixed_w_workspace of
+ * the calls); they run one after the other and leave it zero-filled, so
+ * launches of the graph on one stream may follow each other, but launches
+ * that may run at the same time need graphs with separate workspaces.  Host
+ * call; captures on a stream of its own (default priority), allocates only
+ * the graph.  On success *out owns the graph.
+ * Errors: GBB_E_ARG (NULL, n < 1, M < 1), those of gbb_gemm_mixed_w,
+ * GBB_E_DEVICE (capture or instantiation failed). */
+typedef struct gbb_graph gbb_graph;
+gbb_status gbb_graph_create(int n, const void* const* images, const int* N, const int* K,
+                            const uint16_t* const* x, uint16_t* const* y, int M,
+                            void* workspace, size_t ws_bytes, gbb_graph** out);
+
+/* Launch a captured graph on `stream` (asynchronous). */
+gbb_status gbb_graph_launch(const gbb_graph* g, void* stream);
+
+/* Free a graph (NULL is allowed).  The caller makes sure no launch of it is
+ * still running. */
+gbb_status gbb_graph_destroy(gbb_graph* g);
+
 /* Same as gbb_gemm_mixed_w with the kernel chosen by `path`: 0 = automatic,
  * 1 = decode kernel (requires M <= 32), 2 = prefill kernel.  For tests. */
 gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t* x,

@@ -298,6 +298,42 @@ def test_graph_replay_matches_eager():
         del junk
 
 
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_library_graph_matches_eager(M):
+    """Four calls captured into one library graph (a layer's launch groups in
+    miniature, with split-K decode and, at M = 64, the prefill kernel)
+    replayed several times, with eager work and synchronizations between the
+    replays: every replay equals the eager calls bit for bit."""
+    shapes = [(384, 1024), (256, 1024), (1792, 1024), (256, 3584)]
+    calls, eager = [], []
+    for i, (N, K) in enumerate(shapes):
+        W = small(N, K, 40 + i)
+        bits = synth.random_bitmap(N, K, ALLOWED, 40 + i)
+        img = packed(W, bits)
+        x = to_dev(rand_x(M, K, 50 + i))
+        y = torch.empty((M, N), dtype=torch.float16, device=dev())
+        calls.append((img, N, K, x, y))
+        eager.append(gbb.gemm_mixed_w(img, N, K, x).clone())
+    g = gbb.Graph(calls)
+    try:
+        for rep in range(3):
+            for (_, _, _, _, y) in calls:
+                y.fill_(float("nan"))
+            g.launch()
+            torch.cuda.synchronize()
+            for (_, _, _, _, y), ref in zip(calls, eager):
+                assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+            # eager work between replays, on other buffers
+            gbb.gemm_mixed_w(calls[0][0], calls[0][1], calls[0][2], calls[0][3])
+            torch.cuda.synchronize()
+    finally:
+        g.close()
+    # a call the library rejects (K not a multiple of 128) fails the capture
+    with pytest.raises(gbb.GbbError):
+        gbb.Graph([(calls[0][0], 384, 1000, torch.empty((M, 1000), dtype=torch.float16, device=dev()),
+                    calls[0][4])])
+
+
 def test_auto_path_and_empty_batch():
     N, K = 128, 256
     W = small(N, K, 5)

@@ -199,3 +199,16 @@ def test_pack_w48_errors():
     expect_status(-2, gbb.pack_w48, W, np.array([5, 2], np.int32))
     expect_status(-2, gbb.pack_w48, W, np.array([64], np.int32))
     expect_status(-2, gbb.pack_w48, small(64, 200, 1), np.array([1], np.int32))
+
+
+def test_graph_create_argument_errors():
+    """gbb_graph_create rejects bad arguments before touching the device."""
+    import ctypes
+    L = gbb.lib()
+    out = ctypes.c_void_p(1)
+    assert L.gbb_graph_create(0, None, None, None, None, None, 1, None, 0, ctypes.byref(out)) == -1
+    assert out.value is None
+    assert L.gbb_graph_create(1, None, None, None, None, None, 1, None, 0, ctypes.byref(out)) == -1
+    assert L.gbb_graph_create(1, None, None, None, None, None, 1, None, 0, None) == -1
+    assert L.gbb_graph_launch(None, None) == -1
+    assert L.gbb_graph_destroy(None) == 0
