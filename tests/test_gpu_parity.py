@@ -486,6 +486,8 @@ def test_w48_group_acc_bit_exact(N, K, M, frac):
                                            (300, 1024, 130, None, 0.1), (300, 1024, 77, 128, 0.1),
                                            (1000, 4096, 1, None, 0.1), (256, 1024, 64, None, 0.1),
                                            (128, 640, 17, None, 0.3),
+                                           # MixLLM's 20 % and 50 % 8-bit row fractions
+                                           (320, 1024, 48, None, 0.2), (192, 512, 130, 128, 0.5), (192, 512, 24, None, 0.5),
                                            # batches above 64 with no 8-bit rows / only 8-bit rows
                                            (64, 256, 100, None, 0.0), (80, 256, 200, 128, 1.0)])
 def test_w48_parity(N, K, M, ga, frac):
