@@ -255,6 +255,10 @@ def main():
         log("calibration copy: 5 x (read 268435456 B, write 268435456 B)")
         del src, dst
 
+    device_info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "memory_GiB": round(props.total_memory / 2**30, 1)}
+
     # ---------------- headline: Llama-3-8B layers, decode M = 1 ----------------
     log("packing Llama-3-8B-shaped layer (qkv, o, gate_up, down)")
     L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
@@ -317,6 +321,25 @@ def main():
              "graph_step_us": round(sec * 1e6, 1), "graph_step_us_p10_p50_p90": step_pct,
              "library_graph_step_us": round(lib_graph_us, 1),
              "host_wall_us_per_step": round(wall * 1e6, 1)}
+
+    extra["device"] = device_info
+    if not args.quick:
+        # context: a plain device-to-device copy of 1 GiB (read + write bytes)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        extra["copy_1GiB_GBps"] = round(2 * 10 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
+        log(f"device copy of 1 GiB: {extra['copy_1GiB_GBps']} GB/s (read + write)")
+        del src, dst
+        torch.cuda.empty_cache()
 
     if "llama3_8b_m8" in want:
         # ---------------- same layers at M = 8 ----------------
@@ -452,6 +475,7 @@ def main():
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
         cpu = cpu_baseline(gbb, synth)
+        extra["cpu_baseline_one_thread_o_proj_GBps"] = cpu_baseline_one_thread(gbb, synth)
 
     out = {
         "metric": "fused dequant-GEMM: weight GB/s (%HBM peak) at M=1; TFLOP/s (%MFMA) at M=2048",
@@ -509,6 +533,27 @@ def cpu_baseline(gbb, synth):
     return {"value": round(total_bytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one layer copy (7 projections, {total_bytes / 1e6:.1f} MB packed) at M=1: oracle unpack + "
                       f"fp32 dequant + fp64 GEMV, {t:.1f} s"}
+
+
+def cpu_baseline_one_thread(gbb, synth):
+    """The same oracle on one thread (BLAS limited to one), over the o
+    projection only, for context next to the multi-thread figure."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import blockquant as bq
+    from oracle import image as oimg
+
+    p, W, bits = synth.llama3_8b_proj(3)
+    img, _, _ = gbb.pack_blocks(W, bits)
+    del W
+    x = np.random.default_rng(7).standard_normal((1, p.K)).astype(np.float16)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        d = oimg.read_block_image(img)
+        w = bq.dequant_fp32(d["q"], d["s16"], d["z16"])
+        bq.gemm_fp64(x, w)
+        t = time.perf_counter() - t0
+    return round(weight_bytes(bits) / t / 1e9, 3)
 
 
 if __name__ == "__main__":
