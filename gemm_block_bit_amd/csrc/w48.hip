@@ -445,9 +445,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------------------
 template <int TM>   // token tiles: M <= 16 TM
 struct StreamCfg {
-  // The kernel is bound by how many bytes each CU keeps in flight (stages - 1
-  // groups per workgroup, two workgroups per CU): five stages still fit two
-  // workgroups in the LDS for M <= 32, four for M <= 64.
+  // Stages - 1 groups per workgroup are in flight, two workgroups per CU:
+  // five stages still fit two workgroups in the LDS for M <= 32, four for
+  // M <= 64.  (Deeper pipelines for the 4-bit rows, whose stages are
+  // smaller, measured the same: the loads themselves bound the kernel.)
   static constexpr int kStages = TM <= 2 ? 5 : 4;
   static constexpr int NA = (2 * TM + 3) / 4;           // activation loads per wave per group
   static constexpr int kA = 4 * NA * 1024;              // activation fragments per stage
