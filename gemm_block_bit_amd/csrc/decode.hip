@@ -23,9 +23,13 @@
 //    s (2^(24 - o) C - z X) = s sum_k x_k (q_k - z) to fp32 accumulators.
 //  * Each wave streams its blocks through LDS rings filled by global->LDS
 //    loads (global_load_lds_dword[x4]), so data in flight costs no
-//    registers.  For M > 1 one ring of 1 KiB slots (16, or 32 for M > 16)
-//    holds per block a scale/zero slot, ceil(M / 4) activation slots and the
-//    b code slots.  A single token has its own kernel with an 8-slot code ring
+//    registers.  For M > 1 one ring of 1 KiB slots (12 for M <= 8, 13 for
+//    M <= 16, 32 above) holds per block a scale/zero slot, ceil(M / 4)
+//    activation slots and the b code slots; the two-row kernel for
+//    17 <= M <= 32 keeps the activations in a buffer of their own beside a
+//    12-slot ring of scale/zero and code records.  The multi-token epilogue
+//    folds 2^(24 - o) into s and z once per row tile (exact).  A single
+//    token has its own kernel with an 8-slot code ring
 //    and a 4-entry ring of 512-byte scale/zero + activation records: 10 KiB
 //    per wave, 16 waves per CU.  Blocks are issued ahead while they fit; the
 //    wait for a block is a vmcnt bound, and a block's slots are refilled as
@@ -92,8 +96,9 @@ __device__ __forceinline__ void splitk_publish(const DecodeArgs& a, size_t idx, 
   __hip_atomic_store(a.acc + idx, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Ring slots per wave (a power of two): a block takes 1 + nx + b slots
-// (nx = ceil(M / 4) activation slots of four tokens each).
+// Default ring slots per wave (a power of two): a block takes 1 + nx + b
+// slots (nx = ceil(M / 4) activation slots of four tokens each).  The
+// launches for M <= 16 pass smaller rings (kRing8, kRing16) instead.
 template <int MT>
 struct Ring {
   static constexpr int kSlots = MT == 1 ? 16 : 32;
