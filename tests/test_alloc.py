@@ -220,3 +220,16 @@ def test_library_allocation_errors():
         gbb.allocate_bits(Wn, 3.0)
     with pytest.raises(gbb.GbbError):
         gbb.channel_order(Wn)
+
+
+def test_library_allocation_matches_oracle_heavy_rows():
+    """A 1024 x 4096 weight with heavy-tailed rows (512 blocks), reordered
+    by the channel order first, at two budgets."""
+    import synth
+    W = synth.weight_heavy_rows(1024, 4096, synth.WL_LLAMA3_8B, 2)
+    r, c = gbb.channel_order(W)
+    rr, cc = alloc.channel_order(W)
+    assert np.array_equal(r, rr) and np.array_equal(c, cc)
+    Wr = np.ascontiguousarray(W[r][:, c])
+    for target in (2.5, 3.5):
+        assert np.array_equal(gbb.allocate_bits(Wr, target), alloc.allocate(Wr, target))

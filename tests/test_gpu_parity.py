@@ -334,6 +334,25 @@ def test_library_graph_matches_eager(M):
                     calls[0][4])])
 
 
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_maximum_rows(M):
+    """N = 2^20 rows (the largest N the block entry points take) on a single
+    block column, through each kernel family; one block row more is an
+    error."""
+    N, K = 1 << 20, 128
+    g = np.random.default_rng(60)
+    W = (0.02 * g.standard_normal((N, K), dtype=np.float32)).astype(np.float16)
+    bits = synth.random_bitmap(N, K, ALLOWED, 60)
+    img = packed(W, bits)
+    x = rand_x(M, K, 61)
+    y = gbb.gemm_mixed_w(img, N, K, to_dev(x)).cpu().numpy()
+    rows = sample_rows(N, 62, 64)
+    ref = bq.reference_rows(x, W, bits, rows)
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+    with pytest.raises(gbb.GbbError):
+        gbb.gemm_mixed_w(img, N + 64, K, to_dev(x))
+
+
 def test_auto_path_and_empty_batch():
     N, K = 128, 256
     W = small(N, K, 5)
