@@ -233,7 +233,7 @@ def main():
         want = set()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the fused dequant-GEMM path has no multi-GPU component here "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "(the path would shard by output rows or by K; that is not built here); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -17,7 +17,7 @@ Sources (cited by page title and section):
 * Same page, section 4.2: bitwidths {1,2,3,4,6,8}; start from 3 bits and
   lower the budget from there.
 
-Readings where the pages are silent or garbled (all listed in the design doc):
+Readings where the pages are silent or garbled:
 
 * The pages' sensitivity |grad L(w_Q) . dw_i| needs a model and calibration
   data.  The proxy objective of block i at bitwidth b is S_i * e_i(b): S_i

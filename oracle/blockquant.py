@@ -10,7 +10,7 @@ Sources (cited by page title and section):
   set {1,2,3,4,6,8}; section 3.2 the fused dequantize-multiply kernel.
 * SBVR page, section 4.1: groups of 128 run along the GEMV inner dimension.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 * a block is 64 output rows x 128 input columns, so each (row, 128-column
   group) lies in one block and has one bitwidth;
 * s and z are chosen by min/max: s = (max - min) / (2^b - 1) rounded to fp16,

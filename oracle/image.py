@@ -1,12 +1,12 @@
 """Independent readers for the two packed weight images.
 
-These follow the byte-level format description ("Packed image
-formats") and are written without reference to the library's packer, so a
-mistake in either shows up as a mismatch.  The format itself is this build's
-choice: the pages say only that each 64x128 block is stored with its own
-bitwidth next to its metadata (ScaleBITS explainer, section 3.2, block-wise
-memory layout) and that MixLLM pre-packs its weights so nothing is permuted at
-run time (MixLLM page, section 3.3).
+These follow the byte-level format described below and are written without
+reference to the library's packer, so a mistake in either shows up as a
+mismatch.  The format itself is the library's own choice: the pages say only
+that each 64x128 block is stored with its own bitwidth next to its metadata
+(ScaleBITS explainer, section 3.2, block-wise memory layout) and that MixLLM
+pre-packs its weights so nothing is permuted at run time (MixLLM page,
+section 3.3).
 
 Block image ("GBB1")
 --------------------

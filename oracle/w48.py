@@ -11,7 +11,7 @@ Sources (MixLLM page):
 * section 3.3: two-step dequantization -- per group, the integer product
   A_q (W_q - z) first, then the two scales s_a * s_w.
 
-Readings (the design doc lists them): the symmetric range is +-(2^(b-1) - 1), i.e.
+Readings where the pages are silent: the symmetric range is +-(2^(b-1) - 1), i.e.
 +-127, with s = max|v| / 127 rounded to fp16 (1 if the group is all zero);
 activations are quantized per token (the benchmark layer) or per 128-group
 (the page's own choice); the activation decisions are taken in fp32, the

@@ -255,7 +255,9 @@ def test_packed_size_identity():
     assert [(b, int((bits == b).sum())) for b in (2, 3, 4)] == [(2, 512), (3, 819), (4, 717)]
     codes = sum(64 * 128 * int(b) // 8 for b in bits.reshape(-1))
     assert codes == 6_501_376
-    assert image.block_image_size(bits) == 7_036_416   # computed by hand, see the design doc
+    # by hand: 256 (header, padded) + 2048 (bitwidths) + 8448 (2049 offsets, padded)
+    # + 524,288 (scale/zero records) + 6,501,376 (codes)
+    assert image.block_image_size(bits) == 7_036_416
 
 
 def _slow_block_image(q, s16, z16, bits):

@@ -212,3 +212,19 @@ def test_graph_create_argument_errors():
     assert L.gbb_graph_create(1, None, None, None, None, None, 1, None, 0, None) == -1
     assert L.gbb_graph_launch(None, None) == -1
     assert L.gbb_graph_destroy(None) == 0
+
+
+def test_graph_wrapper_rejects_mismatched_shapes():
+    """gbb.Graph checks x [M][K] and y [M][N] before calling the library."""
+    import pytest
+
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 256), dtype=torch.float16)
+    y = torch.zeros((4, 64), dtype=torch.float16)
+    img = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        gbb.Graph([(img, 64, 128, x, y)])            # x has K = 256, not 128
+    with pytest.raises(ValueError):
+        gbb.Graph([(img, 128, 256, x, y)])           # y has N = 64, not 128
+    with pytest.raises(ValueError):
+        gbb.Graph([])
