@@ -353,6 +353,34 @@ def test_maximum_rows(M):
         gbb.gemm_mixed_w(img, N + 64, K, to_dev(x))
 
 
+def _random_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        N = 64 * int(g.integers(1, 41))
+        K = 128 * int(g.integers(1, 41))
+        M = int(g.choice([1, 2, 3, 5, 8, 13, 16, 17, 24, 31, 32, 33, 47, 64, 100, 129, 200]))
+        cases.append((N, K, M, int(g.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,M,seed", _random_cases(40, 2024))
+def test_random_shapes(N, K, M, seed):
+    """Seeded random shapes (ragged M, odd block-row counts, short and long
+    K) and random bitmaps over every width, through whichever kernel the
+    library picks, against the oracle on sampled rows."""
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((N, K))).astype(np.float16)
+    W[g.random((N, K)) < 0.005] *= np.float16(10)
+    bits = synth.random_bitmap(N, K, ALLOWED, seed % 1000)
+    img = packed(W, bits)
+    x = g.standard_normal((M, K)).astype(np.float16)
+    y = gbb.gemm_mixed_w(img, N, K, to_dev(x)).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, min(N, 48), replace=False)]))
+    ref = bq.reference_rows(x, W, bits, rows)
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
 def test_auto_path_and_empty_batch():
     N, K = 128, 256
     W = small(N, K, 5)
