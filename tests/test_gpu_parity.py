@@ -555,6 +555,34 @@ def w44a8_image():
     return W, rows8, to_dev(img)
 
 
+def _random_w48_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        N = int(g.integers(1, 400))
+        K = 128 * int(g.integers(1, 24))
+        M = int(g.choice([1, 2, 7, 16, 17, 31, 32, 33, 64, 65, 130, 257]))
+        frac = float(g.choice([0.0, 0.05, 0.1, 0.2, 0.5, 1.0]))
+        ga = None if g.random() < 0.6 else 128
+        cases.append((N, K, M, frac, ga, int(g.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("N,K,M,frac,ga,seed", _random_w48_cases(20, 77))
+def test_w48_random_shapes(N, K, M, frac, ga, seed):
+    """Seeded random W4.4A8 shapes (any N, ragged M, every kernel), 8-bit row
+    fractions from 0 to 1 and both activation-scale granularities."""
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((N, K))).astype(np.float16)
+    rows8 = synth.salient_rows_by_l2(W, frac) if frac < 1 else np.arange(N, dtype=np.int32)
+    img, _, _ = gbb.pack_w48(W, rows8)
+    x = g.standard_normal((M, K)).astype(np.float16)
+    xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+    y = gbb.gemm_w48a8(to_dev(img), N, K, rows8.size, xq, xs, ga)
+    ref = ow48.reference(x, W, rows8, act_group=ga)
+    assert rel_err(y, ref) <= TOL
+
+
 @pytest.mark.parametrize("M", [32, 512, 4096])
 def test_w44a8_28672x8192(M):
     W, rows8, img = w44a8_image()
