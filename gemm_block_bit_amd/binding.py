@@ -235,7 +235,7 @@ def gemm_mixed_w_path(image, N: int, K: int, x, path: int, out=None, workspace=N
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M][{K}]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
-    need = gemm_mixed_w_workspace(N, K, M) if (path == 1 or (path == 0 and M <= 32)) else 0
+    need = gemm_mixed_w_workspace(N, K, M) if path != 2 else 0   # 0 when the call needs none
     ws = workspace if workspace is not None else _workspace(x.device, need)
     _check(lib().gbb_gemm_mixed_w_path(
         _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),

@@ -71,13 +71,33 @@ W48ImageView w48_view(const void* image, int N, int K, int n8) {
   return v;
 }
 
+// For 32 < M the prefill kernel gives each CU one tile of 128 tokens x 512
+// rows over the whole of K and does not split K, so few tiles leave most CUs
+// idle (the Llama-3-70B down projection, 8192 x 28672, has 16 tiles at
+// M <= 128: ~0.8 ms whatever M is).  When ceil(M / 32) chunks of the prefill
+// grid still fit in one wave of CUs, the decode kernels run the batch in
+// 32-token chunks instead; each chunk rereads the weights, but at 48 us per
+// chunk on that shape that is far cheaper.
+bool decode_in_chunks(int N, int M) {
+  if (M <= 32) return false;
+  return size_t((M + 31) / 32) * size_t(prefill_tiles(N, M)) <= size_t(device_compute_units());
+}
+
+// Workspace of the decode launches of a batch of M tokens run as 32-token
+// chunks: the largest over the full chunks and the last, shorter one.
+size_t chunked_workspace(int N, int K, int M) {
+  size_t need = decode_plan(N, K, 32).ws_bytes;
+  if (M % 32) need = need > decode_plan(N, K, M % 32).ws_bytes ? need : decode_plan(N, K, M % 32).ws_bytes;
+  return need;
+}
+
 }  // namespace
 
 extern "C" int gbb_version(void) { return 100; }
 
 extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
   if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % kGroup) return 0;
-  if (M > 32) return 0;
+  if (M > 32) return decode_in_chunks(N, M) ? chunked_workspace(N, K, M) : 0;
   const DecodePlan p = decode_plan(N, K, M);
   return p.ws_bytes;
 }
@@ -95,6 +115,22 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
   const char* yb = reinterpret_cast<const char*>(y);
   if (xb < yb + size_t(M) * N * 2 && yb < xb + size_t(M) * K * 2) return fail(GBB_E_ARG, "x and y overlap");
   const BlockImageView v = block_view(image, N, K);
+  if (path == 0 && decode_in_chunks(N, M)) {
+    const size_t need = chunked_workspace(N, K, M);
+    if (need) {
+      if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
+      if (ws_bytes < need) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+      if (!aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
+    }
+    for (int m0 = 0; m0 < M; m0 += 32) {
+      const int mc = M - m0 < 32 ? M - m0 : 32;
+      const gbb_status st = device_status(launch_decode(v, x + size_t(m0) * K, y + size_t(m0) * N, mc, workspace,
+                                                        decode_plan(N, K, mc), stream),
+                                          "decode launch");
+      if (st != GBB_OK) return st;
+    }
+    return GBB_OK;
+  }
   const bool decode = path == 1 || (path == 0 && M <= 32);
   if (decode) {
     const DecodePlan p = decode_plan(N, K, M);

@@ -40,6 +40,10 @@ DecodePlan decode_plan(int N, int K, int M);
 int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M,
                   void* workspace, const DecodePlan& plan, void* stream);
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream);
+// Workgroup tiles of the prefill kernel for N rows and M tokens, and the
+// current device's compute units (looked up once per device).
+int prefill_tiles(int N, int M);
+int device_compute_units();
 int launch_unpack(const BlockImageView& im, uint8_t* q, float* w32, uint16_t* w16, void* stream);
 
 struct W48ImageView {

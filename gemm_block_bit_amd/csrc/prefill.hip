@@ -275,8 +275,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int gm = min(kGroupM, a.tiles_m - first_m);
   const int tm = first_m + (t % gsize) % gm;
   const int tn = (t % gsize) / gm;
-  if (half < 0) {
+  if (half < 0 && a.M > kBM / 2) {
     prefill_tile<kMT>(a, tm * kBM, tn, xs, stage);
+  } else if (half < 0) {   // at most 64 tokens: the tile's first half holds them all
+    prefill_tile<kMT / 2>(a, tm * kBM, tn, xs, stage);
   } else {
     const int m0 = tm * kBM + half * (kBM / 2);
     if (m0 >= a.M) return;
@@ -298,6 +300,10 @@ int compute_units() {
 }
 
 }  // namespace
+
+int prefill_tiles(int N, int M) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+int device_compute_units() { return compute_units(); }
 
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream) {
   PrefillArgs a;

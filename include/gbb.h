@@ -131,9 +131,10 @@ gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 
 /* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M); may be 0 (it is
  * M * N * 12 when K is split across workgroups: per output element an int64
- * fixed-point and an fp32 accumulator).  The workspace must be zero-filled
- * once before its first use; every call leaves it zero-filled again.  Calls
- * that run at the same time need separate workspaces. */
+ * fixed-point and an fp32 accumulator; for batches run as 32-token chunks,
+ * that of the largest chunk).  The workspace must be zero-filled once before
+ * its first use; every call leaves it zero-filled again.  Calls that run at
+ * the same time need separate workspaces. */
 size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
 
 /* y = x . dequant(W)^T over a packed block image (ScaleBITS explainer page,
@@ -142,8 +143,12 @@ size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
  *   image  device copy of gbb_pack_blocks' output for this N, K.
  *   x      device fp16 [M][K];  y device fp16 [M][N] (fp32 accumulation,
  *          round-to-nearest-even at the end).
- *   M >= 1.  M <= 32 runs the decode kernel (weights streamed once, matrix
- *   cores for the dot products); larger M runs the tiled prefill kernel.
+ *   M >= 1.  M <= 32 runs the decode kernels (weights streamed once, matrix
+ *   cores for the dot products).  Larger M runs the tiled prefill kernel,
+ *   unless its grid of 128-token x 512-row tiles, ceil(M / 32) times over,
+ *   still fits in one wave of the device's compute units: then the decode
+ *   kernels run the batch in 32-token chunks, one launch each, which keeps
+ *   every CU busy where the prefill kernel would leave most of them idle.
  *   workspace/ws_bytes  device memory of gbb_gemm_mixed_w_workspace(N, K, M)
  *          bytes (NULL allowed when that is 0). */
 gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,

@@ -265,17 +265,20 @@ def test_split_k_nan_then_clean(M):
 
 
 def test_graph_replay_matches_eager():
-    """The decode and prefill launches captured in a HIP graph: every replay,
-    with eager work in between, reproduces the eager result bit for bit."""
+    """The decode launches (M = 1, 8, and 64 as two 32-token chunks) and a
+    prefill launch (M = 1024) captured in a HIP graph: every replay, with
+    eager work in between, reproduces the eager result bit for bit."""
     N, K = 1024, 4096
     W = small(N, K, 88)
     bits = synth.random_bitmap(N, K, ALLOWED, 88)
     img = packed(W, bits)
-    xs = [to_dev(rand_x(M, K, 88 + M)) for M in (1, 8, 64)]
+    Ms = (1, 8, 64, 1024)
+    xs = [to_dev(rand_x(M, K, 88 + M)) for M in Ms]
     eager = [gbb.gemm_mixed_w(img, N, K, x) for x in xs]
     torch.cuda.synchronize()
     outs = [torch.empty_like(e) for e in eager]
-    ws = torch.zeros(gbb.gemm_mixed_w_workspace(N, K, 8) + 256, dtype=torch.uint8, device=dev())
+    need = max(gbb.gemm_mixed_w_workspace(N, K, M) for M in Ms)
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device=dev())
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -379,6 +382,29 @@ def test_random_shapes(N, K, M, seed):
     rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, min(N, 48), replace=False)]))
     ref = bq.reference_rows(x, W, bits, rows)
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+@pytest.mark.parametrize("M", [33, 64, 100])
+def test_batches_as_decode_chunks(M):
+    """Batches just above 32 tokens on a matrix whose prefill grid would
+    leave most CUs idle run as 32-token decode chunks: a workspace is then
+    required (and checked), and the result matches the oracle."""
+    N, K = 4096, 4096
+    W = small(N, K, 90 + M)
+    bits = synth.random_bitmap(N, K, ALLOWED, 90 + M)
+    img = packed(W, bits)
+    need = gbb.gemm_mixed_w_workspace(N, K, M)
+    assert need > 0
+    x = rand_x(M, K, 91 + M)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    y = gbb.gemm_mixed_w(img, N, K, to_dev(x), workspace=ws)
+    rows = sample_rows(N, 92 + M)
+    ref = bq.reference_rows(x, W, bits, rows)
+    assert bq.rel_inf_err(y.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
+    assert torch.count_nonzero(ws) == 0
+    small_ws = torch.zeros(need - 16, dtype=torch.uint8, device=dev())
+    with pytest.raises(gbb.GbbError):
+        gbb.gemm_mixed_w(img, N, K, to_dev(x), workspace=small_ws)
 
 
 def test_auto_path_and_empty_batch():
