@@ -618,6 +618,23 @@ int launch(const W48Args& a, void* stream) {
   const int T = a.T8 + a.T4;
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int tile_rows = (a.T8 + 7) / 8 + (a.T4 + 7) / 8;   // 128-row workgroups of the tile kernel
+  if (a.M > 64 && a.M <= 128 && a.ga != 128 && !a.acc_out && tile_rows <= device_compute_units()) {
+    // Neither kernel splits K.  Here the tile kernel's single row of
+    // workgroups leaves CUs idle while each walks all of K, so two 64-token
+    // passes of the stream kernel, which reads the weights at HBM speed, are
+    // faster.  Per-token scales make a token range a self-contained call.
+    W48Args c = a;
+    for (int m0 = 0; m0 < a.M; m0 += 64) {
+      c.M = a.M - m0 < 64 ? a.M - m0 : 64;
+      c.xq = a.xq + size_t(m0) * size_t(a.K);
+      c.xs = a.xs + m0;
+      c.y = a.y + size_t(m0) * size_t(a.N);
+      const int rc = launch(c, stream);
+      if (rc != 0) return rc;
+    }
+    return 0;
+  }
   if (a.M <= 64 && a.ga != 128 && !a.acc_out) {
     const dim3 grid(unsigned((a.T8 + 3) / 4 + (a.T4 + 3) / 4));
     if (a.M <= 16)

@@ -609,7 +609,7 @@ def test_w48_random_shapes(N, K, M, frac, ga, seed):
     assert rel_err(y, ref) <= TOL
 
 
-@pytest.mark.parametrize("M", [32, 512, 4096])
+@pytest.mark.parametrize("M", [32, 96, 512, 4096])
 def test_w44a8_28672x8192(M):
     W, rows8, img = w44a8_image()
     assert rows8.size == 2867
