@@ -434,13 +434,24 @@ def main():
             # matrix-core-bound launches reach steady clocks only after some
             # tens of milliseconds of such work: warm up for ~30 launches
             sp = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, x, out=y), 30, 30)
+            # moderate batches: the library's own choice between the prefill
+            # kernel and 32-token decode chunks, against the prefill kernel forced
+            mid = {}
+            for Mm in (64, 256):
+                xm = x[:Mm].contiguous()
+                ym = y[:Mm]
+                sa = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, xm, out=ym), 30, 12)
+                sf = time_eager(torch, lambda: gbb.gemm_mixed_w_path(rot.next(), p.N, p.K, xm, 2, out=ym), 30, 12)
+                mid[f"M{Mm}"] = {"us": round(sa * 1e6, 1), "prefill_kernel_us": round(sf * 1e6, 1)}
+                log(f"prefill {p.name} M={Mm}: {sa * 1e6:.1f} us (prefill kernel alone {sf * 1e6:.1f} us)")
             del rot
             w32, w16 = gbb.dequant(imgd, p.N, p.K)
             del w32
             sl = time_eager(torch, lambda: torch.matmul(x, w16.t(), out=y), 30, 30)
             pre[p.name] = {"N": p.N, "K": p.K, "ms": round(sp * 1e3, 3), "TFLOPs": round(fl / sp / 1e12, 1),
                            "frac_fp16_peak": round(fl / sp / 1e12 / FP16_PEAK_TFLOPS, 3),
-                           "fp16_library_gemm_on_dequantized_TFLOPs": round(fl / sl / 1e12, 1)}
+                           "fp16_library_gemm_on_dequantized_TFLOPs": round(fl / sl / 1e12, 1),
+                           "moderate_batches": mid}
             log(f"prefill {p.name}: {fl / sp / 1e12:.0f} TFLOP/s (library fp16 GEMM {fl / sl / 1e12:.0f})")
             del imgd, x, y, w16
             torch.cuda.empty_cache()
@@ -456,7 +467,7 @@ def main():
         # last-level cache between calls.
         rot = Rotation([imgd] + [imgd.clone() for _ in range(3)])
         w48 = {}
-        for M in (32, 512, 4096):
+        for M in (32, 96, 512, 4096):
             x = torch.from_numpy(synth.activations(M, 8192, synth.WL_W44A8, 0)).to(dev)
             xq, xs = gbb.quant_act_i8(x)
             y = torch.empty((M, 28672), dtype=torch.float16, device=dev)
