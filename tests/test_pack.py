@@ -228,3 +228,25 @@ def test_graph_wrapper_rejects_mismatched_shapes():
         gbb.Graph([(img, 128, 256, x, y)])           # y has N = 64, not 128
     with pytest.raises(ValueError):
         gbb.Graph([])
+
+
+@pytest.mark.parametrize("N,K", [(8192, 28672), (28672, 8192), (4096, 4096), (64, 128)])
+def test_workspace_follows_the_batch_route(N, K):
+    """Host side of the dispatch: above 32 tokens a workspace is asked for
+    exactly when the batch runs as 32-token decode chunks, that is when
+    ceil(M/32) prefill grids of 128x512 tiles fit in one wave of the CUs
+    (256 when the library finds no device), and it is then the larger of the
+    full and the ragged last chunk's needs."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    for M in (33, 64, 65, 96, 128, 200, 256, 512, 1024, 2048):
+        tiles = -(-M // 128) * -(-N // 512)
+        chunked = -(-M // 32) * tiles <= cus
+        need = gbb.gemm_mixed_w_workspace(N, K, M)
+        if not chunked:
+            assert need == 0, (M, need)
+            continue
+        want = gbb.gemm_mixed_w_workspace(N, K, 32)
+        if M % 32:
+            want = max(want, gbb.gemm_mixed_w_workspace(N, K, M % 32))
+        assert need == want, (M, need, want)
