@@ -528,3 +528,102 @@ def test_oracle_w48_reader_against_slow_writer():
     assert np.array_equal(d["s4"].view(np.uint16), s4.view(np.uint16))
     assert np.array_equal(d["z4"], z4)
     assert np.all(d["q8_pad"] == 0) and np.all(d["q4_pad"] == 0)
+
+
+# ----------------------------------------------------------------------------
+# the parity checker itself
+# ----------------------------------------------------------------------------
+def test_rel_inf_err_hand_cases():
+    """||y - y_ref||_inf / ||y_ref||_inf on hand-computed cases: the maximum
+    (not a mean) over every element, the reference's norm (not y's) below,
+    an absolute error for an all-zero reference, and a failure for NaN or
+    infinite outputs."""
+    f = bq.rel_inf_err
+    assert f([1.0, -4.0, 2.0], [1.0, -4.0, 2.0]) == 0.0
+    assert f([1.5, -4.0, 2.0], [1.0, -4.0, 2.0]) == 0.125            # 0.5 / 4
+    # the denominator is max|y_ref| = 2, not max|y| = 10 (which gives 0.8)
+    assert f([1.0, 10.0], [1.0, 2.0]) == 4.0
+    # a maximum, not a mean: one element off by 0.4 out of four (a mean gives 0.05)
+    assert f([2.0, 2.0, 2.0, 2.4], [2.0, 2.0, 2.0, 2.0]) == pytest.approx(0.2, rel=1e-15)
+    # over all elements of a 2-D output
+    assert f([[1.0, 1.0], [0.0, -8.0]], [[1.0, 0.0], [0.0, -8.0]]) == 0.125
+    # a negated output is off by twice the reference
+    assert f([-3.0, 1.0], [3.0, -1.0]) == 2.0
+    # all-zero reference: the absolute error
+    assert f([0.0, 3e-4], [0.0, 0.0]) == 3e-4
+    # NaN or inf anywhere in y fails any tolerance
+    for bad in (np.nan, np.inf, -np.inf):
+        assert not (f([1.0, bad], [1.0, 2.0]) <= 2e-3)
+
+
+# ----------------------------------------------------------------------------
+# activation quantizer at exact ties, and codes for given scales and zeros
+# ----------------------------------------------------------------------------
+def _round_half_even(fr: Fraction) -> int:
+    """Python's round() of a Fraction is round-half-to-even (exact)."""
+    return round(fr)
+
+
+@pytest.mark.parametrize("group", [None, 128])
+def test_act_quant_exact_ties_half_even(group):
+    """x / s exactly halfway between two integers: round-half-to-even picks
+    the even one, where round-half-up (2.5 -> 3, 126.5 -> 127) and
+    round-half-away (-2.5 -> -3) do not.  The scale is exact: max|x| =
+    127 * 2^-4 gives s = 2^-4."""
+    s = Fraction(1, 16)
+    ties = [0.5, 1.5, 2.5, 3.5, 4.5, 126.5, -0.5, -1.5, -2.5, -3.5, -126.5]
+    K = 256
+    x = np.zeros((2, K), np.float16)
+    for m in range(2):
+        for gi in range(K // 128):
+            x[m, 128 * gi] = np.float16(127 * float(s) * (1 if m == 0 else -1))
+            for j, t in enumerate(ties):
+                x[m, 128 * gi + 1 + j] = np.float16(t * float(s))
+    assert Fraction(float(x[0, 1 + ties.index(126.5)])) == Fraction(253, 32)   # exact in fp16
+    A, sa = w48.quant_act(x, group)
+    assert np.all(sa.astype(np.float64) == float(s))
+    for m in range(2):
+        for k in range(K):
+            want = _round_half_even(Fraction(float(x[m, k])) / s)
+            assert A[m, k] == max(-127, min(127, want)), (m, k, float(x[m, k]))
+    # the cases that tell the rules apart
+    assert A[0, 1 + ties.index(2.5)] == 2 and A[0, 1 + ties.index(-2.5)] == -2
+    assert A[0, 1 + ties.index(126.5)] == 126 and A[0, 1 + ties.index(-1.5)] == -2
+
+
+def test_codes_with_given_scale_zero_brute_force():
+    """Codes for caller-given scales and zeros (a clipping search's, say):
+    every checked code is the in-range code whose grid point (q - z) s is
+    nearest to w, ties to (q - z) even -- found by trying every code.  The
+    inputs include exact ties, values beyond both ends of the grid and
+    zeros at both ends of the range, over every bitwidth."""
+    g = np.random.default_rng(31)
+    bits = np.array([[1, 2, 3], [4, 6, 8]], np.uint8)
+    N, K = 128, 384
+    G = K // 128
+    L = (2 ** np.repeat(bits.astype(np.int64), 64, axis=0)) - 1          # [N][G]
+    s16 = (g.uniform(0.002, 0.03, (N, G))).astype(np.float16)
+    z = np.floor(g.random((N, G)) * (L + 1)).astype(np.int64)
+    z[0] = 0
+    z[1] = L[1]
+    W = np.empty((N, K), np.float16)
+    ties = {}
+    for n in range(N):
+        for gi in range(G):
+            s = float(s16[n, gi])
+            lo, hi = -z[n, gi] - 2.0, L[n, gi] - z[n, gi] + 2.0        # a little beyond both ends
+            W[n, 128 * gi:128 * gi + 128] = (g.uniform(lo, hi, 128) * s).astype(np.float16)
+            for j in range(4):                                          # exact ties, if fp16 holds them
+                t = float(g.integers(int(lo), int(hi))) + 0.5
+                v = np.float16(t * s)
+                if Fraction(float(v)) == Fraction(t) * Fraction(s):
+                    W[n, 128 * gi + 120 + j] = v
+                    ties[(n, gi)] = ties.get((n, gi), 0) + 1
+    assert sum(ties.values()) > 50
+    q = bq.codes_with(W, bits, s16, z.astype(np.float16))
+    for n in range(N):
+        for gi in range(G):
+            s = Fraction(float(s16[n, gi]))
+            for k in list(range(0, 120, 9)) + list(range(120, 128)):
+                v = Fraction(float(W[n, 128 * gi + k]))
+                assert q[n, 128 * gi + k] == nearest_code(v, s, int(z[n, gi]), int(L[n, gi])), (n, gi, k)
