@@ -79,11 +79,6 @@ def weight_bytes(bits: np.ndarray) -> int:
     return 1024 * int(bits.astype(np.int64).sum()) + 256 * nblk + nblk + 4 * (nblk + 1)
 
 
-# launch groups of a decoder layer: projections that share their input are
-# stacked along the output rows into one packed matrix
-GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
-
-
 class DecodeLayerSet:
     """R copies of one decoder layer's packed launch groups on the GPU, with
     their activations, outputs and one shared split-K workspace."""
@@ -92,13 +87,11 @@ class DecodeLayerSet:
         self.torch, self.gbb = torch, gbb
         self.M = M
         host = []
-        for name, idx in GROUPS:
-            parts = [gen(i) for i in idx]
-            W = np.concatenate([W for (_, W, _) in parts])
-            bits = np.concatenate([b for (_, _, b) in parts])
+        for name, idx in synth.LAYER_LAUNCH_GROUPS:
+            N, K, W, bits = synth.stacked_group(gen, idx)
             img, _, _ = gbb.pack_blocks(W, bits)
-            host.append((name, W.shape, img, bits))
-            del W, parts
+            host.append((name, (N, K), img, bits))
+            del W
         self.images = [[torch.from_numpy(img).to(dev) for (_, _, img, _) in host] for _ in range(copies)]
         self.shapes = [shape for (_, shape, _, _) in host]
         self.names = [name for (name, _, _, _) in host]

@@ -51,7 +51,7 @@ _SIGS = {
     "gbb_pack_w48": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _sz]),
     "gbb_quant_act_i8": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "gbb_gemm_w48a8": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp]),
-    "gbb_w48_group_acc": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _vp]),
+    "gbb_w48_group_acc": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -339,10 +339,13 @@ def gemm_w48a8(image, N: int, K: int, n8: int, xq, xs, ga: int | None = None, ou
     return y
 
 
-def w48_group_acc(image, N: int, K: int, n8: int, xq):
+def w48_group_acc(image, N: int, K: int, n8: int, xq, ga: int | None = None):
+    """int32 [M][N][K/128] exact group sums xq . (q - z) from the kernel that
+    gbb_gemm_w48a8 runs for this M and ga (K: per-token scales, or 128)."""
     torch = _torch()
     M = xq.shape[0]
+    ga = K if ga is None else ga
     acc = torch.empty((M, N, K // 128), dtype=torch.int32, device=xq.device)
     _check(lib().gbb_w48_group_acc(_dev_ptr(image, torch.uint8, "image"), N, K, n8,
-                                   _dev_ptr(xq, torch.int8, "xq"), acc.data_ptr(), M, _stream(xq)))
+                                   _dev_ptr(xq, torch.int8, "xq"), ga, acc.data_ptr(), M, _stream(xq)))
     return acc

@@ -22,6 +22,7 @@ gbb_status check_block_args(const void* image, int N, int K, int M) {
   if (!image) return fail(GBB_E_ARG, "image is NULL");
   if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
   if (N > kMaxRows) return fail(GBB_E_SHAPE, "N=%d exceeds %d", N, kMaxRows);
+  if (K > kMaxCols) return fail(GBB_E_SHAPE, "K=%d exceeds %d", K, kMaxCols);
   if (M < 0) return fail(GBB_E_ARG, "M must not be negative (M=%d)", M);
   if (N % kBlockRows || K % kGroup)
     return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);
@@ -188,12 +189,13 @@ extern "C" gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, co
   return device_status(launch_w48(w48_view(image, N, K, n8), xq, xs, ga, y, M, stream), "w48 launch");
 }
 
-extern "C" gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq,
+extern "C" gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq, int ga,
                                         int32_t* acc, int M, void* stream) {
   gbb_status st = check_w48_args(image, N, K, n8);
   if (st != GBB_OK) return st;
   if (M <= 0) return fail(GBB_E_ARG, "M must be positive (M=%d)", M);
   if (!xq || !acc) return fail(GBB_E_ARG, "xq and acc must not be NULL");
+  if (ga != K && ga != 128) return fail(GBB_E_ARG, "ga must be K or 128 (ga=%d)", ga);
   if (!aligned16(xq)) return fail(GBB_E_ALIGN, "xq must be 16-byte aligned");
-  return device_status(launch_w48_acc(w48_view(image, N, K, n8), xq, acc, M, stream), "w48 acc launch");
+  return device_status(launch_w48_acc(w48_view(image, N, K, n8), xq, ga, acc, M, stream), "w48 acc launch");
 }

@@ -29,6 +29,8 @@ struct BlockImageView {
 // accumulator (first M * N * 8 bytes of the workspace) and one fp32 overflow
 // accumulator (next M * N * 4 bytes); both return to zero when a call ends.
 constexpr int kMaxRows = 1 << 20;   // N limit of the block format's entry points
+constexpr int kMaxCols = 1 << 20;   // K limit: the decode kernels address a token's row with a
+                                    // 32-bit byte offset (up to 32 tokens x 2 K bytes)
 constexpr int kMaxSegments = 32;    // K segments per block row (fits the count field)
 struct DecodePlan {
   int nw, nseg, seg_cols;
@@ -57,7 +59,7 @@ struct W48ImageView {
 int launch_quant_act(const uint16_t* x, int M, int K, int ga, int8_t* xq, uint16_t* xs, void* stream);
 int launch_w48(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
                int M, void* stream);
-int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int32_t* acc, int M, void* stream);
+int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int ga, int32_t* acc, int M, void* stream);
 
 // Returns a message for a HIP error code, or nullptr for success.
 const char* device_error_text(int err);

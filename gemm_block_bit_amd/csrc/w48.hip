@@ -295,7 +295,10 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
 
-template <bool GA>   // GA: activation scales per (token, group), else per token
+// GA: activation scales per (token, group), else per token.  ACC: store the
+// exact int32 group sums to a.acc_out instead of scaling them (the integer
+// step of this kernel, checked bit for bit).
+template <bool GA, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void w48_tile_kernel(W48Args a) {
   __shared__ u32x4 lds[kLdsW48 / 16];
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
@@ -385,6 +388,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < 4; ++j) c[i][j] = mfma16_i8(av[i], bv[j], c[i][j]);
     }
+    if constexpr (ACC) {
+      // the group sums as they are, at their original rows
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 4 * wn + j;
+        const int n = t < tend ? a.rows[16 * t + r16] : -1;
+        if (n < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
+            if (m < a.M) a.acc_out[(size_t(m) * a.N + n) * G + grp] = c[i][j][v];
+          }
+      }
+    } else {
     // step two: scale the exact group sums into the fp32 accumulators
     float sw[4];
 #pragma unroll
@@ -407,6 +426,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int v = 0; v < 4; ++v) tot[i][j][v] = __builtin_fmaf(float(c[i][j][v]), sw[j], tot[i][j][v]);
     }
+    }
     if (grp + 1 < G) {
       // the next group's loads have landed (this wave's), then everyone's;
       // the barrier also retires this group's reads of `buf`
@@ -415,6 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
+  if constexpr (ACC) return;
   // per-token scale, fused scatter to the original rows
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -467,8 +488,9 @@ __device__ __forceinline__ void wait_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.
-template <int TM, bool Q4>
+// One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.  ACC:
+// store each group's exact int32 sums to a.acc_out instead of scaling them.
+template <int TM, bool Q4, bool ACC>
 __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend) {
   using C = StreamCfg<TM>;
   constexpr int kStages = C::kStages;
@@ -512,6 +534,13 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
   for (int i = 0; i < TM; ++i) cp[i] = i32x4{0, 0, 0, 0};
   float swp = 0.0f;
 
+  // ACC: this lane's original row (-1: none), loaded and awaited before the
+  // first global->LDS load, so no later wait of the compiler's covers them
+  int n_acc = -1;
+  if constexpr (ACC) {
+    if (t0 + wave < tend) n_acc = a.rows[16 * (t0 + wave) + r16];
+    wait_vm<0>();
+  }
   for (int p = 0; p < kStages - 1 && p < G; ++p) issue(p);
   for (int grp = 0; grp < G; ++grp) {
     // this wave's loads of group grp have landed once at most the loads of the
@@ -555,6 +584,20 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
       c[i] = mfma16_i8(av[i][0], bv[0], i32x4{0, 0, 0, 0});
       c[i] = mfma16_i8(av[i][1], bv[1], c[i]);
     }
+    if constexpr (ACC) {
+      // the group sums as they are, at their original rows (stores add to the
+      // vector-memory count, which only makes the fixed waits above stricter)
+      if (n_acc >= 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = 16 * i + 4 * g + v;
+            if (m < a.M) a.acc_out[(size_t(m) * a.N + n_acc) * G + grp] = c[i][v];
+          }
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -563,6 +606,7 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     for (int i = 0; i < TM; ++i) cp[i] = c[i];
     swp = sw;
   }
+  if constexpr (ACC) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -580,7 +624,7 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     }
 }
 
-template <int TM>
+template <int TM, bool ACC>
 __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
   using C = StreamCfg<TM>;
   static_assert(2 * C::kStages * C::kStage <= 160 * 1024, "two workgroups per CU");
@@ -588,9 +632,9 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
   const int nb8 = (a.T8 + 3) / 4;
   if (int(blockIdx.x) < nb8)
-    stream_tiles<TM, false>(a, base, int(blockIdx.x) * 4, a.T8);
+    stream_tiles<TM, false, ACC>(a, base, int(blockIdx.x) * 4, a.T8);
   else
-    stream_tiles<TM, true>(a, base, a.T8 + (int(blockIdx.x) - nb8) * 4, a.T8 + a.T4);
+    stream_tiles<TM, true, ACC>(a, base, a.T8 + (int(blockIdx.x) - nb8) * 4, a.T8 + a.T4);
 }
 
 W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
@@ -614,12 +658,37 @@ W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, 
   return a;
 }
 
+template <bool ACC>
+void launch_stream(const W48Args& a, hipStream_t s) {
+  const dim3 grid(unsigned((a.T8 + 3) / 4 + (a.T4 + 3) / 4));
+  if (a.M <= 16)
+    hipLaunchKernelGGL((w48_stream_kernel<1, ACC>), grid, dim3(256), 0, s, a);
+  else if (a.M <= 32)
+    hipLaunchKernelGGL((w48_stream_kernel<2, ACC>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((w48_stream_kernel<4, ACC>), grid, dim3(256), 0, s, a);
+}
+
+template <bool ACC>
+void launch_tile(const W48Args& a, hipStream_t s) {
+  const unsigned by = unsigned((a.T8 + 7) / 8 + (a.T4 + 7) / 8);
+  const dim3 grid(unsigned((a.M + kTB - 1) / kTB), by);
+  if (a.ga == 128)
+    hipLaunchKernelGGL((w48_tile_kernel<true, ACC>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a);
+}
+
+// Picks the kernel for (M, ga).  A call with a.acc_out set takes the same
+// route with the kernel's group-sum store in place of its scaling step, so
+// the exported int32 sums are those of the kernel that runs the product.
 int launch(const W48Args& a, void* stream) {
   const int T = a.T8 + a.T4;
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool acc = a.acc_out != nullptr;
   const int tile_rows = (a.T8 + 7) / 8 + (a.T4 + 7) / 8;   // 128-row workgroups of the tile kernel
-  if (a.M > 64 && a.M <= 128 && a.ga != 128 && !a.acc_out && tile_rows <= device_compute_units()) {
+  if (a.M > 64 && a.M <= 128 && a.ga != 128 && tile_rows <= device_compute_units()) {
     // Neither kernel splits K.  Here the tile kernel's single row of
     // workgroups leaves CUs idle while each walks all of K, so two 64-token
     // passes of the stream kernel, which reads the weights at HBM speed, are
@@ -628,34 +697,28 @@ int launch(const W48Args& a, void* stream) {
     for (int m0 = 0; m0 < a.M; m0 += 64) {
       c.M = a.M - m0 < 64 ? a.M - m0 : 64;
       c.xq = a.xq + size_t(m0) * size_t(a.K);
-      c.xs = a.xs + m0;
-      c.y = a.y + size_t(m0) * size_t(a.N);
+      c.xs = a.xs ? a.xs + m0 : nullptr;
+      c.y = a.y ? a.y + size_t(m0) * size_t(a.N) : nullptr;
+      c.acc_out = acc ? a.acc_out + size_t(m0) * size_t(a.N) * size_t(a.K / 128) : nullptr;
       const int rc = launch(c, stream);
       if (rc != 0) return rc;
     }
     return 0;
   }
-  if (a.M <= 64 && a.ga != 128 && !a.acc_out) {
-    const dim3 grid(unsigned((a.T8 + 3) / 4 + (a.T4 + 3) / 4));
-    if (a.M <= 16)
-      hipLaunchKernelGGL(w48_stream_kernel<1>, grid, dim3(256), 0, s, a);
-    else if (a.M <= 32)
-      hipLaunchKernelGGL(w48_stream_kernel<2>, grid, dim3(256), 0, s, a);
+  if (a.M <= 64 && a.ga != 128) {
+    if (acc)
+      launch_stream<true>(a, s);
     else
-      hipLaunchKernelGGL(w48_stream_kernel<4>, grid, dim3(256), 0, s, a);
-  } else if (a.M > 64 && !a.acc_out) {
-    const unsigned by = unsigned((a.T8 + 7) / 8 + (a.T4 + 7) / 8);
-    const dim3 grid(unsigned((a.M + kTB - 1) / kTB), by);
-    if (a.ga == 128)
-      hipLaunchKernelGGL(w48_tile_kernel<true>, grid, dim3(256), 0, s, a);
+      launch_stream<false>(a, s);
+  } else if (a.M > 64) {
+    if (acc)
+      launch_tile<true>(a, s);
     else
-      hipLaunchKernelGGL(w48_tile_kernel<false>, grid, dim3(256), 0, s, a);
-  } else if (a.M <= 32) {
+      launch_tile<false>(a, s);
+  } else if (a.M <= 32) {   // group activation scales, M <= 64
     hipLaunchKernelGGL(w48_kernel<32>, dim3(unsigned((a.M + 31) / 32), gy), dim3(256), 0, s, a);
-  } else if (a.M <= 64) {
-    hipLaunchKernelGGL(w48_kernel<64>, dim3(unsigned((a.M + 63) / 64), gy), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(w48_kernel<128>, dim3(unsigned((a.M + 127) / 128), gy), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(w48_kernel<64>, dim3(unsigned((a.M + 63) / 64), gy), dim3(256), 0, s, a);
   }
   return int(hipGetLastError());
 }
@@ -673,8 +736,8 @@ int launch_w48(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int
   return launch(make_args(im, xq, xs, ga, y, nullptr, M), stream);
 }
 
-int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int32_t* acc, int M, void* stream) {
-  return launch(make_args(im, xq, nullptr, im.K, nullptr, acc, M), stream);
+int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int ga, int32_t* acc, int M, void* stream) {
+  return launch(make_args(im, xq, nullptr, ga, nullptr, acc, M), stream);
 }
 
 }  // namespace gbb

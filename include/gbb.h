@@ -150,7 +150,11 @@ size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
  *   kernels run the batch in 32-token chunks, one launch each, which keeps
  *   every CU busy where the prefill kernel would leave most of them idle.
  *   workspace/ws_bytes  device memory of gbb_gemm_mixed_w_workspace(N, K, M)
- *          bytes (NULL allowed when that is 0). */
+ *          bytes (NULL allowed when that is 0).
+ * Errors: GBB_E_ARG (NULL image/x/y, N or K <= 0, M < 0, x and y overlap,
+ * missing workspace), GBB_E_SHAPE (N % 64, K % 128, N or K above 2^20, or
+ * M * K >= 2^31 on the prefill kernel), GBB_E_ALIGN, GBB_E_SPACE (workspace
+ * too small), GBB_E_DEVICE (launch failed).  M == 0 does nothing. */
 gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
                             uint16_t* y, int M, void* workspace, size_t ws_bytes,
                             void* stream);
@@ -235,10 +239,16 @@ gbb_status gbb_quant_act_i8(const uint16_t* x, int M, int K, int ga, int8_t* xq,
 gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, const int8_t* xq,
                           const uint16_t* xs, int ga, uint16_t* y, int M, void* stream);
 
-/* Debug export: the int32 group products acc[m][n][g] = sum over the group of
- * xq[m][k] * (q[n][k] - z[n][g]) for every original row n (device int32
- * [M][N][K/128]), for bit-exact tests on small shapes. */
-gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq,
+/* Debug export of the first step of the two-step dequantization (MixLLM
+ * page, section 3.3: per group an exact integer product of the int8
+ * activations and the int8 weight codes (q - z), before any scale):
+ * acc[m][n][g] = sum over group g of xq[m][k] * (q[n][k] - z[n][g]) for every
+ * original row n (device int32 [M][N][K/128]), for bit-exact tests.  The call
+ * runs the kernel gbb_gemm_w48a8 runs for the same M and ga (K or 128), with
+ * that kernel's scaling step replaced by a store of the group sums, so the
+ * integers checked are those the product path forms.  Errors as
+ * gbb_gemm_w48a8. */
+gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq, int ga,
                              int32_t* acc, int M, void* stream);
 
 #ifdef __cplusplus

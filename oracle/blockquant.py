@@ -129,16 +129,22 @@ def reference_gemm(x16, W16, bits) -> np.ndarray:
 
 
 def reference_rows(x16, W16, bits, rows) -> np.ndarray:
-    """Reference outputs y[:, rows] for selected rows only (quantizes just the
-    64-row block rows that hold them), for sampled checks at full size."""
-    rows = np.asarray(rows)
-    out = np.empty((np.asarray(x16).shape[0], rows.size), np.float64)
-    for j, n in enumerate(rows):
-        br = int(n) // BLOCK_ROWS
-        q, s16, z16 = quantize_blocks(W16[br * 64:(br + 1) * 64], bits[br:br + 1])
-        w = dequant_fp32(q, s16, z16)[int(n) - br * 64]
-        out[:, j] = np.asarray(x16, np.float64) @ w.astype(np.float64)
-    return out
+    """Reference outputs y[:, rows] for selected rows only, for sampled checks
+    at full size.  Each (row, group) is quantized on its own, so only the
+    selected rows are quantized, with their blocks' bitwidths -- the same
+    steps as quantize_blocks, then the exact dequantization and an fp64
+    product."""
+    rows = np.asarray(rows, np.int64)
+    W16 = np.asarray(W16, np.float16)
+    N, K = W16.shape
+    G = K // GROUP
+    gb = group_bits(bits, N, K)[rows]                       # [n][G]
+    v = W16[rows].astype(np.float64).reshape(rows.size, G, GROUP)
+    levels = 2.0 ** gb - 1.0
+    sc, z = choose_scale_zero(v.min(axis=2), v.max(axis=2), levels)
+    q = _codes(v, sc, z, levels).reshape(rows.size, K)
+    w = dequant_fp32(q, sc, z.astype(np.float16))
+    return gemm_fp64(x16, w)
 
 
 def rel_inf_err(y, y_ref) -> float:

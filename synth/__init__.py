@@ -232,5 +232,21 @@ def w44a8_28672x8192() -> Tuple[np.ndarray, np.ndarray]:
     return W, salient_rows_by_l2(W, 0.10)
 
 
+# Launch groups of a decoder layer: projections that read the same input are
+# stacked along the output rows into one matrix, as serving stacks do
+# (q|k|v and gate|up), so a layer is four products.
+LAYER_LAUNCH_GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def stacked_group(gen, idx) -> Tuple[int, int, np.ndarray, np.ndarray]:
+    """(N, K, W, bits) of the projections gen(i), i in idx, stacked along the
+    output rows (same K); the bitmaps are stacked the same way."""
+    parts = [gen(i) for i in idx]
+    K = parts[0][0].K
+    W = np.concatenate([w for (_, w, _) in parts]) if len(parts) > 1 else parts[0][1]
+    bits = np.concatenate([b for (_, _, b) in parts]) if len(parts) > 1 else parts[0][2]
+    return W.shape[0], K, W, bits
+
+
 def mean_bits(bits: np.ndarray) -> float:
     return float(np.asarray(bits, np.float64).mean())

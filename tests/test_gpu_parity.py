@@ -337,11 +337,11 @@ def test_library_graph_matches_eager(M):
                     calls[0][4])])
 
 
-@pytest.mark.parametrize("M", [1, 8, 64])
+@pytest.mark.parametrize("M", [1, 8, 17, 32, 64])
 def test_maximum_rows(M):
     """N = 2^20 rows (the largest N the block entry points take) on a single
-    block column, through each kernel family; one block row more is an
-    error."""
+    block column, through each kernel family (at M = 17 and 32 the two-row
+    decode kernel with no K split); one block row more is an error."""
     N, K = 1 << 20, 128
     g = np.random.default_rng(60)
     W = (0.02 * g.standard_normal((N, K), dtype=np.float32)).astype(np.float16)
@@ -486,14 +486,64 @@ def test_llama3_70b_layer_decode(i):
         assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
 
 
+def one_row_per_block_row(N, seed):
+    """One row at a random offset inside every 64-row block row, so every
+    decode workgroup (and each of its K segments, which all write every row
+    of the block row) and every prefill wave is checked."""
+    g = np.random.default_rng(seed)
+    return np.arange(0, N, 64) + g.integers(0, 64, N // 64)
+
+
 @pytest.mark.parametrize("i", [0, 1])
 def test_prefill_70b_mlp_m2048(i):
     p, W, bits, img = workload("prefill", i)
     x = synth.prefill_x(2048, p.K, i)
     y = gbb.gemm_mixed_w(img, p.N, p.K, to_dev(x)).cpu().numpy()
-    rows = sample_rows(p.N, 20 + i, 12)
+    rows = one_row_per_block_row(p.N, 20 + i)
     ref = bq.reference_rows(x, W, bits, rows)
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+@functools.lru_cache(maxsize=1)
+def stacked_launch(layer, group):
+    """One launch group of a decoder layer, stacked as the benchmark packs it
+    (q|k|v and gate|up are one matrix each)."""
+    gen = synth.llama3_8b_proj if layer == "8b" else synth.llama3_70b_proj
+    idx = dict(synth.LAYER_LAUNCH_GROUPS)[group]
+    N, K, W, bits = synth.stacked_group(gen, idx)
+    img, _, _ = gbb.pack_blocks(W, bits)
+    return N, K, W, bits, to_dev(img)
+
+
+# the launches and batch sizes the benchmark times: Llama-3-8B at M = 1, 8 and
+# Llama-3-70B at M = 1, 8, 32 (70B gate|up at M = 32 is the two-row kernel
+# without a K split)
+BENCH_LAUNCHES = [("8b", gname, (1, 8)) for gname, _ in synth.LAYER_LAUNCH_GROUPS] + \
+                 [("70b", gname, (1, 8, 32)) for gname, _ in synth.LAYER_LAUNCH_GROUPS]
+
+
+@pytest.mark.parametrize("layer,group,Ms", BENCH_LAUNCHES)
+def test_benchmark_launches(layer, group, Ms):
+    N, K, W, bits, img = stacked_launch(layer, group)
+    rows = one_row_per_block_row(N, N + K)
+    wl = synth.WL_LLAMA3_8B if layer == "8b" else synth.WL_LLAMA3_70B
+    ws = torch.zeros(max(gbb.gemm_mixed_w_workspace(N, K, M) for M in Ms) + 256, dtype=torch.uint8,
+                     device=dev())
+    for M in Ms:
+        x = synth.activations(M, K, wl, 50 + M)
+        y = gbb.gemm_mixed_w(img, N, K, to_dev(x), workspace=ws).cpu().numpy()
+        ref = bq.reference_rows(x, W, bits, rows)
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL, M
+    assert not torch.any(ws)
+
+
+def test_linear_4096_output():
+    """The single 4096 x 4096 layer with bits {2,3,4} on its own x, every
+    output against the oracle."""
+    W, bits, x = synth.linear_4096()
+    img = packed(W, bits)
+    y = gbb.gemm_mixed_w(img, 4096, 4096, to_dev(x))
+    assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
 
 
 def test_reordered_allocated_layer():
@@ -535,24 +585,46 @@ def test_act_quant_bit_exact(M, K, ga):
     assert np.array_equal(xs.cpu().numpy().view(np.uint16), s.view(np.uint16))
 
 
-@pytest.mark.parametrize("N,K,M,frac", [(48, 256, 3, 0.1), (200, 384, 40, 0.1), (64, 128, 17, 0.0),
-                                        (40, 256, 70, 1.0), (300, 1024, 130, 0.2)])
-def test_w48_group_acc_bit_exact(N, K, M, frac):
-    W = small(N, K, N + M)
-    rows8 = synth.salient_rows_by_l2(W, frac) if frac < 1 else np.arange(N, dtype=np.int32)
-    img, _, _ = gbb.pack_w48(W, rows8)
-    x = rand_x(M, K, N)
-    xq, _ = gbb.quant_act_i8(to_dev(x))
-    acc = gbb.w48_group_acc(to_dev(img), N, K, rows8.size, xq).cpu().numpy()
-    qd = ow48.quantize_w48(W, rows8)
-    A, _ = ow48.quant_act(x)
-    ref = np.zeros((M, N, K // 128), np.int64)
+def w48_acc_reference(x, W, rows8, rows=None, ga=None):
+    """int64 [M][n][G] exact group sums of the oracle for the original rows
+    `rows` (all rows if None), activations quantized per token (ga None) or
+    per group of ga columns."""
+    N = W.shape[0]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    is8 = np.isin(rows, rows8)
+    qd = ow48.quantize_w48(W[rows], np.nonzero(is8)[0])
+    A, _ = ow48.quant_act(x, ga)
+    ref = np.zeros((x.shape[0], rows.size, W.shape[1] // 128), np.int64)
     if qd["rows8"].size:
         ref[:, qd["rows8"]] = ow48.group_acc(A, qd["q8"].astype(np.int64))
     if qd["rows4"].size:
         Wz = qd["q4"].astype(np.int64) - np.repeat(qd["z4"].astype(np.int64), 128, axis=1)
         ref[:, qd["rows4"]] = ow48.group_acc(A, Wz)
-    assert np.array_equal(acc.astype(np.int64), ref)
+    return ref
+
+
+# (N, K, M, 8-bit row fraction, ga): the kernel gbb_gemm_w48a8 picks for the
+# same M and ga -- stream (M <= 64, per-token scales; 1, 2 and 4 token tiles),
+# two 64-token stream passes (65-128 tokens on a short tile grid), tile
+# (M > 64, both scale granularities), and the register-staged kernel (group
+# scales at M <= 64) -- forms the sums; K = 8192 with N reduced stands in for
+# the 28672 x 8192 layer
+W48_ACC_CASES = [(48, 256, 3, 0.1, None), (200, 384, 32, 0.1, None), (200, 384, 40, 0.1, None),
+                 (64, 128, 17, 0.0, None), (40, 256, 70, 1.0, None), (300, 1024, 96, 0.2, None),
+                 (300, 1024, 130, 0.2, None), (300, 1024, 40, 0.2, 128), (300, 1024, 130, 0.2, 128),
+                 (200, 512, 77, 0.5, 128), (2048, 8192, 32, 0.1, None), (2048, 8192, 96, 0.1, None),
+                 (2048, 8192, 512, 0.1, None), (2048, 8192, 512, 0.1, 128)]
+
+
+@pytest.mark.parametrize("N,K,M,frac,ga", W48_ACC_CASES)
+def test_w48_group_acc_bit_exact(N, K, M, frac, ga):
+    W = small(N, K, N + M)
+    rows8 = synth.salient_rows_by_l2(W, frac) if frac < 1 else np.arange(N, dtype=np.int32)
+    img, _, _ = gbb.pack_w48(W, rows8)
+    x = rand_x(M, K, N)
+    xq, _ = gbb.quant_act_i8(to_dev(x), ga)
+    acc = gbb.w48_group_acc(to_dev(img), N, K, rows8.size, xq, ga).cpu().numpy()
+    assert np.array_equal(acc.astype(np.int64), w48_acc_reference(x, W, rows8, ga=ga))
 
 
 @pytest.mark.parametrize("N,K,M,ga,frac", [(48, 256, 3, None, 0.1), (200, 384, 40, None, 0.1),
@@ -609,14 +681,52 @@ def test_w48_random_shapes(N, K, M, frac, ga, seed):
     assert rel_err(y, ref) <= TOL
 
 
+def packed_rows(N, rows8):
+    """Original rows in the packed order of the W4/W8 image: the 8-bit rows,
+    then the 4-bit rows, each ascending and padded with -1 to 16-row tiles."""
+    r8 = np.asarray(rows8, np.int64)
+    r4 = np.setdiff1d(np.arange(N), r8)
+    pad = lambda r: np.concatenate([r, -np.ones((-r.size) % 16, np.int64)])
+    return np.concatenate([pad(r8), pad(r4)])
+
+
+def one_row_per(packed, stride, seed):
+    """One original row from every `stride` consecutive packed rows."""
+    g = np.random.default_rng(seed)
+    out = []
+    for c0 in range(0, packed.size, stride):
+        chunk = packed[c0:c0 + stride]
+        chunk = chunk[chunk >= 0]
+        if chunk.size:
+            out.append(int(g.choice(chunk)))
+    return np.unique(out)
+
+
 @pytest.mark.parametrize("M", [32, 96, 512, 4096])
 def test_w44a8_28672x8192(M):
+    """The 28672 x 8192 layer in the launches the benchmark times: one
+    checked row in every 16-row tile (a stream-kernel wave) at M <= 128, in
+    every 128-row block of tiles (a tile-kernel workgroup) above."""
     W, rows8, img = w44a8_image()
     assert rows8.size == 2867
     x = synth.activations(M, 8192, synth.WL_W44A8, 0)
     xq, xs = gbb.quant_act_i8(to_dev(x))
     y = gbb.gemm_w48a8(img, 28672, 8192, rows8.size, xq, xs).cpu().numpy()
-    rows = np.unique(np.concatenate([rows8[:8], sample_rows(28672, M, 16)]))
-    qd = ow48.quantize_w48(W[rows], np.nonzero(np.isin(rows, rows8))[0])
-    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0], quant=qd)
+    rows = one_row_per(packed_rows(28672, rows8), 16 if M <= 128 else 128, M)
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0])
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+@pytest.mark.parametrize("M", [32, 96, 512])
+def test_w44a8_28672x8192_group_acc_bit_exact(M):
+    """Exact int32 group sums of the kernels that run the 28672 x 8192 layer
+    (stream at 32 tokens, two stream passes at 96, tile at 512), one row per
+    16-row tile."""
+    W, rows8, img = w44a8_image()
+    x = synth.activations(M, 8192, synth.WL_W44A8, 1)
+    xq, _ = gbb.quant_act_i8(to_dev(x))
+    rows = one_row_per(packed_rows(28672, rows8), 16, 100 + M)
+    acc = gbb.w48_group_acc(img, 28672, 8192, rows8.size, xq)
+    got = acc[:, torch.from_numpy(rows).to(acc.device)].cpu().numpy().astype(np.int64)
+    del acc
+    assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows))

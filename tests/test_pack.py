@@ -152,6 +152,23 @@ def test_pack_errors():
     assert b"multiple" in L.gbb_last_error()
 
 
+def test_device_entry_points_reject_shapes_before_any_device_work():
+    """Shape checks come first, on the host: a bogus (aligned) image pointer
+    is never touched, so this runs without a GPU.  N and K are each capped at
+    2^20 (the decode kernels address a token's activations with a 32-bit
+    byte offset of up to 32 * 2 * K)."""
+    L = gbb.lib()
+    fake = 1 << 20
+    for N, K, st in [((1 << 20) + 64, 128, -2), (64, (1 << 20) + 128, -2), (96, 128, -2), (64, 200, -2),
+                     (0, 128, -1), (64, -128, -1)]:
+        assert L.gbb_gemm_mixed_w(fake, N, K, fake, fake, 1, None, 0, None) == st, (N, K)
+        assert L.gbb_gemm_mixed_w_path(fake, N, K, fake, fake, 1, None, 0, 1, None) == st, (N, K)
+    assert b"exceeds" in (L.gbb_gemm_mixed_w(fake, 64, 1 << 21, fake, fake, 1, None, 0, None) == -2
+                          and L.gbb_last_error())
+    assert L.gbb_gemm_mixed_w(None, 64, 128, fake, fake, 1, None, 0, None) == -1
+    assert L.gbb_gemm_mixed_w(fake + 8, 64, 128, fake, fake, 1, None, 0, None) == -4
+
+
 def test_check_image():
     W = small(128, 256, 3)
     bits = synth.random_bitmap(128, 256, ALLOWED, 3)
