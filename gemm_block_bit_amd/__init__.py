@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     check_image,
     dequant,
     gemm_mixed_w,
+    gemm_mixed_w_noalloc,
     gemm_mixed_w_path,
     gemm_mixed_w_workspace,
     gemm_w48a8,

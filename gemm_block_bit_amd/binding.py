@@ -42,6 +42,7 @@ _SIGS = {
     "gbb_gemm_mixed_w_workspace": (_sz, [_i, _i, _i]),
     "gbb_gemm_mixed_w": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_gemm_mixed_w_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
+    "gbb_gemm_mixed_w_noalloc": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp]),
     "gbb_graph_create": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_graph_launch": (_i, [_vp, _vp]),
     "gbb_graph_destroy": (_i, [_vp]),
@@ -248,6 +249,21 @@ def gemm_mixed_w_path(image, N: int, K: int, x, path: int, out=None, workspace=N
 def gemm_mixed_w(image, N: int, K: int, x, out=None, workspace=None):
     """y = x . dequant(W)^T (fp16 [M][N]) on torch's current stream."""
     return gemm_mixed_w_path(image, N, K, x, 0, out, workspace)
+
+
+def gemm_mixed_w_noalloc(image, N: int, K: int, x, out=None):
+    """gemm_mixed_w without a workspace: the library's fixed per-device
+    scratch array holds the split-K accumulators (calls on one GPU must not
+    overlap)."""
+    torch = _torch()
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M][{K}]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check(lib().gbb_gemm_mixed_w_noalloc(
+        _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),
+        _dev_ptr(y, torch.float16, "y"), M, _stream(x)))
+    return y
 
 
 class Graph:

@@ -103,8 +103,8 @@ extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
   return p.ws_bytes;
 }
 
-extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t* x, uint16_t* y,
-                                            int M, void* workspace, size_t ws_bytes, int path, void* stream) {
+gbb_status gbb::check_gemm_args(const void* image, int N, int K, const uint16_t* x, const uint16_t* y, int M,
+                                int path) {
   gbb_status st = check_block_args(image, N, K, M);
   if (st != GBB_OK) return st;
   if (M == 0) return GBB_OK;
@@ -115,6 +115,13 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
   const char* xb = reinterpret_cast<const char*>(x);
   const char* yb = reinterpret_cast<const char*>(y);
   if (xb < yb + size_t(M) * N * 2 && yb < xb + size_t(M) * K * 2) return fail(GBB_E_ARG, "x and y overlap");
+  return GBB_OK;
+}
+
+extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t* x, uint16_t* y,
+                                            int M, void* workspace, size_t ws_bytes, int path, void* stream) {
+  gbb_status st = check_gemm_args(image, N, K, x, y, M, path);
+  if (st != GBB_OK || M == 0) return st;
   const BlockImageView v = block_view(image, N, K);
   if (path == 0 && decode_in_chunks(N, M)) {
     const size_t need = chunked_workspace(N, K, M);

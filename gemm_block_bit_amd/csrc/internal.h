@@ -11,6 +11,11 @@ namespace gbb {
 gbb_status fail(gbb_status st, const char* fmt, ...);
 gbb_status ok();
 
+// Argument checks of gbb_gemm_mixed_w_path (path 0 = automatic), shared by
+// the entry points that run it.
+gbb_status check_gemm_args(const void* image, int N, int K, const uint16_t* x, const uint16_t* y, int M,
+                           int path);
+
 // IEEE binary16 <-> binary64, round-to-nearest-even (host).
 double half_to_double(uint16_t h);
 uint16_t double_to_half(double d);

@@ -159,6 +159,26 @@ gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
                             uint16_t* y, int M, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/* Allocation-free variant of gbb_gemm_mixed_w, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (without the workspace),
+ * checks and kernels as gbb_gemm_mixed_w; the split-K accumulators live in a
+ * fixed array of GBB_NOALLOC_SCRATCH_BYTES of device memory that the library
+ * holds on each GPU it runs on, from the first call on that GPU until the
+ * process ends.  That first call also zero-fills the array on `stream`
+ * (again on later calls while the fills so far were recorded under stream
+ * capture); every call leaves it zero.  All calls on one GPU share that
+ * GPU's array, so calls that may overlap on one GPU (several streams or
+ * threads, graphs replayed concurrently) race and give wrong results.  The
+ * call allocates and frees nothing.
+ * Errors: those of gbb_gemm_mixed_w; GBB_E_SPACE when the shape needs more
+ * than GBB_NOALLOC_SCRATCH_BYTES of workspace (gbb_gemm_mixed_w_workspace;
+ * no shape the block entry points accept needs more than 12 MiB);
+ * GBB_E_DEVICE when the array's address cannot be obtained. */
+#define GBB_NOALLOC_SCRATCH_BYTES (16u << 20)
+gbb_status gbb_gemm_mixed_w_noalloc(const void* image, int N, int K, const uint16_t* x,
+                                    uint16_t* y, int M, void* stream);
+
 /* Whole-layer execution (ScaleBITS explainer page, section 3.2: an execution
  * plan generated for a given bit configuration; MixLLM page, section 3.3:
  * the kernels of a step replayed from a captured graph).  Captures n
