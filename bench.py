@@ -1,21 +1,23 @@
 """Benchmark of the fused dequantize-and-multiply path on one MI355X.
 
-Headline (one JSON line): decode (M = 1) weight GB/s over Llama-3-8B-shaped
+Headline (one JSON line): decode (M = 1) weight GB/s over Llama-3-70B-shaped
 decoder layers -- q, k, v, o, gate, up, down at 64x128 blocks with bitwidths
-from {1,2,3,4,6,8} (mean 3.1) -- against the 8 TB/s HBM peak.  Projections
+from {1,2,3,4,6,8} (mean 2.1) -- against the 8 TB/s HBM peak.  Projections
 that read the same input are packed as one matrix, as serving stacks do:
-q|k|v (6144 x 4096) and gate|up (28672 x 4096), so a layer is four launches
-(qkv, o, gate_up, down).  One step is one token through a stack of distinct
-layer copies whose packed weights (732 MB) exceed the 256 MiB Infinity
-Cache, so every weight byte comes from HBM.  The step is replayed from a HIP
-graph of its 32 launches.
+q|k|v (10240 x 8192) and gate|up (57344 x 8192), so a layer is four dependent
+launches (qkv, o, gate_up, down).  One step is one token through a stack of
+three distinct layer copies whose packed weights (756 MB) exceed the 256 MiB
+Infinity Cache, so every weight byte comes from HBM.  The step is replayed
+from a HIP graph of its 12 launches.
 
-Also reported: p10/p50/p90 of single step replays, M = 8 on the same
-layers, the same shapes with uniform 3- and 4-bit bitmaps (the cost of
-mixing bitwidths), one 4096 x 4096 matrix at M = 1, the 70B-shaped layer at
-M = 1, 8 and 32, the M = 2048 prefill GEMM (TFLOP/s against the 2.5 PFLOP/s fp16 dense peak) with
-an fp16 library GEMM on the dequantized weights for context, the W4.4A8 layer
-(M = 32, 512, 4096) and the oracle timed on the host cores (cpu_baseline).
+Also reported: p10/p50/p90 of single step replays, each launch group alone
+(a graph of that group's launches), the same step as one library graph, the
+70B layer at M = 8 and 32, the Llama-3-8B layer at M = 1 and 8, the same 8B
+shapes with uniform 3- and 4-bit bitmaps (the cost of mixing bitwidths), one
+4096 x 4096 matrix at M = 1, the M = 2048 prefill GEMM (TFLOP/s against the
+2.5 PFLOP/s fp16 dense peak) with an fp16 library GEMM on the dequantized
+weights for context, the W4.4A8 layer (M = 32 ... 4096) and the oracle timed
+on the host cores over one copy of the headline layer (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--extras a,b,...]
 """
@@ -36,10 +38,10 @@ HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
 LAYER_COPIES_8B = 8       # 8 x 91.5 MB > 512 MiB
-LAYER_COPIES_70B = 3      # 3 x 252 MB
+LAYER_COPIES_70B = 3      # 3 x 252 MB > 512 MiB
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode1_llama3_8b_layer_m1.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode1_llama3_70b_layer_m1.md")
 DECODE_SOURCE = os.path.join(ROOT, "gemm_block_bit_amd", "csrc", "decode.hip")
 
 
@@ -64,7 +66,7 @@ def measured_traffic():
 
 
 # extra workloads after the headline, in run order
-EXTRAS = ("llama3_8b_m8", "mixed_vs_uniform", "linear_4096", "llama3_70b", "prefill", "w44a8")
+EXTRAS = ("llama3_70b_batch", "llama3_8b", "mixed_vs_uniform", "linear_4096", "prefill", "w44a8")
 
 
 def log(msg):
@@ -83,7 +85,7 @@ class DecodeLayerSet:
     """R copies of one decoder layer's packed launch groups on the GPU, with
     their activations, outputs and one shared split-K workspace."""
 
-    def __init__(self, torch, gbb, synth, gen, copies, M, dev):
+    def __init__(self, torch, gbb, synth, gen, copies, M, dev, keep_host=False):
         self.torch, self.gbb = torch, gbb
         self.M = M
         host = []
@@ -100,6 +102,7 @@ class DecodeLayerSet:
         nblk = sum(b.size for (_, _, _, b) in host)
         self.mean_bits = float(sum(int(b.astype(np.int64).sum()) for (_, _, _, b) in host)) / nblk
         self.copies = copies
+        self.host = host if keep_host else None
         g = np.random.default_rng(7)
         self.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
         self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (N, _) in self.shapes]
@@ -128,17 +131,21 @@ class DecodeLayerSet:
             for i, (N, K) in enumerate(self.shapes):
                 yield r, i, N, K
 
-    def step(self, stream_handle, events=None):
-        fn, ws = self.fn, self.ws
-        for r, i, N, K in self.launches():
-            if events is not None:
-                events[r][i][0].record()
-            st = fn(self.images[r][i].data_ptr(), N, K, self.x[i].data_ptr(), self.y[i].data_ptr(), self.M,
-                    ws.data_ptr(), ws.numel(), stream_handle)
-            if st:
-                raise RuntimeError(self.gbb.lib().gbb_last_error().decode())
-            if events is not None:
-                events[r][i][1].record()
+    def launch(self, r, i, stream_handle):
+        N, K = self.shapes[i]
+        st = self.fn(self.images[r][i].data_ptr(), N, K, self.x[i].data_ptr(), self.y[i].data_ptr(), self.M,
+                     self.ws.data_ptr(), self.ws.numel(), stream_handle)
+        if st:
+            raise RuntimeError(self.gbb.lib().gbb_last_error().decode())
+
+    def step(self, stream_handle):
+        for r, i, _, _ in self.launches():
+            self.launch(r, i, stream_handle)
+
+    def group_step(self, i, stream_handle):
+        """Launch group i of every copy."""
+        for r in range(self.copies):
+            self.launch(r, i, stream_handle)
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -205,6 +212,36 @@ def time_eager(torch, fn, reps, warmup):
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def group_graph_times(torch, L, steps, warmup, h):
+    """Each launch group alone: a graph of that group's launch in every copy,
+    replayed; microseconds and weight GB/s per launch."""
+    out = {}
+    for i, name in enumerate(L.names):
+        sec, _, g = time_graph(torch, lambda i=i: L.group_step(i, h()), steps, warmup)
+        del g
+        us = sec * 1e6 / L.copies
+        out[name] = {"N": L.shapes[i][0], "K": L.shapes[i][1], "us": round(us, 2), "MB": round(L.bytes[i] / 1e6, 2),
+                     "GBps": round(L.bytes[i] / us / 1e3, 1),
+                     "frac_hbm": round(L.bytes[i] / us / 1e3 / HBM_PEAK_GBS, 3)}
+    return out
+
+
+def library_graph_us(torch, gbb, L, steps, warmup):
+    """The step as one library graph (gbb_graph_create over its launches)."""
+    lg = gbb.Graph([(L.images[r][i], N, K, L.x[i], L.y[i]) for r, i, N, K in L.launches()])
+    for _ in range(warmup):
+        lg.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        lg.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    lg.close()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,71 +288,36 @@ def main():
     device_info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
                    "memory_GiB": round(props.total_memory / 2**30, 1)}
-
-    # ---------------- headline: Llama-3-8B layers, decode M = 1 ----------------
-    log("packing Llama-3-8B-shaped layer (qkv, o, gate_up, down)")
-    L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
-    log(f"layer weight bytes {L8.layer_bytes / 1e6:.1f} MB x {L8.copies} copies")
     h = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
 
-    sec, wall, g8 = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
-    total_bytes = L8.layer_bytes * L8.copies
+    # ---------------- headline: Llama-3-70B layers, decode M = 1 ----------------
+    log("packing Llama-3-70B-shaped layer (qkv, o, gate_up, down)")
+    L70 = DecodeLayerSet(torch, gbb, synth, synth.llama3_70b_proj, LAYER_COPIES_70B, 1, dev,
+                         keep_host=not args.quick and not args.no_cpu_baseline)
+    log(f"layer weight bytes {L70.layer_bytes / 1e6:.1f} MB x {L70.copies} copies, mean {L70.mean_bits:.3f} bits")
+    sec, wall, g70 = time_graph(torch, lambda: L70.step(h()), args.steps, args.warmup)
+    total_bytes = L70.layer_bytes * L70.copies
     value = total_bytes / sec / 1e9
     log(f"decode M=1: {sec * 1e6:.1f} us/step, {value:.0f} GB/s")
-    step_pct = replay_percentiles(torch, g8, args.steps)
-    del g8
+    step_pct = replay_percentiles(torch, g70, args.steps)
+    del g70
+    # each launch group on its own, and the step as one library graph
+    per_group = group_graph_times(torch, L70, args.steps, args.warmup, h)
+    log(f"per launch group: {per_group}")
+    lib_us = library_graph_us(torch, gbb, L70, args.steps, args.warmup)
+    log(f"the same step as one library graph: {lib_us:.1f} us")
 
-    # the same step as one library graph (gbb_graph_create over the 32 calls)
-    lg = gbb.Graph([(L8.images[r][i], N, K, L8.x[i], L8.y[i]) for r, i, N, K in L8.launches()])
-    for _ in range(args.warmup):
-        lg.launch()
-    torch.cuda.synchronize()
-    le0, le1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    le0.record()
-    for _ in range(args.steps):
-        lg.launch()
-    le1.record()
-    torch.cuda.synchronize()
-    lib_graph_us = le0.elapsed_time(le1) * 1e3 / args.steps
-    lg.close()
-    log(f"the same step as one library graph: {lib_graph_us:.1f} us")
-
-    # per-launch events over the same timed work (eager launches, one stream)
-    ng = len(L8.shapes)
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ng)] for _ in range(L8.copies)]
-    durs = np.zeros((args.steps, L8.copies, ng))
-    for _ in range(args.warmup):
-        L8.step(h())
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        L8.step(h(), ev)
-        torch.cuda.synchronize()
-        for r in range(L8.copies):
-            for i in range(ng):
-                durs[s, r, i] = ev[r][i][0].elapsed_time(ev[r][i][1]) * 1e3   # us
-    # average launch: the graph replays the step's launches back to back on
-    # this stream, so step time / launches is the mean duration per launch
-    n_launch = L8.copies * ng
+    # The graph replays the step's launches back to back on this stream, so
+    # step time / launches is the mean duration per launch (gaps included)
+    n_launch = L70.copies * len(L70.shapes)
     mean_us = sec * 1e6 / n_launch
-    eager_mean_us = float(durs.mean())
-    mean_bytes = float(np.mean(L8.bytes))
-    per_proj = {}
-    for i, n in enumerate(L8.names):
-        d = float(durs[:, :, i].mean())
-        per_proj[n] = {"us": round(d, 2), "MB": round(L8.bytes[i] / 1e6, 2),
-                       "GBps": round(L8.bytes[i] / d / 1e3, 1),
-                       "frac_hbm": round(L8.bytes[i] / d / 1e3 / HBM_PEAK_GBS, 3)}
+    mean_bytes = float(np.mean(L70.bytes))
     achieved = mean_bytes / mean_us / 1e3
-    log(f"decode kernel: mean {mean_us:.2f} us/launch in the graph ({eager_mean_us:.2f} between eager events), "
-        f"{achieved:.0f} GB/s; per launch group {per_proj}")
+    extra = {"per_launch_group_m1_graph": per_group, "graph_step_us": round(sec * 1e6, 1),
+             "graph_step_us_p10_p50_p90": step_pct, "library_graph_step_us": round(lib_us, 1),
+             "host_wall_us_per_step": round(wall * 1e6, 1), "layer_MB": round(L70.layer_bytes / 1e6, 1),
+             "mean_bits": round(L70.mean_bits, 3), "device": device_info}
 
-    extra = {"per_launch_group_m1_eager_events": per_proj,
-             "kernel_sum_us_per_step": round(float(durs.sum(axis=(1, 2)).mean()), 1),
-             "graph_step_us": round(sec * 1e6, 1), "graph_step_us_p10_p50_p90": step_pct,
-             "library_graph_step_us": round(lib_graph_us, 1),
-             "host_wall_us_per_step": round(wall * 1e6, 1)}
-
-    extra["device"] = device_info
     if not args.quick:
         # context: a plain device-to-device copy of 1 GiB (read + write bytes)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -334,39 +336,62 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    if "llama3_8b_m8" in want:
-        # ---------------- same layers at M = 8 ----------------
-        L8b = L8.with_batch(8, 8)
-        s8, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)
-        extra["llama3_8b_decode_m8_GBps"] = round(total_bytes / s8 / 1e9, 1)
-        log(f"decode M=8: {total_bytes / s8 / 1e9:.0f} GB/s")
-        del L8b
-
-    if "mixed_vs_uniform" in want:
-        # ------- the same shapes with uniform 3- and 4-bit bitmaps, M = 1 -------
-        # The mixed layers' GB/s against uniform layers' GB/s interpolated to
-        # the same mean bitwidth: the cost of mixing bitwidths in one launch.
-        uni = {}
-        for b in (3, 4):
-            def gen_uniform(i, b=b):
-                p, W, _ = synth.llama3_8b_proj(i)
-                return p, W, synth.uniform_bitmap(p.N, p.K, b)
-            log(f"packing Llama-3-8B-shaped layer with uniform {b}-bit blocks")
-            Lu = DecodeLayerSet(torch, gbb, synth, gen_uniform, LAYER_COPIES_8B, 1, dev)
-            su, _, _ = time_graph(torch, lambda: Lu.step(h()), args.steps, args.warmup)
-            uni[b] = Lu.layer_bytes * Lu.copies / su / 1e9
-            log(f"uniform {b}-bit decode M=1: {uni[b]:.0f} GB/s")
-            del Lu
-            torch.cuda.empty_cache()
-        ref = uni[3] + (L8.mean_bits - 3.0) * (uni[4] - uni[3])
-        extra["mixed_vs_uniform_8b_m1"] = {
-            "uniform3_GBps": round(uni[3], 1), "uniform4_GBps": round(uni[4], 1),
-            "mixed_GBps": round(value, 1), "mixed_mean_bits": round(L8.mean_bits, 3),
-            "mixed_over_uniform_at_same_bits": round(value / ref, 3)}
-        log(f"mixed / uniform at {L8.mean_bits:.2f} bits: {value / ref:.3f}")
-
-    del L8
+    if "llama3_70b_batch" in want:
+        # ---------------- the same 70B layers at M = 8 and 32 ----------------
+        for M in (8, 32):
+            Lm = L70.with_batch(M, M)
+            sm, _, _ = time_graph(torch, lambda: Lm.step(h()), max(10, args.steps // 2), args.warmup)
+            extra[f"llama3_70b_decode_m{M}_GBps"] = round(total_bytes / sm / 1e9, 1)
+            log(f"70B decode M={M}: {total_bytes / sm / 1e9:.0f} GB/s")
+            del Lm
+    host70 = L70.host
+    del L70
     torch.cuda.empty_cache()
+
+    if "llama3_8b" in want:
+        # ---------------- Llama-3-8B layers, decode M = 1 and 8 ----------------
+        log("packing Llama-3-8B-shaped layer (qkv, o, gate_up, down)")
+        L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
+        b8 = L8.layer_bytes * L8.copies
+        s8, _, _ = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
+        v8 = b8 / s8 / 1e9
+        e8 = {"GBps": round(v8, 1), "frac_hbm": round(v8 / HBM_PEAK_GBS, 3), "graph_step_us": round(s8 * 1e6, 1),
+              "layers_per_step": L8.copies, "layer_MB": round(L8.layer_bytes / 1e6, 1),
+              "mean_bits": round(L8.mean_bits, 3),
+              "per_launch_group_m1_graph": group_graph_times(torch, L8, args.steps, args.warmup, h),
+              "library_graph_step_us": round(library_graph_us(torch, gbb, L8, args.steps, args.warmup), 1)}
+        log(f"8B decode M=1: {v8:.0f} GB/s; per group {e8['per_launch_group_m1_graph']}")
+        L8b = L8.with_batch(8, 8)
+        s8b, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)
+        e8["decode_m8_GBps"] = round(b8 / s8b / 1e9, 1)
+        log(f"8B decode M=8: {b8 / s8b / 1e9:.0f} GB/s")
+        del L8b
+        extra["llama3_8b_layer_m1"] = e8
+
+        if "mixed_vs_uniform" in want:
+            # ------- the same shapes with uniform 3- and 4-bit bitmaps, M = 1 -------
+            # The mixed layers' GB/s against uniform layers' GB/s interpolated to
+            # the same mean bitwidth: the cost of mixing bitwidths in one launch.
+            uni = {}
+            for b in (3, 4):
+                def gen_uniform(i, b=b):
+                    p, W, _ = synth.llama3_8b_proj(i)
+                    return p, W, synth.uniform_bitmap(p.N, p.K, b)
+                log(f"packing Llama-3-8B-shaped layer with uniform {b}-bit blocks")
+                Lu = DecodeLayerSet(torch, gbb, synth, gen_uniform, LAYER_COPIES_8B, 1, dev)
+                su, _, _ = time_graph(torch, lambda: Lu.step(h()), args.steps, args.warmup)
+                uni[b] = Lu.layer_bytes * Lu.copies / su / 1e9
+                log(f"uniform {b}-bit decode M=1: {uni[b]:.0f} GB/s")
+                del Lu
+                torch.cuda.empty_cache()
+            ref = uni[3] + (L8.mean_bits - 3.0) * (uni[4] - uni[3])
+            extra["mixed_vs_uniform_8b_m1"] = {
+                "uniform3_GBps": round(uni[3], 1), "uniform4_GBps": round(uni[4], 1),
+                "mixed_GBps": round(v8, 1), "mixed_mean_bits": round(L8.mean_bits, 3),
+                "mixed_over_uniform_at_same_bits": round(v8 / ref, 3)}
+            log(f"mixed / uniform at {L8.mean_bits:.2f} bits: {v8 / ref:.3f}")
+        del L8
+        torch.cuda.empty_cache()
 
     if "linear_4096" in want:
         # ---------------- one 4096 x 4096 matrix, M = 1 ----------------
@@ -392,24 +417,7 @@ def main():
         del lin, d
         torch.cuda.empty_cache()
 
-    if "llama3_70b" in want:
-        # ---------------- Llama-3-70B layer, decode M = 1 ----------------
-        log("packing Llama-3-70B-shaped layer")
-        L70 = DecodeLayerSet(torch, gbb, synth, synth.llama3_70b_proj, LAYER_COPIES_70B, 1, dev)
-        s70, _, _ = time_graph(torch, lambda: L70.step(h()), max(10, args.steps // 2), args.warmup)
-        b70 = L70.layer_bytes * L70.copies
-        extra["llama3_70b_decode_m1_GBps"] = round(b70 / s70 / 1e9, 1)
-        extra["llama3_70b_layer_MB"] = round(L70.layer_bytes / 1e6, 1)
-        log(f"70B decode M=1: {b70 / s70 / 1e9:.0f} GB/s")
-        for M in (8, 32):
-            Lm = L70.with_batch(M, M)
-            sm, _, _ = time_graph(torch, lambda: Lm.step(h()), max(10, args.steps // 2), args.warmup)
-            extra[f"llama3_70b_decode_m{M}_GBps"] = round(b70 / sm / 1e9, 1)
-            log(f"70B decode M={M}: {b70 / sm / 1e9:.0f} GB/s")
-            del Lm
-        del L70
-        torch.cuda.empty_cache()
-
+    roof2048 = None
     if "prefill" in want:
         # ---------------- prefill M = 2048 on the 70B MLP ----------------
         pre = {}
@@ -449,6 +457,13 @@ def main():
             del imgd, x, y, w16
             torch.cuda.empty_cache()
         extra["prefill_m2048_70b_mlp"] = pre
+        fl_all = sum(2.0 * 2048 * v["N"] * v["K"] for v in pre.values())
+        ms_all = sum(v["ms"] for v in pre.values())
+        roof2048 = {"bound": "mfma", "achieved": round(fl_all / (ms_all * 1e-3) / 1e12, 1), "peak": FP16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(fl_all / (ms_all * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 3),
+                    "traffic": None, "kernel": "prefill_kernel",
+                    "workload": "M=2048 x Llama-3-70B MLP (28672x8192 gate and 8192x28672 down), 2*M*N*K flops "
+                                "over both launches"}
 
     if "w44a8" in want:
         # ---------------- W4.4A8 28672 x 8192 ----------------
@@ -478,8 +493,8 @@ def main():
 
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
-        cpu = cpu_baseline(gbb, synth)
-        extra["cpu_baseline_one_thread_o_proj_GBps"] = cpu_baseline_one_thread(gbb, synth)
+        cpu = cpu_baseline(host70)
+        extra["cpu_baseline_one_thread_o_proj_GBps"] = cpu_baseline_one_thread(host70)
 
     out = {
         "metric": "fused dequant-GEMM: weight GB/s (%HBM peak) at M=1; TFLOP/s (%MFMA) at M=2048",
@@ -493,39 +508,37 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
-        "data": "synthetic (seeded random weights and activations of Llama-3 layer shapes)",
-        "config": {"workload": "llama3_8b_layer_decode_m1", "layers_per_step": LAYER_COPIES_8B,
+        "data": "synthetic (seeded random weights and activations of Llama-3-70B layer shapes)",
+        "config": {"workload": "llama3_70b_layer_decode_m1", "layers_per_step": LAYER_COPIES_70B,
                    "projections": "q,k,v,o,gate,up,down", "launches_per_layer": "qkv,o,gate_up,down",
-                   "M": 1, "block": "64x128",
-                   "bits": "{1,2,3,4,6,8} mean 3.10", "group": 128,
+                   "M": 1, "block": "64x128", "bits": "{1,2,3,4,6,8} mean 2.10", "group": 128,
                    "weight_MB_per_step": round(total_bytes / 1e6, 1), "parallelism": "single GPU"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 3), "traffic": measured_traffic(),
                      "kernel": "decode1_kernel<4>", "mean_launch_us": round(mean_us, 3),
                      "mean_algorithmic_bytes_per_launch": round(mean_bytes)},
+        "roofline_m2048": roof2048,
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(gbb, synth):
+def cpu_baseline(host):
     """The oracle as it stands -- its own unpacker, exact fp32 dequant and an
-    fp64 product -- over one copy of the headline layer (7 projections, M=1)."""
+    fp64 product -- over one copy of the headline layer (its four packed
+    launch groups, M = 1), on the host's cores."""
     from threadpoolctl import threadpool_info
 
     from oracle import blockquant as bq
     from oracle import image as oimg
 
-    log("cpu baseline: oracle over one Llama-3-8B-shaped layer at M=1")
+    log("cpu baseline: oracle over one Llama-3-70B-shaped layer at M=1")
     total_bytes = 0
     t = 0.0
-    for i in range(7):
-        p, W, bits = synth.llama3_8b_proj(i)
-        img, _, _ = gbb.pack_blocks(W, bits)
-        del W
-        x = np.random.default_rng(7).standard_normal((1, p.K)).astype(np.float16)
+    for (name, (N, K), img, bits) in host:
+        x = np.random.default_rng(7).standard_normal((1, K)).astype(np.float16)
         t0 = time.perf_counter()
         d = oimg.read_block_image(img)
         w = bq.dequant_fp32(d["q"], d["s16"], d["z16"])
@@ -535,11 +548,11 @@ def cpu_baseline(gbb, synth):
         del d, w
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
     return {"value": round(total_bytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one layer copy (7 projections, {total_bytes / 1e6:.1f} MB packed) at M=1: oracle unpack + "
-                      f"fp32 dequant + fp64 GEMV, {t:.1f} s"}
+            "sample": f"one copy of the headline layer (q|k|v, o, gate|up, down; {total_bytes / 1e6:.1f} MB "
+                      f"packed) at M=1: oracle unpack + fp32 dequant + fp64 GEMV, {t:.1f} s"}
 
 
-def cpu_baseline_one_thread(gbb, synth):
+def cpu_baseline_one_thread(host):
     """The same oracle on one thread (BLAS limited to one), over the o
     projection only, for context next to the multi-thread figure."""
     from threadpoolctl import threadpool_limits
@@ -547,10 +560,8 @@ def cpu_baseline_one_thread(gbb, synth):
     from oracle import blockquant as bq
     from oracle import image as oimg
 
-    p, W, bits = synth.llama3_8b_proj(3)
-    img, _, _ = gbb.pack_blocks(W, bits)
-    del W
-    x = np.random.default_rng(7).standard_normal((1, p.K)).astype(np.float16)
+    name, (N, K), img, bits = [hh for hh in host if hh[0] == "o"][0]
+    x = np.random.default_rng(7).standard_normal((1, K)).astype(np.float16)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         d = oimg.read_block_image(img)

@@ -13,7 +13,7 @@ def run(*args):
 
 
 def test_unknown_extra_is_rejected():
-    r = run("--extras", "llama3_70b,nonsense")
+    r = run("--extras", "llama3_70b_batch,nonsense")
     assert r.returncode == 2 and "nonsense" in r.stdout
 
 
