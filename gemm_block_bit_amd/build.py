@@ -33,7 +33,10 @@ HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip", "noalloc.hip
 # code right away, so it keeps them in VGPRs rather than accumulation
 # registers; its single-token kernel takes its arguments preloaded into
 # scalar registers
-HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
+             # the W4.4A8 kernels scale their int32 MFMA results with VALU code
+             # right away too, so they also keep them in VGPRs
+             "w48.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["pack.cpp", "api.cpp"]
 
 

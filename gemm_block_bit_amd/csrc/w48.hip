@@ -251,25 +251,42 @@ __global__ __launch_bounds__(256) void w48_kernel(W48Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large batches: 128 tokens x 128 packed rows per workgroup.  Workgroups are
-// homogeneous: the first ceil(T8 / 8) row blocks hold 8-bit tiles, the rest
-// 4-bit tiles.  Per 128-column group everything the matrix cores read is
-// brought into LDS by global->LDS loads in MFMA fragment order -- activation
-// fragments gathered 16 tokens at a time, weight fragments as packed, the
-// group's weight scales and zero points -- so operand reads are conflict-free
-// lane-linear reads and no staging registers are needed.  4-bit fragments
-// land raw (512 B) and each wave expands the ones it multiplies into int8
-// (q - z) in registers right before its MFMAs.  LDS is double-buffered: the
-// next group's loads fly while the current group runs; one wait and one
-// barrier per group.  Wave (wm, wn) owns tokens 64 wm + [0, 64) and rows
-// 64 wn + [0, 64): 4 x 4 MFMA tiles, two k halves per group.
+// Large batches: tiles of 128 tokens x 128 packed 4-bit rows or 128 tokens x
+// 64 packed 8-bit rows per workgroup, one row set per workgroup.  Wave w
+// owns NJ packed row tiles (two 4-bit tiles or one 8-bit tile) for all eight
+// 16-token tiles, so each weight fragment is read and, for 4-bit rows,
+// expanded to int8 (q - z) by one wave only, and its expansion serves eight
+// MFMAs.  Per 128-column group everything the matrix cores read reaches LDS
+// by global->LDS loads in MFMA fragment order: the activation fragments (16
+// tokens x 64 columns each, shared by the four waves), each wave's own weight
+// fragments, scales and zero points, so no staging registers are needed and
+// every operand read is a lane-linear LDS read.  Groups flow through two LDS
+// stages: the next group's loads fly while the current group runs; one fixed
+// vmcnt wait and one barrier per group.  Either tile takes 52 KiB, so three
+// workgroups share a CU.  Each token tile's int32 sums are scaled into fp32
+// while the next tile's MFMAs run.  Workgroups are dealt to the XCDs in
+// contiguous stretches of a grouped tile order, so the tiles in flight on an
+// XCD share their activation and weight tiles in its L2.
 // ---------------------------------------------------------------------------
-constexpr int kTB = 128;   // tokens and packed rows per workgroup
+constexpr int kTB = 128;   // tokens per workgroup
 
-// LDS map (bytes): A[2] 16 KiB each, B[2] 16 KiB each (8-bit fragments, or
-// the raw 4-bit fragments in the first 8 KiB), weight scales[2] 256 B each,
-// zero points[2] 256 B each
-constexpr int kLdsA = 0, kLdsB = 32768, kLdsS = 65536, kLdsZ = 66048, kLdsW48 = 66560;
+template <bool Q4>
+struct TileCfg {
+  static constexpr int NJ = Q4 ? 2 : 1;             // packed row tiles per wave
+  static constexpr int kRows = 64 * NJ;             // packed rows per workgroup
+  static constexpr int kStages = 2;
+  static constexpr int kA = 16 * 1024;              // activation fragments (8 token tiles x 2 k halves)
+  static constexpr int kBw = 2048;                  // weight fragments of one wave (NJ tiles x 2 halves)
+  static constexpr int kB = 4 * kBw;
+  static constexpr int kS = 4 * 256;                // weight scales, 256 B per wave
+  static constexpr int kZ = Q4 ? 4 * 256 : 0;       // zero points, 256 B per wave
+  static constexpr int kStage = kA + kB + kS + kZ;
+  // global->LDS loads per wave per group: 4 activation, 2 weight, scales, zero points
+  static constexpr int kLoads = 4 + 2 + 1 + (Q4 ? 1 : 0);
+};
+constexpr int kTileLds = TileCfg<true>::kStages * TileCfg<true>::kStage;
+static_assert(TileCfg<false>::kStages * TileCfg<false>::kStage <= kTileLds, "one LDS size serves both");
+static_assert(3 * kTileLds <= 160 * 1024, "three workgroups per CU");
 
 // global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
 // LDS address lds + 16 l (4 l).  No output registers: completion is waited
@@ -290,169 +307,195 @@ __device__ __forceinline__ void gdma4_once(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
 
-// GA: activation scales per (token, group), else per token.  ACC: store the
-// exact int32 group sums to a.acc_out instead of scaling them (the integer
-// step of this kernel, checked bit for bit).
-template <bool GA, bool ACC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void w48_tile_kernel(W48Args a) {
-  __shared__ u32x4 lds[kLdsW48 / 16];
-  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
-  const uint32_t lbase = lds_u32(lds);
+// One workgroup's tile: tokens m0 ... m0 + 127, packed tiles t0 ... t0 +
+// 4 NJ - 1 of one row set.  Q4: the row set (4-bit or 8-bit rows).  GA:
+// activation scales per (token, group), else per token.  ACC: store the exact
+// int32 group sums to a.acc_out instead of scaling them (the integer step of
+// this kernel, checked bit for bit).
+template <bool Q4, bool GA, bool ACC>
+__device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m0, int t0) {
+  using C = TileCfg<Q4>;
+  constexpr int S = C::kStages, NJ = C::NJ;
+  const uint32_t lbase = lds_u32(base);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * kTB;
-  const int nb8 = (a.T8 + 7) / 8;
-  const bool q4 = int(blockIdx.y) >= nb8;
-  // first packed tile of this workgroup and the end of its row set
-  const int t0 = q4 ? a.T8 + (int(blockIdx.y) - nb8) * 8 : int(blockIdx.y) * 8;
-  const int tend = q4 ? a.T8 + a.T4 : a.T8;
+  const int tend = Q4 ? a.T8 + a.T4 : a.T8;   // end of this row set's packed tiles
+  const int tw = t0 + NJ * wave;              // this wave's first packed tile
   const int G = a.K / 128, KT = a.K / 64;
 
-  // Loads of one group into buffer `buf`.  Wave w brings activation
-  // fragments f = w + 4 q (token tile f / 2, k half f % 2) and weight
-  // fragments f (row tile f / 2, k tile 2 grp + f % 2); wave 0 the scales,
-  // wave 1 the zero points.  Tokens and tiles past the end are clamped to the
-  // last valid one (read, then discarded).
-  auto issue = [&](int grp, int buf) {
+  // Loads of group grp into its stage.  Tokens and tiles past the end are
+  // clamped to the last valid one (read, then discarded).
+  auto issue = [&](int grp) {
+    const uint32_t sb = lbase + uint32_t((grp % S) * C::kStage);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q) {   // activation fragment f: token tile f / 2, k half f % 2
       const int f = wave + 4 * q, i = f >> 1, h = f & 1;
       const int m = min(m0 + 16 * i + r16, a.M - 1);
-      gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g,
-             lbase + kLdsA + buf * 16384 + f * 1024);
-      const int t = min(t0 + i, tend - 1), kt = 2 * grp + h;
-      if (!q4) {
-        gdma16(a.c8 + (size_t(t) * KT + kt) * 1024 + 16 * lane, lbase + kLdsB + buf * 16384 + f * 1024);
-      } else {
-        const uint8_t* src = a.c4 + (size_t(t - a.T8) * KT + kt) * 512;
-        gdma4(src + 4 * lane, lbase + kLdsB + buf * 16384 + f * 512);
-        gdma4(src + 256 + 4 * lane, lbase + kLdsB + buf * 16384 + f * 512 + 256);
+      gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g, sb + f * 1024);
+    }
+    const uint32_t bb = sb + C::kA + wave * C::kBw;
+    if constexpr (!Q4) {   // one 8-bit tile: two 1 KiB fragments
+      const int tt = min(tw, tend - 1);
+      gdma16(a.c8 + (size_t(tt) * KT + 2 * grp) * 1024 + 16 * lane, bb);
+      gdma16(a.c8 + (size_t(tt) * KT + 2 * grp + 1) * 1024 + 16 * lane, bb + 1024);
+    } else {   // two 4-bit tiles: each group's two 512-byte fragments are one contiguous KiB
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tt = min(tw + j, tend - 1);
+        gdma16(a.c4 + (size_t(tt - a.T8) * KT + 2 * grp) * 512 + 16 * lane, bb + j * 1024);
       }
     }
-    if (wave == 0) {
-      const int t = min(t0 + (lane >> 3), tend - 1);
-      gdma4(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), lbase + kLdsS + buf * 256);
-    } else if (wave == 1 && q4) {
-      const int t = min(t0 + ((lane & 31) >> 2), tend - 1);
-      gdma4(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), lbase + kLdsZ + buf * 256);
+    {   // scales: lanes 8 j + 0..7 bring tile j's 16 (the other lanes repeat them)
+      const int tt = min(tw + ((lane >> 3) & (NJ - 1)), tend - 1);
+      gdma4(a.s + (size_t(tt) * G + grp) * 16 + 2 * (lane & 7), sb + C::kA + C::kB + wave * 256);
+    }
+    if constexpr (Q4) {   // zero points: lanes 4 j + 0..3 bring tile j's 16
+      const int tt = min(tw + ((lane >> 2) & 1), tend - 1);
+      gdma4(a.z + (size_t(tt - a.T8) * G + grp) * 16 + 4 * (lane & 3), sb + C::kA + C::kB + C::kS + wave * 256);
     }
   };
 
-  f32x4 tot[4][4];
+  f32x4 tot[8][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < NJ; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
-  __syncthreads();
+  issue(0);
   for (int grp = 0; grp < G; ++grp) {
-    const int buf = grp & 1;
-    if (grp + 1 < G) issue(grp + 1, buf ^ 1);
-    const uint8_t* A = base + kLdsA + buf * 16384;
-    const uint8_t* B = base + kLdsB + buf * 16384;
-    const _Float16* S = reinterpret_cast<const _Float16*>(base + kLdsS + buf * 256);
-    i32x4 c[4][4];
+    wait_vm<0>();      // this wave's loads of group grp have landed
+    __syncthreads();   // everyone's have; every wave is done with grp - 1's stage
+    if (grp + 1 < G) issue(grp + 1);   // into grp - 1's stage
+    const uint8_t* st = base + (grp % S) * C::kStage;
+    const uint8_t* B = st + C::kA + wave * C::kBw;
+    const _Float16* Sv = reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256);
+    float sw[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NJ; ++j) sw[j] = (float)Sv[16 * j + r16];
+    uint32_t zb[NJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < NJ; ++j)
+      zb[j] = Q4 ? (128u - st[C::kA + C::kB + C::kS + wave * 256 + 16 * j + r16]) * 0x01010101u : 0u;
+    auto bfrag = [&](int h, int j) -> i32x4 {
+      if constexpr (Q4)
+        return expand4(*reinterpret_cast<const uint2*>(B + j * 1024 + h * 512 + 8 * lane), zb[j]);
+      else
+        return *reinterpret_cast<const i32x4*>(B + h * 1024 + 16 * lane);
+    };
+    auto afrag = [&](int i, int h) -> i32x4 {
+      return *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
+    };
+    // step two for token tile i: the exact sums into fp32, scaled (or stored)
+    auto finish = [&](int i, const i32x4 (&ci)[NJ]) {
+      if constexpr (ACC) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      i32x4 av[4], bv[4];
+        for (int j = 0; j < NJ; ++j) {
+          const int tt = tw + j;
+          const int n = tt < tend ? a.rows[16 * tt + r16] : -1;
+          if (n < 0) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = *reinterpret_cast<const i32x4*>(A + (2 * (4 * wm + i) + h) * 1024 + 16 * lane);
-      if (q4) {
+          for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 16 * i + 4 * g + v;
+            if (m < a.M) a.acc_out[(size_t(m) * a.N + n) * G + grp] = ci[j][v];
+          }
+        }
+      } else if constexpr (GA) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int f = 2 * (4 * wn + j) + h;
-          const uint2 w = *reinterpret_cast<const uint2*>(B + f * 512 + 8 * lane);
-          const uint32_t z = base[kLdsZ + buf * 256 + 16 * (4 * wn + j) + r16];
-          bv[j] = expand4(w, (128u - z) * 0x01010101u);
+        for (int v = 0; v < 4; ++v) {
+          const float sa = (float)a.xs[size_t(min(m0 + 16 * i + 4 * g + v, a.M - 1)) * G + grp];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) tot[i][j][v] = __builtin_fmaf(float(ci[j][v]), sw[j] * sa, tot[i][j][v]);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bv[j] = *reinterpret_cast<const i32x4*>(B + (2 * (4 * wn + j) + h) * 1024 + 16 * lane);
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) tot[i][j][v] = __builtin_fmaf(float(ci[j][v]), sw[j], tot[i][j][v]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c[i][j] = mfma16_i8(av[i], bv[j], c[i][j]);
-    }
-    if constexpr (ACC) {
-      // the group sums as they are, at their original rows
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * wn + j;
-        const int n = t < tend ? a.rows[16 * t + r16] : -1;
-        if (n < 0) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
-            if (m < a.M) a.acc_out[(size_t(m) * a.N + n) * G + grp] = c[i][j][v];
-          }
-      }
-    } else {
-    // step two: scale the exact group sums into the fp32 accumulators
-    float sw[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sw[j] = (float)S[(4 * wn + j) * 16 + r16];
-    if constexpr (GA) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = min(m0 + 64 * wm + 16 * i + 4 * g + v, a.M - 1);
-          const float sa = (float)a.xs[size_t(m) * G + grp];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) tot[i][j][v] = __builtin_fmaf(float(c[i][j][v]), sw[j] * sa, tot[i][j][v]);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) tot[i][j][v] = __builtin_fmaf(float(c[i][j][v]), sw[j], tot[i][j][v]);
-    }
-    }
-    if (grp + 1 < G) {
-      // the next group's loads have landed (this wave's), then everyone's;
-      // the barrier also retires this group's reads of `buf`
-      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-      __syncthreads();
-    }
-  }
+    };
 
+    // every LDS read of the group first; then the first k half's MFMAs, and
+    // the second half token tile by token tile, each tile's sums scaled while
+    // the next tile's MFMAs run
+    i32x4 av0[8], av1[8], b0[NJ], b1[NJ];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) av0[i] = afrag(i, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b0[j] = bfrag(0, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) av1[i] = afrag(i, 1);
+    i32x4 c[8][NJ];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av0[i], b0[j], i32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b1[j] = bfrag(1, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av1[i], b1[j], c[i][j]);
+      if (i > 0) finish(i - 1, c[i - 1]);
+    }
+    finish(7, c[7]);
+  }
   if constexpr (ACC) return;
+
   // per-token scale, fused scatter to the original rows
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + 4 * wn + j;
-    if (t >= tend) continue;
-    const int n = a.rows[16 * t + r16];
+  for (int j = 0; j < NJ; ++j) {
+    const int tt = tw + j;
+    if (tt >= tend) continue;
+    const int n = a.rows[16 * tt + r16];
     if (n < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
+        const int m = m0 + 16 * i + 4 * g + v;
         if (m >= a.M) continue;
         const float sa = GA ? 1.0f : (float)a.xs[m];
         a.y[size_t(m) * a.N + n] = (_Float16)(tot[i][j][v] * sa);
       }
   }
+}
+
+// Tile order: ntm token tiles x (nrb8 8-bit + nrb4 4-bit) row blocks (8-bit
+// row blocks first), walked in groups of kGroupRows row blocks: within a
+// group the row blocks vary fastest, so the workgroups in flight on an XCD
+// share both their activation and their weight tiles in its L2.
+constexpr int kGroupRows = 8;
+
+// per_xcd tiles of that order per XCD.
+template <bool GA, bool ACC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ? 2 : 3))) void w48_tile_kernel(
+    W48Args a, int ntm, int nrb8, int nrb4, int per_xcd) {
+  __shared__ u32x4 lds[kTileLds / 16];
+  // workgroup i runs on XCD i % 8, which owns tiles [x per_xcd, (x + 1) per_xcd)
+  const int bid = int(blockIdx.x);
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  const int nrb = nrb8 + nrb4;
+  if (t >= ntm * nrb) return;
+  const int q = t / (kGroupRows * ntm), r = t - q * (kGroupRows * ntm);
+  const int gr = min(kGroupRows, nrb - q * kGroupRows);   // row blocks in this group
+  const int tm = r / gr, rb = q * kGroupRows + (r - tm * gr);
+  uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
+  if (rb < nrb8)
+    tile_body<false, GA, ACC>(a, base, tm * kTB, rb * 4);
+  else
+    tile_body<true, GA, ACC>(a, base, tm * kTB, a.T8 + (rb - nrb8) * 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -480,13 +523,6 @@ struct StreamCfg {
   static constexpr int kLoads8 = NA + 3;                // loads per wave per group, 8-bit rows
   static constexpr int kLoads4 = NA + 3;                // 4-bit rows
 };
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.  ACC:
 // store each group's exact int32 sums to a.acc_out instead of scaling them.
@@ -671,12 +707,13 @@ void launch_stream(const W48Args& a, hipStream_t s) {
 
 template <bool ACC>
 void launch_tile(const W48Args& a, hipStream_t s) {
-  const unsigned by = unsigned((a.T8 + 7) / 8 + (a.T4 + 7) / 8);
-  const dim3 grid(unsigned((a.M + kTB - 1) / kTB), by);
+  const int ntm = (a.M + kTB - 1) / kTB, nrb8 = (a.T8 + 3) / 4, nrb4 = (a.T4 + 7) / 8;
+  const int per_xcd = (ntm * (nrb8 + nrb4) + 7) / 8;
+  const dim3 grid(unsigned(8 * per_xcd));
   if (a.ga == 128)
-    hipLaunchKernelGGL((w48_tile_kernel<true, ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w48_tile_kernel<true, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   else
-    hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
 }
 
 // Picks the kernel for (M, ga).  A call with a.acc_out set takes the same
@@ -687,7 +724,7 @@ int launch(const W48Args& a, void* stream) {
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool acc = a.acc_out != nullptr;
-  const int tile_rows = (a.T8 + 7) / 8 + (a.T4 + 7) / 8;   // 128-row workgroups of the tile kernel
+  const int tile_rows = (a.T8 + 3) / 4 + (a.T4 + 7) / 8;   // row blocks of the tile kernel
   if (a.M > 64 && a.M <= 128 && a.ga != 128 && tile_rows <= device_compute_units()) {
     // Neither kernel splits K.  Here the tile kernel's single row of
     // workgroups leaves CUs idle while each walks all of K, so two 64-token
