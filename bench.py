@@ -242,6 +242,19 @@ def library_graph_us(torch, gbb, L, steps, warmup):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+def grouped_step(torch, gbb, L, steps, warmup):
+    """The step's products as independent problems in ONE grouped launch
+    (gbb_gemm_mixed_w_batched; every product gets its own output): weight
+    GB/s of a graph replaying it.  This ignores the dependencies between a
+    layer's products, so it is a measure of the grouped launch, not of a
+    decoder step."""
+    ys = [torch.empty((L.M, N), dtype=torch.float16, device=L.x[i].device) for _, i, N, _ in L.launches()]
+    b = gbb.Batched([(L.images[r][i], N, K, L.x[i], y) for (r, i, N, K), y in zip(L.launches(), ys)])
+    sec, _, g = time_graph(torch, b.launch, steps, warmup)
+    del g
+    return L.layer_bytes * L.copies / sec / 1e9, sec * 1e6
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +319,8 @@ def main():
     log(f"per launch group: {per_group}")
     lib_us = library_graph_us(torch, gbb, L70, args.steps, args.warmup)
     log(f"the same step as one library graph: {lib_us:.1f} us")
+    grp_gbs, grp_us = grouped_step(torch, gbb, L70, args.steps, args.warmup)
+    log(f"the step's 12 products as one grouped launch (independent): {grp_us:.1f} us, {grp_gbs:.0f} GB/s")
 
     # The graph replays the step's launches back to back on this stream, so
     # step time / launches is the mean duration per launch (gaps included)
@@ -315,6 +330,8 @@ def main():
     achieved = mean_bytes / mean_us / 1e3
     extra = {"per_launch_group_m1_graph": per_group, "graph_step_us": round(sec * 1e6, 1),
              "graph_step_us_p10_p50_p90": step_pct, "library_graph_step_us": round(lib_us, 1),
+             "grouped_launch_independent_products": {"us": round(grp_us, 1), "GBps": round(grp_gbs, 1),
+                                                     "frac_hbm": round(grp_gbs / HBM_PEAK_GBS, 3)},
              "host_wall_us_per_step": round(wall * 1e6, 1), "layer_MB": round(L70.layer_bytes / 1e6, 1),
              "mean_bits": round(L70.mean_bits, 3), "device": device_info}
 
@@ -360,6 +377,10 @@ def main():
               "mean_bits": round(L8.mean_bits, 3),
               "per_launch_group_m1_graph": group_graph_times(torch, L8, args.steps, args.warmup, h),
               "library_graph_step_us": round(library_graph_us(torch, gbb, L8, args.steps, args.warmup), 1)}
+        g8, g8us = grouped_step(torch, gbb, L8, args.steps, args.warmup)
+        e8["grouped_launch_independent_products"] = {"us": round(g8us, 1), "GBps": round(g8, 1),
+                                                     "frac_hbm": round(g8 / HBM_PEAK_GBS, 3)}
+        log(f"8B: the step's 32 products as one grouped launch: {g8us:.1f} us, {g8:.0f} GB/s")
         log(f"8B decode M=1: {v8:.0f} GB/s; per group {e8['per_launch_group_m1_graph']}")
         L8b = L8.with_batch(8, 8)
         s8b, _, _ = time_graph(torch, lambda: L8b.step(h()), args.steps, args.warmup)

@@ -7,6 +7,7 @@ packer, torch tensors for device memory and the current HIP stream.  There is
 no CPU fallback -- if the library is missing every call raises.
 """
 from .binding import (  # noqa: F401
+    Batched,
     GbbError,
     Graph,
     allocate_bits,
@@ -14,6 +15,7 @@ from .binding import (  # noqa: F401
     check_image,
     dequant,
     gemm_mixed_w,
+    gemm_mixed_w_batched_workspace,
     gemm_mixed_w_noalloc,
     gemm_mixed_w_path,
     gemm_mixed_w_workspace,

@@ -43,6 +43,8 @@ _SIGS = {
     "gbb_gemm_mixed_w": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_gemm_mixed_w_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
     "gbb_gemm_mixed_w_noalloc": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp]),
+    "gbb_gemm_mixed_w_batched_workspace": (_sz, [_i, _vp, _vp, _i]),
+    "gbb_gemm_mixed_w_batched": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_graph_create": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_graph_launch": (_i, [_vp, _vp]),
     "gbb_graph_destroy": (_i, [_vp]),
@@ -264,6 +266,46 @@ def gemm_mixed_w_noalloc(image, N: int, K: int, x, out=None):
         _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),
         _dev_ptr(y, torch.float16, "y"), M, _stream(x)))
     return y
+
+
+def gemm_mixed_w_batched_workspace(shapes, M: int) -> int:
+    n = len(shapes)
+    Ns = (ctypes.c_int * n)(*[int(N) for N, _ in shapes])
+    Ks = (ctypes.c_int * n)(*[int(K) for _, K in shapes])
+    return lib().gbb_gemm_mixed_w_batched_workspace(n, Ns, Ks, M)
+
+
+class Batched:
+    """Independent products (image, N, K, x, y) with one M, run by
+    gbb_gemm_mixed_w_batched: one launch for M <= 16.  The pointer arrays are
+    built once; launch() enqueues on torch's current stream."""
+
+    def __init__(self, calls, workspace=None):
+        torch = _torch()
+        if not calls:
+            raise ValueError("no calls")
+        M = calls[0][3].shape[0]
+        for (img, N, K, x, y) in calls:
+            if x.dim() != 2 or tuple(x.shape) != (M, K) or tuple(y.shape) != (M, N):
+                raise ValueError(f"x must be [{M}][{K}] and y [{M}][{N}]")
+        n = len(calls)
+        self.M, self.n = M, n
+        self._images = (ctypes.c_void_p * n)(*[_dev_ptr(c[0], torch.uint8, "image") for c in calls])
+        self._N = (ctypes.c_int * n)(*[c[1] for c in calls])
+        self._K = (ctypes.c_int * n)(*[c[2] for c in calls])
+        self._x = (ctypes.c_void_p * n)(*[_dev_ptr(c[3], torch.float16, "x") for c in calls])
+        self._y = (ctypes.c_void_p * n)(*[_dev_ptr(c[4], torch.float16, "y") for c in calls])
+        need = lib().gbb_gemm_mixed_w_batched_workspace(n, self._N, self._K, M)
+        dev = calls[0][3].device
+        self._ws = workspace if workspace is not None else torch.zeros(max(need, 256), dtype=torch.uint8,
+                                                                       device=dev)
+        self._calls = list(calls)
+
+    def launch(self):
+        torch = _torch()
+        _check(lib().gbb_gemm_mixed_w_batched(self.n, self._images, self._N, self._K, self._x, self._y, self.M,
+                                              self._ws.data_ptr(), self._ws.numel(),
+                                              torch.cuda.current_stream(self._ws.device).cuda_stream))
 
 
 class Graph:

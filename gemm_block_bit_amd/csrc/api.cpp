@@ -206,3 +206,61 @@ extern "C" gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8,
   if (!aligned16(xq)) return fail(GBB_E_ALIGN, "xq must be 16-byte aligned");
   return device_status(launch_w48_acc(w48_view(image, N, K, n8), xq, ga, acc, M, stream), "w48 acc launch");
 }
+
+namespace {
+
+// Workspace bytes of problem i of a grouped call (each region 256-aligned).
+size_t batch_ws_one(int N, int K, int M) {
+  const size_t w = M <= 16 ? decode_plan(N, K, M).ws_bytes : gbb_gemm_mixed_w_workspace(N, K, M);
+  return (w + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+extern "C" size_t gbb_gemm_mixed_w_batched_workspace(int n, const int* N, const int* K, int M) {
+  if (n < 1 || n > kMaxBatch || !N || !K || M <= 0) return 0;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (N[i] <= 0 || K[i] <= 0 || N[i] % kBlockRows || K[i] % kGroup) return 0;
+    total += batch_ws_one(N[i], K[i], M);
+  }
+  return total;
+}
+
+extern "C" gbb_status gbb_gemm_mixed_w_batched(int n, const void* const* images, const int* N, const int* K,
+                                               const uint16_t* const* x, uint16_t* const* y, int M, void* workspace,
+                                               size_t ws_bytes, void* stream) {
+  if (n < 1 || n > kMaxBatch) return fail(GBB_E_ARG, "n must be in 1 ... %d (n=%d)", kMaxBatch, n);
+  if (!images || !N || !K || !x || !y) return fail(GBB_E_ARG, "images, N, K, x and y must not be NULL");
+  for (int i = 0; i < n; ++i) {
+    const gbb_status st = check_gemm_args(images[i], N[i], K[i], x[i], y[i], M, 0);
+    if (st != GBB_OK) return fail(st, "problem %d: %s", i, gbb_last_error());
+  }
+  if (M == 0) return GBB_OK;
+  size_t off[kMaxBatch + 1];
+  off[0] = 0;
+  for (int i = 0; i < n; ++i) off[i + 1] = off[i] + batch_ws_one(N[i], K[i], M);
+  if (off[n]) {
+    if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", off[n]);
+    if (ws_bytes < off[n]) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", off[n], ws_bytes);
+    if (!aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
+  }
+  char* ws = static_cast<char*>(workspace);
+  if (M > 16) {   // one launch (or chunk sequence) per problem, as gbb_gemm_mixed_w
+    for (int i = 0; i < n; ++i) {
+      const gbb_status st = gbb_gemm_mixed_w(images[i], N[i], K[i], x[i], y[i], M, ws ? ws + off[i] : nullptr,
+                                             off[i + 1] - off[i], stream);
+      if (st != GBB_OK) return st;
+    }
+    return GBB_OK;
+  }
+  BlockImageView views[kMaxBatch];
+  DecodePlan plans[kMaxBatch];
+  void* wss[kMaxBatch];
+  for (int i = 0; i < n; ++i) {
+    views[i] = block_view(images[i], N[i], K[i]);
+    plans[i] = decode_plan(N[i], K[i], M);
+    wss[i] = ws ? ws + off[i] : nullptr;
+  }
+  return device_status(launch_decode_batch(n, views, x, y, M, plans, wss, stream), "grouped decode launch");
+}

@@ -312,14 +312,16 @@ __device__ __forceinline__ void block_mma(const u32x4* ring, uint32_t szb, uint3
 constexpr int kRing8 = 12;
 constexpr int kRing16 = 13;
 
-template <int NW, int MT, int RS = Ring<MT>::kSlots>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3))) void decode_kernel(DecodeArgs a) {
+// Workgroup wg of a launch of one problem: block row wg / nseg, K segment
+// wg % nseg.
+template <int NW, int MT, int RS>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg) {
   constexpr int R = RS;
   // wave-uniform values go through readfirstlane so the compiler keeps them
   // in scalar registers and branches on them with scalar branches
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int br = blockIdx.x / a.nseg, seg = blockIdx.x - br * a.nseg;
+  const int br = int(unsigned(wg) / unsigned(a.nseg)), seg = wg - br * a.nseg;
   // this workgroup's columns, split evenly between its waves
   const int wg_begin = seg * a.seg_cols;
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
@@ -435,6 +437,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3)))
       }
     }
   }
+}
+
+template <int NW, int MT, int RS = Ring<MT>::kSlots>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3))) void decode_kernel(DecodeArgs a) {
+  decode_body<NW, MT, RS>(a, int(blockIdx.x));
 }
 
 // Two block rows per wave (17 <= M <= 32).  At that batch a block column's
@@ -721,7 +728,7 @@ __device__ __forceinline__ void block1(const u32x4* code, const u32x4* meta, uin
 }
 
 template <int NW>
-__device__ __forceinline__ void decode1_body(const DecodeArgs& a);
+__device__ __forceinline__ void decode1_body(const DecodeArgs& a, int wg);
 // The arguments are passed one by one, those needed first leading, so the
 // dispatcher can place them in scalar registers before the first instruction
 // (kernel argument preloading) instead of every wave loading them from
@@ -747,13 +754,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   a.nbc = nbc;
   a.seg_cols = seg_cols;
   a.nseg = nseg;
-  decode1_body<NW>(a);
+  decode1_body<NW>(a, int(blockIdx.x));
 }
 template <int NW>
-__device__ __forceinline__ void decode1_body(const DecodeArgs& a) {
+__device__ __forceinline__ void decode1_body(const DecodeArgs& a, int wg) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int br = blockIdx.x / a.nseg, seg = blockIdx.x - br * a.nseg;
+  const int br = int(unsigned(wg) / unsigned(a.nseg)), seg = wg - br * a.nseg;
   const int wg_begin = seg * a.seg_cols;
   const int wg_cols = min(a.nbc, wg_begin + a.seg_cols) - wg_begin;
   const int w_begin = wg_begin + (wg_cols * wave) / NW;
@@ -843,6 +850,68 @@ __device__ __forceinline__ void decode1_body(const DecodeArgs& a) {
     splitk_publish(a, n, s, true);
 }
 
+// Grouped launch: independent problems (each its own image, activations,
+// outputs and split-K accumulators, all with the same M) share one grid.
+// Problem i owns workgroups [wg0, wg0 + its own grid); each workgroup finds
+// its problem with a scan over the (uniform) table in the kernel arguments
+// and then runs exactly the single-problem code.
+struct BatchProblem {
+  const uint8_t* bits;
+  const uint32_t* offs;
+  const uint32_t* sz;
+  const uint8_t* codes;
+  const _Float16* x;
+  _Float16* y;
+  uint64_t* acc;
+  float* facc;
+  int N, K, nbr, nbc, seg_cols, nseg, wg0, pad;
+};
+struct DecodeBatch {
+  BatchProblem p[kMaxBatch];
+  int n, M;
+};
+static_assert(sizeof(DecodeBatch) <= 4096, "kernel arguments");
+
+__device__ __forceinline__ int batch_problem(const DecodeBatch& b, int wg) {
+  int i = 0;
+  for (int j = 1; j < b.n; ++j) i = wg >= b.p[j].wg0 ? j : i;
+  return uniform(i);
+}
+
+__device__ __forceinline__ DecodeArgs batch_args(const DecodeBatch& b, int i) {
+  const BatchProblem& p = b.p[i];
+  DecodeArgs a;
+  a.bits = p.bits;
+  a.offs = p.offs;
+  a.sz = p.sz;
+  a.codes = p.codes;
+  a.x = p.x;
+  a.y = p.y;
+  a.acc = p.acc;
+  a.facc = p.facc;
+  a.N = p.N;
+  a.K = p.K;
+  a.M = b.M;
+  a.nbr = p.nbr;
+  a.nbc = p.nbc;
+  a.seg_cols = p.seg_cols;
+  a.nseg = p.nseg;
+  return a;
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode1_batch_kernel(
+    DecodeBatch b) {
+  const int i = batch_problem(b, int(blockIdx.x));
+  decode1_body<NW>(batch_args(b, i), int(blockIdx.x) - b.p[i].wg0);
+}
+
+template <int NW, int MT, int RS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3))) void decode_batch_kernel(DecodeBatch b) {
+  const int i = batch_problem(b, int(blockIdx.x));
+  decode_body<NW, MT, RS>(batch_args(b, i), int(blockIdx.x) - b.p[i].wg0);
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int N, int K, int M) {
@@ -924,6 +993,46 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
     hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode2_kernel<2>), grid, dim3(256), 0, s, a);
+  return int(hipGetLastError());
+}
+
+int launch_decode_batch(int n, const BlockImageView* ims, const uint16_t* const* x, uint16_t* const* y, int M,
+                        const DecodePlan* plans, void* const* workspaces, void* stream) {
+  DecodeBatch b;
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    BatchProblem& p = b.p[i];
+    const BlockImageView& im = ims[i];
+    p.bits = im.bits;
+    p.offs = im.offs;
+    p.sz = im.sz;
+    p.codes = im.codes;
+    p.x = reinterpret_cast<const _Float16*>(x[i]);
+    p.y = reinterpret_cast<_Float16*>(y[i]);
+    p.acc = plans[i].nseg > 1 ? static_cast<uint64_t*>(workspaces[i]) : nullptr;
+    p.facc = plans[i].nseg > 1
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspaces[i]) + size_t(M) * im.N * 8)
+                 : nullptr;
+    p.N = im.N;
+    p.K = im.K;
+    p.nbr = im.nbr;
+    p.nbc = im.nbc;
+    p.seg_cols = plans[i].seg_cols;
+    p.nseg = plans[i].nseg;
+    p.wg0 = wg;
+    p.pad = 0;
+    wg += im.nbr * plans[i].nseg;   // one block row per workgroup at M <= 16
+  }
+  b.n = n;
+  b.M = M;
+  const dim3 grid{static_cast<unsigned>(wg), 1u, 1u};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 1)
+    hipLaunchKernelGGL((decode1_batch_kernel<4>), grid, dim3(256), 0, s, b);
+  else if (M <= 8)
+    hipLaunchKernelGGL((decode_batch_kernel<4, 1, kRing8>), grid, dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((decode_batch_kernel<4, 1, kRing16>), grid, dim3(256), 0, s, b);
   return int(hipGetLastError());
 }
 

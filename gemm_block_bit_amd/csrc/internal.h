@@ -46,6 +46,11 @@ DecodePlan decode_plan(int N, int K, int M);
 
 int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M,
                   void* workspace, const DecodePlan& plan, void* stream);
+// n <= kMaxBatch independent problems with the same M <= 16 in one launch;
+// problem i uses plans[i] (from decode_plan) and workspaces[i].
+constexpr int kMaxBatch = 32;
+int launch_decode_batch(int n, const BlockImageView* ims, const uint16_t* const* x, uint16_t* const* y, int M,
+                        const DecodePlan* plans, void* const* workspaces, void* stream);
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream);
 // Workgroup tiles of the prefill kernel for N rows and M tokens, and the
 // current device's compute units (looked up once per device).

@@ -179,6 +179,28 @@ gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
 gbb_status gbb_gemm_mixed_w_noalloc(const void* image, int N, int K, const uint16_t* x,
                                     uint16_t* y, int M, void* stream);
 
+/* Grouped products: n (1 ... 32) independent block GEMMs y[i] = x[i] .
+ * dequant(W_i)^T with one M, for products that do not depend on each other
+ * (the concurrent sub-problems of the MixLLM page, section 3.3; the
+ * per-bitwidth execution plan of the ScaleBITS explainer page, section 3.2).
+ * For M <= 16 all of them run as ONE launch of the decode kernels: problem
+ * i's workgroups follow problem i-1's in a single grid, so small products
+ * share the GPU instead of paying a launch and a ramp each.  For larger M
+ * the problems run one after another, as gbb_gemm_mixed_w runs them.
+ *   images[i]  device image of N[i] x K[i] (gbb_pack_blocks).
+ *   x[i], y[i] device fp16 [M][K[i]] and [M][N[i]]; no y may overlap another
+ *              problem's x or y.
+ *   workspace  device memory of gbb_gemm_mixed_w_batched_workspace(n, N, K,
+ *              M) bytes (NULL allowed when that is 0), zero-filled once
+ *              before first use; every call leaves it zero-filled.
+ * Errors: GBB_E_ARG (n outside 1 ... 32, NULL arrays, missing workspace),
+ * those of gbb_gemm_mixed_w for each problem (with its index in the
+ * message), GBB_E_SPACE, GBB_E_DEVICE. */
+size_t gbb_gemm_mixed_w_batched_workspace(int n, const int* N, const int* K, int M);
+gbb_status gbb_gemm_mixed_w_batched(int n, const void* const* images, const int* N, const int* K,
+                                    const uint16_t* const* x, uint16_t* const* y, int M,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Whole-layer execution (ScaleBITS explainer page, section 3.2: an execution
  * plan generated for a given bit configuration; MixLLM page, section 3.3:
  * the kernels of a step replayed from a captured graph).  Captures n

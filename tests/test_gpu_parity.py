@@ -306,17 +306,20 @@ def test_library_graph_matches_eager(M):
     """Four calls captured into one library graph (a layer's launch groups in
     miniature, with split-K decode and, at M = 64, the prefill kernel)
     replayed several times, with eager work and synchronizations between the
-    replays: every replay equals the eager calls bit for bit."""
+    replays: every replay equals the eager calls bit for bit and the oracle
+    within 2e-3."""
     shapes = [(384, 1024), (256, 1024), (1792, 1024), (256, 3584)]
-    calls, eager = [], []
+    calls, eager, refs = [], [], []
     for i, (N, K) in enumerate(shapes):
         W = small(N, K, 40 + i)
         bits = synth.random_bitmap(N, K, ALLOWED, 40 + i)
         img = packed(W, bits)
-        x = to_dev(rand_x(M, K, 50 + i))
+        xh = rand_x(M, K, 50 + i)
+        x = to_dev(xh)
         y = torch.empty((M, N), dtype=torch.float16, device=dev())
         calls.append((img, N, K, x, y))
         eager.append(gbb.gemm_mixed_w(img, N, K, x).clone())
+        refs.append(bq.reference_gemm(xh, W, bits))
     g = gbb.Graph(calls)
     try:
         for rep in range(3):
@@ -324,8 +327,9 @@ def test_library_graph_matches_eager(M):
                 y.fill_(float("nan"))
             g.launch()
             torch.cuda.synchronize()
-            for (_, _, _, _, y), ref in zip(calls, eager):
+            for (_, _, _, _, y), ref, oref in zip(calls, eager, refs):
                 assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+                assert rel_err(y, oref) <= TOL, rep
             # eager work between replays, on other buffers
             gbb.gemm_mixed_w(calls[0][0], calls[0][1], calls[0][2], calls[0][3])
             torch.cuda.synchronize()
@@ -335,6 +339,56 @@ def test_library_graph_matches_eager(M):
     with pytest.raises(gbb.GbbError):
         gbb.Graph([(calls[0][0], 384, 1000, torch.empty((M, 1000), dtype=torch.float16, device=dev()),
                     calls[0][4])])
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 24])
+def test_batched_independent_products(M):
+    """Six independent products of different shapes (some with split K) as
+    one grouped call -- one launch for M <= 16 -- twice on one workspace:
+    each output equals its own gbb_gemm_mixed_w call bit for bit and the
+    oracle within 2e-3, and the workspace is clean afterwards."""
+    shapes = [(64, 128), (384, 1024), (1024, 4096), (256, 3584), (4096, 1024), (192, 8192)]
+    calls, refs, singles = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        W = small(N, K, 70 + i)
+        bits = synth.random_bitmap(N, K, ALLOWED, 70 + i)
+        img = packed(W, bits)
+        xh = rand_x(M, K, 80 + i)
+        x = to_dev(xh)
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev())
+        calls.append((img, N, K, x, y))
+        refs.append(bq.reference_gemm(xh, W, bits))
+        singles.append(gbb.gemm_mixed_w(img, N, K, x).clone())
+    b = gbb.Batched(calls)
+    assert b._ws.numel() >= gbb.gemm_mixed_w_batched_workspace([(N, K) for N, K in shapes], M)
+    for rep in range(2):
+        for c in calls:
+            c[4].fill_(float("nan"))
+        b.launch()
+        torch.cuda.synchronize()
+        for (_, N, K, _, y), ref, one in zip(calls, refs, singles):
+            assert torch.equal(y.view(torch.int16), one.view(torch.int16)), (rep, N, K)
+            assert rel_err(y, ref) <= TOL, (rep, N, K)
+        assert not torch.any(b._ws)
+
+
+def test_batched_llama3_8b_layer_m1():
+    """The Llama-3-8B layer's four launch groups (q|k|v, o, gate|up, down)
+    as one grouped launch at M = 1, one checked row per block row."""
+    calls, checks = [], []
+    for gname, idx in synth.LAYER_LAUNCH_GROUPS:
+        N, K, W, bits = synth.stacked_group(synth.llama3_8b_proj, idx)
+        img = packed(W, bits)
+        xh = synth.activations(1, K, synth.WL_LLAMA3_8B, 90 + len(calls))
+        y = torch.empty((1, N), dtype=torch.float16, device=dev())
+        calls.append((img, N, K, to_dev(xh), y))
+        rows = one_row_per_block_row(N, N)
+        checks.append((rows, bq.reference_rows(xh, W, bits, rows)))
+        del W
+    gbb.Batched(calls).launch()
+    torch.cuda.synchronize()
+    for (_, N, K, _, y), (rows, ref) in zip(calls, checks):
+        assert bq.rel_inf_err(y.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL, (N, K)
 
 
 @pytest.mark.parametrize("M", [1, 8, 17, 32, 64])

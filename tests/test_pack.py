@@ -167,6 +167,18 @@ def test_device_entry_points_reject_shapes_before_any_device_work():
                           and L.gbb_last_error())
     assert L.gbb_gemm_mixed_w(None, 64, 128, fake, fake, 1, None, 0, None) == -1
     assert L.gbb_gemm_mixed_w(fake + 8, 64, 128, fake, fake, 1, None, 0, None) == -4
+    # grouped products: the count and every problem are checked first
+    arr = lambda t, v: (t * len(v))(*v)
+    imgs, Ns, Ks = arr(ctypes.c_void_p, [fake, fake]), arr(ctypes.c_int, [64, 64]), arr(ctypes.c_int, [128, 200])
+    xs, ys = arr(ctypes.c_void_p, [fake, fake]), arr(ctypes.c_void_p, [fake + 4096, fake + 8192])
+    assert L.gbb_gemm_mixed_w_batched(0, imgs, Ns, Ks, xs, ys, 1, None, 0, None) == -1
+    assert L.gbb_gemm_mixed_w_batched(33, imgs, Ns, Ks, xs, ys, 1, None, 0, None) == -1
+    assert L.gbb_gemm_mixed_w_batched(2, None, Ns, Ks, xs, ys, 1, None, 0, None) == -1
+    assert L.gbb_gemm_mixed_w_batched(2, imgs, Ns, Ks, xs, ys, 1, None, 0, None) == -2
+    assert b"problem 1" in L.gbb_last_error()
+    assert L.gbb_gemm_mixed_w_batched_workspace(2, Ns, Ks, 1) == 0
+    Ks[1] = 128
+    assert L.gbb_gemm_mixed_w_batched_workspace(0, Ns, Ks, 1) == 0
 
 
 def test_check_image():
