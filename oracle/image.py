@@ -30,6 +30,17 @@ codes  block i occupies 1024 * b_i bytes, split into planes of width
        row = 16 rt + lane % 16, column A = 32 kt + 8 (lane // 16) + 2 p,
        column B = column A + 1 (row and column inside the block).
 
+Version 2: 64x64 blocks (the ScaleBITS explainer's other GPU block size)
+-------------------------------------------------------------------------
+Same header, magic and sections with version 2, K/64 block columns and
+groups of 64 columns.  offs counts 512-byte units.  Block i occupies 512 * b_i
+bytes of codes in the same planes; a plane of width w is w half-slots of
+512 bytes.  In half-slot j, lane l's 8 bytes at 8 l are two little-endian
+words d = 0, 1; each 16-bit half holds 16/w fields of width w, field f of
+the low half of word d being the code of row 16 rt + l % 16, column
+32 kt + 8 (l // 16) + 2 c and the same field of the high half column + 1,
+with c = 2 d + f // (8/w), i = f % (8/w), 4 kt + rt = j (8/w) + i (kt = 0, 1).
+
 W4/W8 image ("GW48")
 --------------------
 header (first 72 B): u32 magic 0x38345747, u32 version 1, u32 N, u32 K,
@@ -59,16 +70,17 @@ def _align256(n: int) -> int:
     return (n + 255) // 256 * 256
 
 
-def block_image_size(bits: np.ndarray) -> int:
+def block_image_size(bits: np.ndarray, block_cols: int = 128) -> int:
     """Byte size of a block image: header, bits, offsets, 256 B of scale/zero
-    per block and 1024*b bytes of codes per block, sections 256-aligned."""
+    per block and 64 * block_cols * b / 8 bytes of codes per block (1024 b for
+    64x128 blocks, 512 b for 64x64), sections 256-aligned."""
     bits = np.asarray(bits)
     nblk = bits.size
     off = 256
     off = _align256(off + nblk)              # after bits
     off = _align256(off + 4 * (nblk + 1))    # after offsets
     off = off + 256 * nblk                   # after scale/zero
-    return off + 1024 * int(bits.astype(np.int64).sum())
+    return off + 8 * block_cols * int(bits.astype(np.int64).sum())
 
 
 def _plane_codes(plane: np.ndarray, w: int) -> np.ndarray:
@@ -97,14 +109,42 @@ def _plane_codes(plane: np.ndarray, w: int) -> np.ndarray:
     return out
 
 
+def _half_plane_codes(plane: np.ndarray, w: int) -> np.ndarray:
+    """Decode one plane of 64x64 blocks (version 2).
+
+    plane: uint8 [nb][w*512]; half-slot j holds, for lane l, two words d;
+    field f of the low half of word d is the code of row 16*rt + l%16, column
+    32*kt + 8*(l//16) + 2*c with c = 2*d + f//(8//w), j*(8//w) + f%(8//w) =
+    4*kt + rt; the high half holds column + 1.  Returns uint8 [nb][64][64]."""
+    nb = plane.shape[0]
+    words = plane.view("<u4").reshape(nb, w, 64, 2)          # [blk][half-slot][lane][d]
+    per = 8 // w
+    mask = (1 << w) - 1
+    out = np.empty((nb, 64, 64), np.uint8)
+    lane = np.arange(64)
+    for j in range(w):
+        for d in range(2):
+            word = words[:, j, :, d].astype(np.uint64)
+            for f in range(16 // w):
+                c, i = 2 * d + f // per, f % per
+                kt, rt = divmod(j * per + i, 4)
+                row = 16 * rt + lane % 16
+                col = 32 * kt + 8 * (lane // 16) + 2 * c
+                out[:, row, col] = ((word >> np.uint64(w * f)) & np.uint64(mask)).astype(np.uint8)
+                out[:, row, col + 1] = ((word >> np.uint64(16 + w * f)) & np.uint64(mask)).astype(np.uint8)
+    return out
+
+
 def read_block_image(buf) -> dict:
     """Decode a block image into N, K, bits [N/64][K/128], q uint8 [N][K],
     s16 / z16 float16 [N][K/128]."""
     b = np.frombuffer(bytes(buf) if not isinstance(buf, np.ndarray) else buf.tobytes(), np.uint8)
     magic, ver, N, K, nbr, nbc = (int(v) for v in b[:24].view("<u4"))
-    if magic != GBB_MAGIC or ver != 1:
-        raise ValueError("not a version-1 block image")
-    if nbr * 64 != N or nbc * 128 != K:
+    if magic != GBB_MAGIC or ver not in (1, 2):
+        raise ValueError("not a version-1 or version-2 block image")
+    bcols = 128 if ver == 1 else 64           # block columns (= group size)
+    unit = 8 * bcols                          # bytes of codes per bit of width per block
+    if nbr * 64 != N or nbc * bcols != K:
         raise ValueError("inconsistent header")
     bits_off, offs_off, sz_off, codes_off, codes_bytes = (int(v) for v in b[24:64].view("<u8"))
     nblk = nbr * nbc
@@ -114,30 +154,31 @@ def read_block_image(buf) -> dict:
     offs = b[offs_off:offs_off + 4 * (nblk + 1)].view("<u4").astype(np.int64)
     if offs[0] != 0 or not np.array_equal(np.diff(offs), bits.astype(np.int64)):
         raise ValueError("block offsets disagree with bitwidths")
-    if offs[-1] * 1024 != codes_bytes or b.size < codes_off + codes_bytes:
+    if offs[-1] * unit != codes_bytes or b.size < codes_off + codes_bytes:
         raise ValueError("code section size")
     sz = b[sz_off:sz_off + 256 * nblk].view("<u2").reshape(nbr, nbc, 16, 4, 2)
     sz = sz.transpose(0, 1, 3, 2, 4).reshape(nbr, nbc, 64, 2)        # row 16 t + r
     s16 = sz[..., 0].copy().view(np.float16).transpose(0, 2, 1).reshape(N, nbc)
     z16 = sz[..., 1].copy().view(np.float16).transpose(0, 2, 1).reshape(N, nbc)
 
-    q = np.empty((nbr, nbc, 64, 128), np.uint8)
+    q = np.empty((nbr, nbc, 64, bcols), np.uint8)
     flat_bits = bits.reshape(-1)
+    decode = _plane_codes if ver == 1 else _half_plane_codes
     for bw, widths in PLANES.items():
         idx = np.nonzero(flat_bits == bw)[0]
         if idx.size == 0:
             continue
-        starts = codes_off + 1024 * offs[idx]
-        raw = np.stack([b[s:s + 1024 * bw] for s in starts])      # [nb][1024*bw]
-        acc = np.zeros((idx.size, 64, 128), np.uint16)
+        starts = codes_off + unit * offs[idx]
+        raw = np.stack([b[s:s + unit * bw] for s in starts])      # [nb][unit*bw]
+        acc = np.zeros((idx.size, 64, bcols), np.uint16)
         pos, shift = 0, 0
         for w in widths:
-            acc |= _plane_codes(np.ascontiguousarray(raw[:, pos:pos + 1024 * w]), w).astype(np.uint16) << shift
-            pos += 1024 * w
+            acc |= decode(np.ascontiguousarray(raw[:, pos:pos + unit * w]), w).astype(np.uint16) << shift
+            pos += unit * w
             shift += w
-        q.reshape(-1, 64, 128)[idx] = acc.astype(np.uint8)
+        q.reshape(-1, 64, bcols)[idx] = acc.astype(np.uint8)
     q = q.transpose(0, 2, 1, 3).reshape(N, K)
-    return dict(N=N, K=K, bits=bits.reshape(nbr, nbc), q=q, s16=s16, z16=z16,
+    return dict(N=N, K=K, bits=bits.reshape(nbr, nbc), q=q, s16=s16, z16=z16, block_cols=bcols,
                 codes_bytes=codes_bytes, size=codes_off + codes_bytes)
 
 

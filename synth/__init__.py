@@ -135,6 +135,12 @@ def random_bitmap(N: int, K: int, choices: Sequence[int], seed: int) -> np.ndarr
     return g.choice(np.asarray(choices, np.uint8), size=(N // BLOCK_ROWS, K // BLOCK_COLS))
 
 
+def random_bitmap64(N: int, K: int, choices: Sequence[int], seed: int) -> np.ndarray:
+    """uint8 [N/64][K/64]: a random bitwidth per 64x64 block."""
+    g = np.random.default_rng(np.random.SeedSequence([0xB10C, 98, seed, TENSOR_BITMAP]))
+    return g.choice(np.asarray(choices, np.uint8), size=(N // BLOCK_ROWS, K // 64))
+
+
 # ----------------------------------------------------------------------------
 # activations and salient rows
 # ----------------------------------------------------------------------------

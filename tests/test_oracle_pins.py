@@ -328,6 +328,139 @@ def test_oracle_reader_against_slow_writer():
 
 
 # ----------------------------------------------------------------------------
+# 64x64 blocks (groups of 64 columns)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("b", ALLOWED)
+def test_64x64_uniform_bitwidth_is_plain_group64_rtn(b):
+    """64x64 blocks with one bitwidth everywhere: plain group-64 RTN --
+    scale, zero and codes agree with an exhaustive search per 64 columns."""
+    N, K = 64, 256
+    W = small_matrix(N, K, 20 + b)
+    q, s16, z16 = bq.quantize_blocks(W, np.full((1, 4), b, np.uint8), block_cols=64)
+    assert s16.shape == (N, 4)
+    L = 2 ** b - 1
+    for n in range(0, N, 9):
+        for g in range(4):
+            vals = [Fraction(float(v)) for v in W[n, 64 * g:64 * g + 64]]
+            s16_ref, s, z = brute_scale_zero(vals, b)
+            assert s16[n, g] == s16_ref and z16[n, g] == z
+            for k in range(0, 64, 3):
+                assert q[n, 64 * g + k] == nearest_code(vals[k], s, z, L)
+
+
+def test_64x64_mixed_bitmap_uses_the_block_of_each_group():
+    """Each (row, 64-column group) follows bits[row // 64][col // 64]; the same
+    matrix with 64x128 blocks quantizes 128-column groups instead."""
+    N, K = 128, 256
+    W = small_matrix(N, K, 23)
+    bits = np.array([[1, 8, 3, 6], [2, 4, 8, 1]], np.uint8)
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    for n in range(0, N, 7):
+        for g in range(4):
+            b = int(bits[n // 64, g])
+            vals = [Fraction(float(v)) for v in W[n, 64 * g:64 * g + 64]]
+            s16_ref, s, z = brute_scale_zero(vals, b)
+            assert s16[n, g] == s16_ref and z16[n, g] == z
+            for k in (0, 13, 31, 32, 63):
+                assert q[n, 64 * g + k] == nearest_code(vals[k], s, z, 2 ** b - 1)
+    with pytest.raises(ValueError):       # a 64x128 map does not fit 64x64 blocks
+        bq.quantize_blocks(W, bits[:, :2], block_cols=64)
+
+
+def test_64x64_gemm_matches_exact_rational_dot_products():
+    N, K, M = 128, 192, 2
+    W = small_matrix(N, K, 24)
+    bits = synth.random_bitmap64(N, K, ALLOWED, 24)
+    x = np.random.default_rng(5).standard_normal((M, K)).astype(np.float16)
+    y = bq.reference_gemm(x, W, bits, block_cols=64)
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    for m in range(M):
+        for n in range(0, N, 11):
+            exact = sum(Fraction(float(x[m, k])) * (int(q[n, k]) - Fraction(float(z16[n, k // 64])))
+                        * Fraction(float(s16[n, k // 64])) for k in range(K))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 15)
+    rows = np.array([0, 63, 64, 127])
+    assert np.allclose(bq.reference_rows(x, W, bits, rows, block_cols=64), y[:, rows], rtol=0, atol=1e-12)
+
+
+def test_64x64_packed_size_identity():
+    """Codes of a 64x64 block are 64 * 64 * b / 8 = 512 b bytes; by hand for a
+    2 x 3 bitmap: 256 (header) + 256 (6 bitwidths, padded) + 256 (7 offsets,
+    padded) + 1536 (scale/zero) + 512 * 24 (codes)."""
+    bits = np.array([[1, 2, 3], [4, 6, 8]], np.uint8)
+    assert sum(64 * 64 * int(b) // 8 for b in bits.reshape(-1)) == 12288
+    assert image.block_image_size(bits, block_cols=64) == 256 + 256 + 256 + 1536 + 12288
+
+
+def _slow_block_image_64(q, s16, z16, bits):
+    """Write a 64x64-block image (version 2) one code at a time from the
+    format description."""
+    N, K = q.shape
+    nbr, nbc = N // 64, K // 64
+    nblk = nbr * nbc
+    al = lambda n: (n + 255) // 256 * 256
+    bits_off = 256
+    offs_off = al(bits_off + nblk)
+    sz_off = al(offs_off + 4 * (nblk + 1))
+    codes_off = sz_off + 256 * nblk
+    total = int(bits.astype(np.int64).sum())
+    buf = bytearray(codes_off + 512 * total)
+    hdr = np.array([0x31424247, 2, N, K, nbr, nbc], "<u4").tobytes()
+    hdr += np.array([bits_off, offs_off, sz_off, codes_off, 512 * total], "<u8").tobytes()
+    buf[:64] = hdr
+    planes = {1: (1,), 2: (2,), 3: (2, 1), 4: (4,), 6: (4, 2), 8: (4, 4)}
+    units = 0
+    for br in range(nbr):
+        for bc in range(nbc):
+            blk = br * nbc + bc
+            b = int(bits[br, bc])
+            buf[bits_off + blk] = b
+            buf[offs_off + 4 * blk:offs_off + 4 * blk + 4] = int(units).to_bytes(4, "little")
+            for r in range(64):
+                o = sz_off + 256 * blk + 4 * (4 * (r % 16) + r // 16)
+                buf[o:o + 2] = np.float16(s16[64 * br + r, bc]).tobytes()
+                buf[o + 2:o + 4] = np.float16(z16[64 * br + r, bc]).tobytes()
+            base = codes_off + 512 * units
+            shift = 0
+            for w in planes[b]:
+                per = 8 // w
+                words = [0] * (128 * w)          # u32 words of the plane: [half-slot][lane][d]
+                for r in range(64):
+                    for k in range(64):
+                        rt, r16 = divmod(r, 16)
+                        kt, g, c, h = k // 32, (k % 32) // 8, (k % 8) // 2, k % 2
+                        j, i = divmod(4 * kt + rt, per)
+                        d, f = c // 2, (c % 2) * per + i
+                        code = (int(q[64 * br + r, 64 * bc + k]) >> shift) & ((1 << w) - 1)
+                        words[128 * j + 2 * (16 * g + r16) + d] |= code << (16 * h + w * f)
+                for n, word in enumerate(words):
+                    buf[base + 4 * n:base + 4 * n + 4] = word.to_bytes(4, "little")
+                base += 512 * w
+                shift += w
+            units += b
+    buf[offs_off + 4 * nblk:offs_off + 4 * nblk + 4] = int(units).to_bytes(4, "little")
+    return bytes(buf)
+
+
+def test_oracle_reader_64x64_against_slow_writer():
+    N, K = 128, 192
+    g = np.random.default_rng(6)
+    bits = np.array([[1, 2, 3], [4, 6, 8]], np.uint8)
+    L = np.repeat(np.repeat(2 ** bits.astype(np.int64) - 1, 64, 0), 64, 1)
+    q = (g.integers(0, 256, (N, K)) % (L + 1)).astype(np.uint8)
+    s16 = g.standard_normal((N, 3)).astype(np.float16)
+    z16 = (g.integers(0, 256, (N, 3)) % (np.repeat(2 ** bits.astype(np.int64), 64, 0))).astype(np.float16)
+    img = _slow_block_image_64(q, s16, z16, bits)
+    assert len(img) == image.block_image_size(bits, block_cols=64)
+    d = image.read_block_image(img)
+    assert d["block_cols"] == 64
+    assert np.array_equal(d["bits"], bits)
+    assert np.array_equal(d["q"], q)
+    assert np.array_equal(d["s16"].view(np.uint16), s16.view(np.uint16))
+    assert np.array_equal(d["z16"], z16)
+
+
+# ----------------------------------------------------------------------------
 # output-feature mixed W8/W4 x A8
 # ----------------------------------------------------------------------------
 def test_sym8_brute_force():
