@@ -66,38 +66,39 @@ def measured_traffic():
 
 
 # extra workloads after the headline, in run order
-EXTRAS = ("llama3_70b_batch", "llama3_8b", "mixed_vs_uniform", "linear_4096", "prefill", "w44a8")
+EXTRAS = ("llama3_70b_batch", "llama3_8b", "mixed_vs_uniform", "blocks_64x64", "linear_4096", "prefill", "w44a8")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def weight_bytes(bits: np.ndarray) -> int:
+def weight_bytes(bits: np.ndarray, block_cols: int = 128) -> int:
     """Algorithmic bytes of one packed matrix: codes (1024 b per 64x128
-    block), 256 B of fp16 scale/zero per block, 1 B bitwidth and 4 B offset
-    per block (+4)."""
+    block, 512 b per 64x64 block), 256 B of fp16 scale/zero per block, 1 B
+    bitwidth and 4 B offset per block (+4)."""
     nblk = bits.size
-    return 1024 * int(bits.astype(np.int64).sum()) + 256 * nblk + nblk + 4 * (nblk + 1)
+    return 8 * block_cols * int(bits.astype(np.int64).sum()) + 256 * nblk + nblk + 4 * (nblk + 1)
 
 
 class DecodeLayerSet:
     """R copies of one decoder layer's packed launch groups on the GPU, with
     their activations, outputs and one shared split-K workspace."""
 
-    def __init__(self, torch, gbb, synth, gen, copies, M, dev, keep_host=False):
+    def __init__(self, torch, gbb, synth, gen, copies, M, dev, keep_host=False, block_cols=128):
         self.torch, self.gbb = torch, gbb
         self.M = M
+        self.block_cols = block_cols
         host = []
         for name, idx in synth.LAYER_LAUNCH_GROUPS:
             N, K, W, bits = synth.stacked_group(gen, idx)
-            img, _, _ = gbb.pack_blocks(W, bits)
+            img, _, _ = gbb.pack_blocks(W, bits, block_cols=block_cols)
             host.append((name, (N, K), img, bits))
             del W
         self.images = [[torch.from_numpy(img).to(dev) for (_, _, img, _) in host] for _ in range(copies)]
         self.shapes = [shape for (_, shape, _, _) in host]
         self.names = [name for (name, _, _, _) in host]
-        self.bytes = [weight_bytes(b) for (_, _, _, b) in host]
+        self.bytes = [weight_bytes(b, block_cols) for (_, _, _, b) in host]
         self.layer_bytes = sum(self.bytes)
         nblk = sum(b.size for (_, _, _, b) in host)
         self.mean_bits = float(sum(int(b.astype(np.int64).sum()) for (_, _, _, b) in host)) / nblk
@@ -106,10 +107,15 @@ class DecodeLayerSet:
         g = np.random.default_rng(7)
         self.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
         self.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (N, _) in self.shapes]
-        ws = max(gbb.gemm_mixed_w_workspace(N, K, M) for (N, K) in self.shapes)
+        ws = max(self._workspace(N, K, M) for (N, K) in self.shapes)
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         # raw arguments for direct C calls (no per-call Python marshalling)
-        self.fn = gbb.lib().gbb_gemm_mixed_w
+        self.fn = gbb.lib().gbb_gemm_mixed_w if block_cols == 128 else gbb.lib().gbb_gemm_mixed_w_64x64
+
+    def _workspace(self, N, K, M):
+        if self.block_cols == 128:
+            return self.gbb.gemm_mixed_w_workspace(N, K, M)
+        return self.gbb.gemm_mixed_w_64x64_workspace(N, K, M)
 
     def with_batch(self, M, seed):
         """The same packed layers with new activations, outputs and workspace
@@ -122,7 +128,7 @@ class DecodeLayerSet:
         g = np.random.default_rng(seed)
         other.x = [torch.from_numpy(g.standard_normal((M, K)).astype(np.float16)).to(dev) for (_, K) in self.shapes]
         other.y = [torch.empty((M, N), dtype=torch.float16, device=dev) for (N, _) in self.shapes]
-        ws = max(gbb.gemm_mixed_w_workspace(N, K, M) for (N, K) in self.shapes)
+        ws = max(self._workspace(N, K, M) for (N, K) in self.shapes)
         other.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         return other
 
@@ -411,6 +417,33 @@ def main():
                 "mixed_GBps": round(v8, 1), "mixed_mean_bits": round(L8.mean_bits, 3),
                 "mixed_over_uniform_at_same_bits": round(v8 / ref, 3)}
             log(f"mixed / uniform at {L8.mean_bits:.2f} bits: {v8 / ref:.3f}")
+
+        if "blocks_64x64" in want:
+            # ------- the same layer with 64x64 blocks at the same mean bits -------
+            # Same weights and bit quotas over twice the blocks: a 64x64 block
+            # carries the same 256 B of scales and zeros for half the codes,
+            # so the step reads more bytes; the comparison is step time and
+            # GB/s at M = 1 and 8.
+            log("packing Llama-3-8B-shaped layer with 64x64 blocks")
+            L64 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj64, LAYER_COPIES_8B, 1, dev, block_cols=64)
+            b64 = L64.layer_bytes * L64.copies
+            s64, _, _ = time_graph(torch, lambda: L64.step(h()), args.steps, args.warmup)
+            L64b = L64.with_batch(8, 8)
+            s64b, _, _ = time_graph(torch, lambda: L64b.step(h()), args.steps, args.warmup)
+            extra["blocks_64x64_8b"] = {
+                "mean_bits": round(L64.mean_bits, 3), "layer_MB": round(L64.layer_bytes / 1e6, 1),
+                "m1": {"GBps": round(b64 / s64 / 1e9, 1), "graph_step_us": round(s64 * 1e6, 1),
+                       "frac_hbm": round(b64 / s64 / 1e9 / HBM_PEAK_GBS, 3)},
+                "m8": {"GBps": round(b64 / s64b / 1e9, 1), "graph_step_us": round(s64b * 1e6, 1)},
+                "blocks_64x128_same_layer": {"mean_bits": round(L8.mean_bits, 3),
+                                             "layer_MB": round(L8.layer_bytes / 1e6, 1),
+                                             "m1": {"GBps": round(v8, 1), "graph_step_us": round(s8 * 1e6, 1)},
+                                             "m8": {"GBps": e8["decode_m8_GBps"],
+                                                    "graph_step_us": round(s8b * 1e6, 1)}}}
+            log(f"8B 64x64 blocks: M=1 {b64 / s64 / 1e9:.0f} GB/s ({s64 * 1e6:.1f} us/step), "
+                f"M=8 {b64 / s64b / 1e9:.0f} GB/s ({s64b * 1e6:.1f} us/step)")
+            del L64, L64b
+            torch.cuda.empty_cache()
         del L8
         torch.cuda.empty_cache()
 

@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     check_image,
     dequant,
     gemm_mixed_w,
+    gemm_mixed_w_64x64,
+    gemm_mixed_w_64x64_workspace,
     gemm_mixed_w_batched_workspace,
     gemm_mixed_w_noalloc,
     gemm_mixed_w_path,

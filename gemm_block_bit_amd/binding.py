@@ -37,6 +37,12 @@ _SIGS = {
     "gbb_packed_bytes": (_sz, [_vp, _i, _i]),
     "gbb_pack_blocks": (_i, [_vp, _i, _i, _vp, _vp, _vp, _u, _vp, _sz]),
     "gbb_check_image": (_i, [_vp, _sz, _i, _i]),
+    "gbb_packed_bytes_64x64": (_sz, [_vp, _i, _i]),
+    "gbb_pack_blocks_64x64": (_i, [_vp, _i, _i, _vp, _vp, _vp, _u, _vp, _sz]),
+    "gbb_gemm_mixed_w_64x64_workspace": (_sz, [_i, _i, _i]),
+    "gbb_gemm_mixed_w_64x64": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "gbb_unpack_codes_64x64": (_i, [_vp, _i, _i, _vp, _vp]),
+    "gbb_dequant_64x64": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "gbb_allocate_bits": (_i, [_vp, _i, _i, ctypes.c_double, ctypes.c_double, _vp]),
     "gbb_channel_order": (_i, [_vp, _i, _i, _vp, _vp]),
     "gbb_gemm_mixed_w_workspace": (_sz, [_i, _i, _i]),
@@ -104,14 +110,24 @@ def _as_u16(W: np.ndarray) -> np.ndarray:
     raise TypeError("W must be float16 (or its uint16 bit pattern)")
 
 
-def packed_bytes(bits: np.ndarray, N: int, K: int) -> int:
+def packed_bytes(bits: np.ndarray, N: int, K: int, block_cols: int = 128) -> int:
     bits = np.ascontiguousarray(bits, np.uint8)
-    n = lib().gbb_packed_bytes(_np_ptr(bits), N, K)
+    size_fn, pack_fn = _block_fns(block_cols)
+    n = size_fn(_np_ptr(bits), N, K)
     if n == 0:
         # the packer validates the map first and reports the precise status
-        _check(lib().gbb_pack_blocks(None, N, K, _np_ptr(bits), None, None, 0, None, 0))
+        _check(pack_fn(None, N, K, _np_ptr(bits), None, None, 0, None, 0))
         _check(-1)
     return n
+
+
+def _block_fns(block_cols: int):
+    L = lib()
+    if block_cols == 128:
+        return L.gbb_packed_bytes, L.gbb_pack_blocks
+    if block_cols == 64:
+        return L.gbb_packed_bytes_64x64, L.gbb_pack_blocks_64x64
+    raise ValueError("block_cols must be 128 (64x128 blocks) or 64 (64x64 blocks)")
 
 
 def allocate_bits(W: np.ndarray, target_bits: float, gamma: float = 0.05) -> np.ndarray:
@@ -136,14 +152,17 @@ def channel_order(W: np.ndarray):
 
 
 def pack_blocks(W: np.ndarray, bits: np.ndarray, scale: np.ndarray | None = None,
-                zero: np.ndarray | None = None):
-    """Quantize fp16 W [N][K] with the per-block bitwidth map and pack it.
-    Returns (image uint8, scale fp16 [N][K/128], zero fp16 [N][K/128]).  With
+                zero: np.ndarray | None = None, block_cols: int = 128):
+    """Quantize fp16 W [N][K] with the per-block bitwidth map and pack it
+    (64 x block_cols blocks: 128, or 64 for 64x64 blocks).  Returns (image
+    uint8, scale fp16 [N][K/block_cols], zero fp16 [N][K/block_cols]).  With
     `scale` and `zero` given they are used instead of min/max."""
     Wu = _as_u16(W)
     N, K = Wu.shape
     bits = np.ascontiguousarray(bits, np.uint8)
-    size = packed_bytes(bits, N, K)
+    size = packed_bytes(bits, N, K, block_cols)
+    _, pack_fn = _block_fns(block_cols)
+    G = K // block_cols
     image = np.empty(size, np.uint8)
     flags = 0
     if scale is not None or zero is not None:
@@ -153,10 +172,9 @@ def pack_blocks(W: np.ndarray, bits: np.ndarray, scale: np.ndarray | None = None
         z = np.ascontiguousarray(zero, np.float16).copy()
         flags = GBB_PACK_GIVEN_SZ
     else:
-        s = np.empty((N, K // 128), np.float16)
-        z = np.empty((N, K // 128), np.float16)
-    _check(lib().gbb_pack_blocks(_np_ptr(Wu), N, K, _np_ptr(bits), _np_ptr(s), _np_ptr(z), flags,
-                                 _np_ptr(image), size))
+        s = np.empty((N, G), np.float16)
+        z = np.empty((N, G), np.float16)
+    _check(pack_fn(_np_ptr(Wu), N, K, _np_ptr(bits), _np_ptr(s), _np_ptr(z), flags, _np_ptr(image), size))
     return image, s, z
 
 
@@ -357,21 +375,42 @@ class Graph:
             pass
 
 
-def unpack_codes(image, N: int, K: int):
+def unpack_codes(image, N: int, K: int, block_cols: int = 128):
     torch = _torch()
     q = torch.empty((N, K), dtype=torch.uint8, device=image.device)
-    _check(lib().gbb_unpack_codes(_dev_ptr(image, torch.uint8, "image"), N, K, q.data_ptr(), _stream(image)))
+    fn = lib().gbb_unpack_codes if block_cols == 128 else lib().gbb_unpack_codes_64x64
+    _check(fn(_dev_ptr(image, torch.uint8, "image"), N, K, q.data_ptr(), _stream(image)))
     return q
 
 
-def dequant(image, N: int, K: int):
+def dequant(image, N: int, K: int, block_cols: int = 128):
     """(w32 fp32 [N][K] = (q - z) * s, w16 = its fp16 rounding)."""
     torch = _torch()
     w32 = torch.empty((N, K), dtype=torch.float32, device=image.device)
     w16 = torch.empty((N, K), dtype=torch.float16, device=image.device)
-    _check(lib().gbb_dequant(_dev_ptr(image, torch.uint8, "image"), N, K, w32.data_ptr(), w16.data_ptr(),
-                             _stream(image)))
+    fn = lib().gbb_dequant if block_cols == 128 else lib().gbb_dequant_64x64
+    _check(fn(_dev_ptr(image, torch.uint8, "image"), N, K, w32.data_ptr(), w16.data_ptr(), _stream(image)))
     return w32, w16
+
+
+def gemm_mixed_w_64x64_workspace(N: int, K: int, M: int) -> int:
+    return lib().gbb_gemm_mixed_w_64x64_workspace(N, K, M)
+
+
+def gemm_mixed_w_64x64(image, N: int, K: int, x, out=None, workspace=None):
+    """y = x . dequant(W)^T over a 64x64-block image (fp16 [M][N])."""
+    torch = _torch()
+    M = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [M][{K}]")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    need = gemm_mixed_w_64x64_workspace(N, K, M)
+    ws = workspace if workspace is not None else _workspace(x.device, need)
+    _check(lib().gbb_gemm_mixed_w_64x64(
+        _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),
+        _dev_ptr(y, torch.float16, "y"), M, ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(x)))
+    return y
 
 
 def quant_act_i8(x, ga: int | None = None):

@@ -28,12 +28,13 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-Wall",
 CXX_FLAGS = ["-O2", "-Wall", "-Wextra", "-fno-fast-math"] + COMMON
 
 # graph.cpp is host code on the HIP runtime (stream capture), so hipcc builds it too
-HIP_SOURCES = ["decode.hip", "prefill.hip", "w48.hip", "debug.hip", "noalloc.hip", "graph.cpp"]
+HIP_SOURCES = ["decode.hip", "decode64.hip", "prefill.hip", "w48.hip", "debug.hip", "noalloc.hip", "graph.cpp"]
 # per-source extra flags: the decode kernel reads its MFMA results with VALU
 # code right away, so it keeps them in VGPRs rather than accumulation
 # registers; its single-token kernel takes its arguments preloaded into
 # scalar registers
 HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
+             "decode64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
              # the W4.4A8 kernels scale their int32 MFMA results with VALU code
              # right away too, so they also keep them in VGPRs
              "w48.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -1,5 +1,6 @@
 // C-ABI entry points of the device path: argument checks, image section
 // addresses and kernel dispatch.  No allocation, no synchronization.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -18,20 +19,21 @@ gbb_status device_status(int err, const char* what) {
   return fail(GBB_E_DEVICE, "%s: HIP error %d (%s)", what, err, msg);
 }
 
-gbb_status check_block_args(const void* image, int N, int K, int M) {
+// bc: block columns, 128 (64x128 blocks) or 64 (64x64 blocks).
+gbb_status check_block_args(const void* image, int N, int K, int M, int bc = kGroup) {
   if (!image) return fail(GBB_E_ARG, "image is NULL");
   if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
   if (N > kMaxRows) return fail(GBB_E_SHAPE, "N=%d exceeds %d", N, kMaxRows);
   if (K > kMaxCols) return fail(GBB_E_SHAPE, "K=%d exceeds %d", K, kMaxCols);
   if (M < 0) return fail(GBB_E_ARG, "M must not be negative (M=%d)", M);
-  if (N % kBlockRows || K % kGroup)
-    return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);
+  if (N % kBlockRows || K % bc)
+    return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of %d (N=%d K=%d)", bc, N, K);
   if (!aligned16(image)) return fail(GBB_E_ALIGN, "image is not 16-byte aligned");
   return GBB_OK;
 }
 
-BlockImageView block_view(const void* image, int N, int K) {
-  const BlockLayout l = block_layout(N, K);
+BlockImageView block_view(const void* image, int N, int K, int bc = kGroup) {
+  const BlockLayout l = block_layout(N, K, bc);
   const uint8_t* b = static_cast<const uint8_t*>(image);
   BlockImageView v;
   v.bits = b + l.bits_off;
@@ -41,7 +43,8 @@ BlockImageView block_view(const void* image, int N, int K) {
   v.N = N;
   v.K = K;
   v.nbr = N / kBlockRows;
-  v.nbc = K / kGroup;
+  v.nbc = K / bc;
+  v.bc = bc;
   return v;
 }
 
@@ -263,4 +266,63 @@ extern "C" gbb_status gbb_gemm_mixed_w_batched(int n, const void* const* images,
     wss[i] = ws ? ws + off[i] : nullptr;
   }
   return device_status(launch_decode_batch(n, views, x, y, M, plans, wss, stream), "grouped decode launch");
+}
+
+// ---------------------------------------------------------------------------
+// 64x64 blocks
+// ---------------------------------------------------------------------------
+namespace {
+
+size_t workspace64(int N, int K, int M) {
+  if (M <= 32) return decode_plan64(N, K, M).ws_bytes;
+  size_t need = decode_plan64(N, K, 32).ws_bytes;   // 32-token chunks
+  if (M % 32) need = std::max(need, decode_plan64(N, K, M % 32).ws_bytes);
+  return need;
+}
+
+}  // namespace
+
+extern "C" size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M) {
+  if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % 64) return 0;
+  return workspace64(N, K, M);
+}
+
+extern "C" gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x, uint16_t* y, int M,
+                                             void* workspace, size_t ws_bytes, void* stream) {
+  gbb_status st = check_block_args(image, N, K, M, 64);
+  if (st != GBB_OK || M == 0) return st;
+  if (!x || !y) return fail(GBB_E_ARG, "x and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(GBB_E_ALIGN, "x and y must be 16-byte aligned");
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* yb = reinterpret_cast<const char*>(y);
+  if (xb < yb + size_t(M) * N * 2 && yb < xb + size_t(M) * K * 2) return fail(GBB_E_ARG, "x and y overlap");
+  const size_t need = workspace64(N, K, M);
+  if (need) {
+    if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
+    if (ws_bytes < need) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
+  }
+  const BlockImageView v = block_view(image, N, K, 64);
+  for (int m0 = 0; m0 < M; m0 += 32) {   // one launch for M <= 32
+    const int mc = M - m0 < 32 ? M - m0 : 32;
+    st = device_status(launch_decode64(v, x + size_t(m0) * K, y + size_t(m0) * N, mc, workspace,
+                                       decode_plan64(N, K, mc), stream),
+                       "decode launch");
+    if (st != GBB_OK) return st;
+  }
+  return GBB_OK;
+}
+
+extern "C" gbb_status gbb_unpack_codes_64x64(const void* image, int N, int K, uint8_t* q, void* stream) {
+  gbb_status st = check_block_args(image, N, K, 1, 64);
+  if (st != GBB_OK) return st;
+  if (!q) return fail(GBB_E_ARG, "q is NULL");
+  return device_status(launch_unpack(block_view(image, N, K, 64), q, nullptr, nullptr, stream), "unpack launch");
+}
+
+extern "C" gbb_status gbb_dequant_64x64(const void* image, int N, int K, float* w32, uint16_t* w16, void* stream) {
+  gbb_status st = check_block_args(image, N, K, 1, 64);
+  if (st != GBB_OK) return st;
+  if (!w32 && !w16) return fail(GBB_E_ARG, "w32 and w16 are both NULL");
+  return device_status(launch_unpack(block_view(image, N, K, 64), nullptr, w32, w16, stream), "dequant launch");
 }

@@ -27,6 +27,7 @@ struct BlockImageView {
   const uint32_t* sz;
   const uint8_t* codes;
   int N, K, nbr, nbc;
+  int bc;   // block columns: 128, or 64 for 64x64 blocks
 };
 
 // Decode (M <= 32) launch plan: one workgroup of nw waves per block row and
@@ -52,6 +53,11 @@ constexpr int kMaxBatch = 32;
 int launch_decode_batch(int n, const BlockImageView* ims, const uint16_t* const* x, uint16_t* const* y, int M,
                         const DecodePlan* plans, void* const* workspaces, void* stream);
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream);
+// 64x64-block images, M <= 32: the plan (seg_cols and nbc in 64-column
+// blocks, one block row per workgroup) and the launch.
+DecodePlan decode_plan64(int N, int K, int M);
+int launch_decode64(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* workspace,
+                    const DecodePlan& plan, void* stream);
 // Workgroup tiles of the prefill kernel for N rows and M tokens, and the
 // current device's compute units (looked up once per device).
 int prefill_tiles(int N, int M);

@@ -16,7 +16,8 @@ namespace gbb {
 
 constexpr uint32_t kMagicBlocks = 0x31424247u;  // "GBB1"
 constexpr uint32_t kMagicW48 = 0x38345747u;     // "GW48"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 1;     // 64x128 blocks
+constexpr uint32_t kVersion64 = 2;   // 64x64 blocks
 constexpr int kBlockRows = 64;
 constexpr int kGroup = 128;
 
@@ -34,13 +35,23 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 //         32 kt + 8 (l / 16) + 2 c, and of the high half the next column, for
 //         4 kt + rt = j (16 / w) + i.  So the four words of a slot at one field
 //         are one v_mfma_f32_16x16x32_f16 B operand (tile rt, kt).
+//
+// Version 2 (64x64 blocks, groups of 64 columns): the same sections with
+// K/64 block columns; offs counts 512-byte units and a block holds 512 * b
+// bytes.  A plane of width w is w half-slots of 512 bytes; lane l's 8 bytes
+// of half-slot j are two u32 words d = 0, 1 whose bit field f (width w) of
+// the low half holds the code of row 16 rt + l % 16, column 32 kt +
+// 8 (l / 16) + 2 c, and of the high half the next column, for
+// c = 2 d + f / (8 / w) and 4 kt + rt = j (8 / w) + f % (8 / w), kt = 0, 1.
+// So the two words, each read at two field positions, give the four words
+// of one MFMA B operand.
 struct BlockLayout {
   size_t nblk, bits_off, offs_off, sz_off, codes_off;
 };
 
-inline BlockLayout block_layout(int N, int K) {
+inline BlockLayout block_layout(int N, int K, int bc = kGroup) {
   BlockLayout l;
-  l.nblk = size_t(N / kBlockRows) * size_t(K / kGroup);
+  l.nblk = size_t(N / kBlockRows) * size_t(K / bc);
   l.bits_off = 256;
   l.offs_off = align256(l.bits_off + l.nblk);
   l.sz_off = align256(l.offs_off + 4 * (l.nblk + 1));

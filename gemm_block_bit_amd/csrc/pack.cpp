@@ -152,23 +152,24 @@ bool all_finite(const uint16_t* W, size_t n) {
 // ---------------------------------------------------------------------------
 // block image
 // ---------------------------------------------------------------------------
-static gbb_status check_bits(const uint8_t* bits, int N, int K) {
+// bc: block columns (and group size), 128 or 64.
+static gbb_status check_bits(const uint8_t* bits, int N, int K, int bc = kGroup) {
   if (!bits) return fail(GBB_E_ARG, "bits is NULL");
   if (N <= 0 || K <= 0) return fail(GBB_E_ARG, "N and K must be positive (N=%d K=%d)", N, K);
-  if (N % kBlockRows || K % kGroup)
-    return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of 128 (N=%d K=%d)", N, K);
-  const size_t nblk = size_t(N / kBlockRows) * size_t(K / kGroup);
+  if (N % kBlockRows || K % bc)
+    return fail(GBB_E_SHAPE, "N must be a multiple of 64 and K of %d (N=%d K=%d)", bc, N, K);
+  const size_t nblk = size_t(N / kBlockRows) * size_t(K / bc);
   for (size_t i = 0; i < nblk; ++i)
     if (!valid_bits(bits[i]))
       return fail(GBB_E_BITS, "block %zu has bitwidth %d, not in {1,2,3,4,6,8}", i, int(bits[i]));
   return GBB_OK;
 }
 
-static size_t packed_bytes_unchecked(const uint8_t* bits, int N, int K) {
-  const BlockLayout l = block_layout(N, K);
-  size_t kib = 0;
-  for (size_t i = 0; i < l.nblk; ++i) kib += bits[i];
-  return l.codes_off + 1024 * kib;
+static size_t packed_bytes_unchecked(const uint8_t* bits, int N, int K, int bc = kGroup) {
+  const BlockLayout l = block_layout(N, K, bc);
+  size_t units = 0;
+  for (size_t i = 0; i < l.nblk; ++i) units += bits[i];
+  return l.codes_off + size_t(8 * bc) * units;
 }
 
 // Write one plane of a block: codes q[64][128] (row, column within the block),
@@ -191,6 +192,123 @@ static void write_plane(const uint8_t (*q)[128], int w, int sh, uint8_t* dst) {
       }
 }
 
+// The same for a 64x64 block (codes q[64][64]) into w half-slots of 512 B.
+static void write_plane64(const uint8_t (*q)[64], int w, int sh, uint8_t* dst) {
+  const int per = 8 / w;
+  const uint32_t mask = (1u << w) - 1u;
+  for (int j = 0; j < w; ++j)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int d = 0; d < 2; ++d) {
+        uint32_t word = 0;
+        for (int f = 0; f < 16 / w; ++f) {
+          const int c = 2 * d + f / per, u = j * per + f % per, kt = u >> 2, rt = u & 3;
+          const int row = 16 * rt + (lane & 15);
+          const int col = 32 * kt + 8 * (lane >> 4) + 2 * c;
+          word |= ((uint32_t(q[row][col]) >> sh) & mask) << (w * f);
+          word |= ((uint32_t(q[row][col + 1]) >> sh) & mask) << (16 + w * f);
+        }
+        std::memcpy(dst + 512 * j + 8 * lane + 4 * d, &word, 4);
+      }
+}
+
+// Quantize and pack with blocks of 64 rows x bc columns (bc = 128 or 64;
+// groups of bc columns).
+static gbb_status pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits, uint16_t* scale, uint16_t* zero,
+                              unsigned flags, void* image, size_t image_cap, int bc) {
+  gbb_status st = check_bits(bits, N, K, bc);
+  if (st != GBB_OK) return st;
+  if (!W || !image) return fail(GBB_E_ARG, "W and image must not be NULL");
+  if (flags & ~GBB_PACK_GIVEN_SZ) return fail(GBB_E_ARG, "unknown flag bits 0x%x", flags);
+  const bool given = flags & GBB_PACK_GIVEN_SZ;
+  if (given && (!scale || !zero)) return fail(GBB_E_ARG, "GBB_PACK_GIVEN_SZ needs scale and zero");
+  const size_t need = packed_bytes_unchecked(bits, N, K, bc);
+  if (image_cap < need) return fail(GBB_E_SPACE, "image needs %zu bytes, capacity %zu", need, image_cap);
+  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+
+  const int nbr = N / kBlockRows, nbc = K / bc, G = nbc;
+  if (given) {
+    for (size_t r = 0; r < size_t(N); ++r)
+      for (int g = 0; g < G; ++g) {
+        const int b = bits[(r / kBlockRows) * nbc + g];
+        const double s = half_to_double(scale[r * G + g]), z = half_to_double(zero[r * G + g]);
+        if (!(s > 0) || !std::isfinite(s))
+          return fail(GBB_E_ARG, "given scale of row %zu group %d is not finite and > 0", r, g);
+        if (!(z >= 0 && z <= double((1 << b) - 1) && z == std::floor(z)))
+          return fail(GBB_E_BITS, "given zero of row %zu group %d is not an integer in [0, 2^b-1]", r, g);
+      }
+  }
+
+  const BlockLayout l = block_layout(N, K, bc);
+  const size_t unit = size_t(8 * bc);   // code bytes per bit of width per block
+  uint8_t* img = static_cast<uint8_t*>(image);
+  std::memset(img, 0, l.codes_off);
+  std::vector<size_t> units(l.nblk + 1, 0);
+  for (size_t i = 0; i < l.nblk; ++i) units[i + 1] = units[i] + bits[i];
+
+  BlockHeader h{};
+  h.magic = kMagicBlocks;
+  h.version = bc == kGroup ? kVersion : kVersion64;
+  h.N = uint32_t(N);
+  h.K = uint32_t(K);
+  h.nbr = uint32_t(nbr);
+  h.nbc = uint32_t(nbc);
+  h.bits_off = l.bits_off;
+  h.offs_off = l.offs_off;
+  h.sz_off = l.sz_off;
+  h.codes_off = l.codes_off;
+  h.codes_bytes = unit * units[l.nblk];
+  std::memcpy(img, &h, sizeof h);
+  std::memcpy(img + l.bits_off, bits, l.nblk);
+  for (size_t i = 0; i <= l.nblk; ++i) {
+    const uint32_t o = uint32_t(units[i]);
+    std::memcpy(img + l.offs_off + 4 * i, &o, 4);
+  }
+
+  parallel_for(long(l.nblk), [&](long blk) {
+    const int br = int(blk / nbc), bcol = int(blk % nbc);
+    const int b = bits[blk];
+    const double levels = double((1 << b) - 1);
+    uint8_t q[64][128];
+    uint8_t q64[64][64];
+    double v[128];
+    for (int r = 0; r < 64; ++r) {
+      const size_t row = size_t(br) * 64 + r;
+      const uint16_t* src = W + row * size_t(K) + size_t(bcol) * bc;
+      for (int k = 0; k < bc; ++k) v[k] = half_to_double(src[k]);
+      GroupQ gq;
+      if (given) {
+        gq.s16 = scale[row * G + bcol];
+        gq.z16 = zero[row * G + bcol];
+        gq.s = half_to_double(gq.s16);
+        gq.z = half_to_double(gq.z16);
+      } else {
+        gq = asym_scale_zero(v, bc, levels);
+        if (scale) scale[row * G + bcol] = gq.s16;
+        if (zero) zero[row * G + bcol] = gq.z16;
+      }
+      for (int k = 0; k < bc; ++k) {
+        const uint8_t c = asym_code(v[k], gq, levels);
+        if (bc == kGroup)
+          q[r][k] = c;
+        else
+          q64[r][k] = c;
+      }
+      const uint32_t e = uint32_t(gq.s16) | (uint32_t(gq.z16) << 16);
+      std::memcpy(img + l.sz_off + 256 * size_t(blk) + 4 * (4 * (r % 16) + r / 16), &e, 4);
+    }
+    uint8_t* dst = img + l.codes_off + unit * units[blk];
+    const int w0 = plane0_width(b), w1 = plane1_width(b);
+    if (bc == kGroup) {
+      write_plane(q, w0, 0, dst);
+      if (w1) write_plane(q, w1, w0, dst + unit * w0);
+    } else {
+      write_plane64(q64, w0, 0, dst);
+      if (w1) write_plane64(q64, w1, w0, dst + unit * w0);
+    }
+  });
+  return GBB_OK;
+}
+
 }  // namespace gbb
 
 using namespace gbb;
@@ -205,85 +323,18 @@ extern "C" size_t gbb_packed_bytes(const uint8_t* bits, int N, int K) {
 extern "C" gbb_status gbb_pack_blocks(const uint16_t* W, int N, int K, const uint8_t* bits,
                                       uint16_t* scale, uint16_t* zero, unsigned flags, void* image,
                                       size_t image_cap) {
-  gbb_status st = check_bits(bits, N, K);
-  if (st != GBB_OK) return st;
-  if (!W || !image) return fail(GBB_E_ARG, "W and image must not be NULL");
-  if (flags & ~GBB_PACK_GIVEN_SZ) return fail(GBB_E_ARG, "unknown flag bits 0x%x", flags);
-  const bool given = flags & GBB_PACK_GIVEN_SZ;
-  if (given && (!scale || !zero)) return fail(GBB_E_ARG, "GBB_PACK_GIVEN_SZ needs scale and zero");
-  const size_t need = packed_bytes_unchecked(bits, N, K);
-  if (image_cap < need) return fail(GBB_E_SPACE, "image needs %zu bytes, capacity %zu", need, image_cap);
-  if (!all_finite(W, size_t(N) * size_t(K))) return fail(GBB_E_ARG, "W holds inf or NaN");
+  return pack_blocks(W, N, K, bits, scale, zero, flags, image, image_cap, kGroup);
+}
 
-  const int nbr = N / kBlockRows, nbc = K / kGroup, G = nbc;
-  if (given) {
-    for (size_t r = 0; r < size_t(N); ++r)
-      for (int g = 0; g < G; ++g) {
-        const int b = bits[(r / kBlockRows) * nbc + g];
-        const double s = half_to_double(scale[r * G + g]), z = half_to_double(zero[r * G + g]);
-        if (!(s > 0) || !std::isfinite(s))
-          return fail(GBB_E_ARG, "given scale of row %zu group %d is not finite and > 0", r, g);
-        if (!(z >= 0 && z <= double((1 << b) - 1) && z == std::floor(z)))
-          return fail(GBB_E_BITS, "given zero of row %zu group %d is not an integer in [0, 2^b-1]", r, g);
-      }
-  }
+extern "C" size_t gbb_packed_bytes_64x64(const uint8_t* bits, int N, int K) {
+  if (check_bits(bits, N, K, 64) != GBB_OK) return 0;
+  return packed_bytes_unchecked(bits, N, K, 64);
+}
 
-  const BlockLayout l = block_layout(N, K);
-  uint8_t* img = static_cast<uint8_t*>(image);
-  std::memset(img, 0, l.codes_off);
-  std::vector<size_t> kib(l.nblk + 1, 0);
-  for (size_t i = 0; i < l.nblk; ++i) kib[i + 1] = kib[i] + bits[i];
-
-  BlockHeader h{};
-  h.magic = kMagicBlocks;
-  h.version = kVersion;
-  h.N = uint32_t(N);
-  h.K = uint32_t(K);
-  h.nbr = uint32_t(nbr);
-  h.nbc = uint32_t(nbc);
-  h.bits_off = l.bits_off;
-  h.offs_off = l.offs_off;
-  h.sz_off = l.sz_off;
-  h.codes_off = l.codes_off;
-  h.codes_bytes = 1024 * kib[l.nblk];
-  std::memcpy(img, &h, sizeof h);
-  std::memcpy(img + l.bits_off, bits, l.nblk);
-  for (size_t i = 0; i <= l.nblk; ++i) {
-    const uint32_t o = uint32_t(kib[i]);
-    std::memcpy(img + l.offs_off + 4 * i, &o, 4);
-  }
-
-  parallel_for(long(l.nblk), [&](long blk) {
-    const int br = int(blk / nbc), bc = int(blk % nbc);
-    const int b = bits[blk];
-    const double levels = double((1 << b) - 1);
-    uint8_t q[64][128];
-    double v[128];
-    for (int r = 0; r < 64; ++r) {
-      const size_t row = size_t(br) * 64 + r;
-      const uint16_t* src = W + row * size_t(K) + size_t(bc) * 128;
-      for (int k = 0; k < 128; ++k) v[k] = half_to_double(src[k]);
-      GroupQ gq;
-      if (given) {
-        gq.s16 = scale[row * G + bc];
-        gq.z16 = zero[row * G + bc];
-        gq.s = half_to_double(gq.s16);
-        gq.z = half_to_double(gq.z16);
-      } else {
-        gq = asym_scale_zero(v, 128, levels);
-        if (scale) scale[row * G + bc] = gq.s16;
-        if (zero) zero[row * G + bc] = gq.z16;
-      }
-      for (int k = 0; k < 128; ++k) q[r][k] = asym_code(v[k], gq, levels);
-      const uint32_t e = uint32_t(gq.s16) | (uint32_t(gq.z16) << 16);
-      std::memcpy(img + l.sz_off + 256 * size_t(blk) + 4 * (4 * (r % 16) + r / 16), &e, 4);
-    }
-    uint8_t* dst = img + l.codes_off + 1024 * kib[blk];
-    const int w0 = plane0_width(b), w1 = plane1_width(b);
-    write_plane(q, w0, 0, dst);
-    if (w1) write_plane(q, w1, w0, dst + 1024 * w0);
-  });
-  return GBB_OK;
+extern "C" gbb_status gbb_pack_blocks_64x64(const uint16_t* W, int N, int K, const uint8_t* bits,
+                                            uint16_t* scale, uint16_t* zero, unsigned flags, void* image,
+                                            size_t image_cap) {
+  return pack_blocks(W, N, K, bits, scale, zero, flags, image, image_cap, 64);
 }
 
 extern "C" gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K) {
@@ -291,9 +342,10 @@ extern "C" gbb_status gbb_check_image(const void* image, size_t image_bytes, int
   if (image_bytes < 64) return fail(GBB_E_FORMAT, "image shorter than its header");
   BlockHeader h;
   std::memcpy(&h, image, sizeof h);
-  if (h.magic != kMagicBlocks || h.version != kVersion) return fail(GBB_E_FORMAT, "not a version-1 block image");
+  if (h.magic != kMagicBlocks || (h.version != kVersion && h.version != kVersion64))
+    return fail(GBB_E_FORMAT, "not a block image (version 1 or 2)");
   if (int(h.N) != N || int(h.K) != K) return fail(GBB_E_FORMAT, "image is %ux%u, call says %dx%d", h.N, h.K, N, K);
-  const BlockLayout l = block_layout(N, K);
+  const BlockLayout l = block_layout(N, K, h.version == kVersion ? kGroup : 64);
   if (h.bits_off != l.bits_off || h.offs_off != l.offs_off || h.sz_off != l.sz_off || h.codes_off != l.codes_off)
     return fail(GBB_E_FORMAT, "section offsets do not match the layout for %dx%d", N, K);
   if (image_bytes < h.codes_off + h.codes_bytes) return fail(GBB_E_FORMAT, "image truncated");

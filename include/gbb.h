@@ -244,6 +244,27 @@ gbb_status gbb_unpack_codes(const void* image, int N, int K, uint8_t* q, void* s
 gbb_status gbb_dequant(const void* image, int N, int K, float* w32, uint16_t* w16,
                        void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* 64x64 blocks (the other GPU block size of the ScaleBITS explainer page,  */
+/* section 4.2): 64 output rows x 64 input columns per block, one bitwidth  */
+/* per block, scale/zero per (row, 64-column group).  The image is version  */
+/* 2 of the block image: 512 * b bytes of codes per block.  Each call below */
+/* is its 64x128 counterpart's with K a multiple of 64 and bits [N/64][K/64].*/
+/* ------------------------------------------------------------------------ */
+size_t gbb_packed_bytes_64x64(const uint8_t* bits, int N, int K);
+gbb_status gbb_pack_blocks_64x64(const uint16_t* W, int N, int K, const uint8_t* bits,
+                                 uint16_t* scale, uint16_t* zero, unsigned flags,
+                                 void* image, size_t image_cap);
+/* M <= 32 runs the decode kernels on 64x64 blocks; larger M runs them in
+ * 32-token chunks (one launch each). */
+size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M);
+gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x,
+                                  uint16_t* y, int M, void* workspace, size_t ws_bytes,
+                                  void* stream);
+gbb_status gbb_unpack_codes_64x64(const void* image, int N, int K, uint8_t* q, void* stream);
+gbb_status gbb_dequant_64x64(const void* image, int N, int K, float* w32, uint16_t* w16,
+                             void* stream);
+
 /* ======================================================================== */
 /* Output-feature mixed format, W8 (symmetric) / W4 (asymmetric) x A8       */
 /* ======================================================================== */

@@ -101,21 +101,22 @@ def bitmap_shuffled(nbr: int, nbc: int, fracs, workload: int, proj: int) -> np.n
     return vals.reshape(nbr, nbc)
 
 
-def block_scores(W: np.ndarray, kind: str) -> np.ndarray:
-    """fp64 [nbr][nbc] block score: 'maxabs' (largest |w|) or 'l1' (sum |w|)."""
+def block_scores(W: np.ndarray, kind: str, block_cols: int = BLOCK_COLS) -> np.ndarray:
+    """fp64 [nbr][nbc] block score of 64 x block_cols blocks: 'maxabs'
+    (largest |w|) or 'l1' (sum |w|)."""
     N, K = W.shape
-    nbr, nbc = N // BLOCK_ROWS, K // BLOCK_COLS
+    nbr, nbc = N // BLOCK_ROWS, K // block_cols
     out = np.empty((nbr, nbc), np.float64)
     for r0 in range(0, nbr, 16):               # chunked to bound memory
-        blk = np.abs(W[r0 * 64:(r0 + 16) * 64].astype(np.float64)).reshape(-1, 64, nbc, 128)
+        blk = np.abs(W[r0 * 64:(r0 + 16) * 64].astype(np.float64)).reshape(-1, 64, nbc, block_cols)
         out[r0:r0 + blk.shape[0]] = blk.max(axis=(1, 3)) if kind == "maxabs" else blk.sum(axis=(1, 3))
     return out
 
 
-def bitmap_by_score(W: np.ndarray, fracs, kind: str) -> np.ndarray:
+def bitmap_by_score(W: np.ndarray, fracs, kind: str, block_cols: int = BLOCK_COLS) -> np.ndarray:
     """uint8 [nbr][nbc]: blocks ranked by descending score (ties to the lower
     block index) take the classes in the order listed (widest first)."""
-    sc = block_scores(W, kind)
+    sc = block_scores(W, kind, block_cols)
     nbr, nbc = sc.shape
     order = np.lexsort((np.arange(nbr * nbc), -sc.reshape(-1)))
     vals = np.empty(nbr * nbc, np.uint8)
@@ -208,6 +209,15 @@ def llama3_8b_proj(i: int) -> Tuple[Proj, np.ndarray, np.ndarray]:
     p = LLAMA3_8B_LAYER[i]
     W = weight_gauss_outliers(p.N, p.K, WL_LLAMA3_8B, i)
     return p, W, bitmap_by_score(W, BITS_8B, "maxabs")
+
+
+def llama3_8b_proj64(i: int) -> Tuple[Proj, np.ndarray, np.ndarray]:
+    """The same projection with 64x64 blocks: the same W, bits over
+    [N/64][K/64] blocks ranked by block max|w| with the same quotas (mean
+    3.10)."""
+    p = LLAMA3_8B_LAYER[i]
+    W = weight_gauss_outliers(p.N, p.K, WL_LLAMA3_8B, i)
+    return p, W, bitmap_by_score(W, BITS_8B, "maxabs", 64)
 
 
 def llama3_70b_proj(i: int) -> Tuple[Proj, np.ndarray, np.ndarray]:

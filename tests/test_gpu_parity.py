@@ -784,3 +784,80 @@ def test_w44a8_28672x8192_group_acc_bit_exact(M):
     got = acc[:, torch.from_numpy(rows).to(acc.device)].cpu().numpy().astype(np.int64)
     del acc
     assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows))
+
+
+# ----------------------------------------------------------------------------
+# 64x64 blocks
+# ----------------------------------------------------------------------------
+def packed64(W, bits):
+    img, _, _ = gbb.pack_blocks(W, bits, block_cols=64)
+    return to_dev(img)
+
+
+@pytest.mark.parametrize("N,K,seed", [(64, 64, 0), (192, 448, 1), (448, 1280, 2)])
+def test_64x64_unpack_dequant_bit_exact(N, K, seed):
+    W = small(N, K, seed)
+    bits = synth.random_bitmap64(N, K, ALLOWED, seed)
+    img = packed64(W, bits)
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    assert np.array_equal(gbb.unpack_codes(img, N, K, block_cols=64).cpu().numpy(), q)
+    w32, w16 = gbb.dequant(img, N, K, block_cols=64)
+    ref = bq.dequant_fp32(q, s16, z16)
+    assert np.array_equal(w32.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(w16.cpu().numpy().view(np.uint16), bq.fp16_rne(ref).view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 40])
+def test_64x64_one_hot_rows_exact(M):
+    """One-hot activations give fp16(w') exactly through every 64x64 decode
+    kernel (and the 32-token chunks above 32)."""
+    N, K = 192, 1216
+    W = small(N, K, 31)
+    bits = synth.random_bitmap64(N, K, ALLOWED, 31)
+    img = packed64(W, bits)
+    ks = np.random.default_rng(M).choice(K, size=M, replace=False)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1
+    y = gbb.gemm_mixed_w_64x64(img, N, K, to_dev(x)).cpu().numpy()
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    w16 = bq.dequant_fp16(q, s16, z16)
+    assert np.array_equal(y.view(np.uint16), w16[:, ks].T.view(np.uint16))
+
+
+DECODE64_CASES = [(64, 64, 1), (128, 192, 3), (192, 320, 5), (1024, 4096, 1), (1024, 4096, 8), (320, 2560, 16),
+                  (960, 1408, 17), (512, 4096, 32), (64, 28672, 2), (1024, 4096, 70), (8192, 8192, 24)]
+
+
+@pytest.mark.parametrize("N,K,M", DECODE64_CASES)
+def test_64x64_decode_parity(N, K, M):
+    W = small(N, K, N + K + 1)
+    bits = synth.random_bitmap64(N, K, ALLOWED, N + M)
+    x = rand_x(M, K, M + 3)
+    img = packed64(W, bits)
+    xd = to_dev(x)
+    need = gbb.gemm_mixed_w_64x64_workspace(N, K, M)
+    ws = torch.zeros(need + 256, dtype=torch.uint8, device=dev())
+    rows = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 64) + 37 % 64]))
+    ref = bq.reference_rows(x, W, bits, rows, block_cols=64)
+    first = None
+    for _ in range(3):                      # split-K counters must reset between calls
+        y = gbb.gemm_mixed_w_64x64(img, N, K, xd, workspace=ws).cpu().numpy()
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+        first = y if first is None else first
+        assert np.array_equal(y.view(np.uint16), first.view(np.uint16))
+    assert not torch.any(ws)
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_64x64_llama3_8b_layer_decode(i):
+    """A mixed 64x64 bitmap (mean 3.10 bits, ranked by block max|w|) on each
+    Llama-3-8B projection at M = 1 and 8, one checked row per block row."""
+    p, W, bits = synth.llama3_8b_proj64(i)
+    assert abs(synth.mean_bits(bits) - 3.1) < 0.01 and bits.shape == (p.N // 64, p.K // 64)
+    img = packed64(W, bits)
+    rows = one_row_per_block_row(p.N, 5 + i)
+    for M in (1, 8):
+        x = synth.activations(M, p.K, synth.WL_LLAMA3_8B, 20 + i)
+        y = gbb.gemm_mixed_w_64x64(img, p.N, p.K, to_dev(x)).cpu().numpy()
+        ref = bq.reference_rows(x, W, bits, rows, block_cols=64)
+        assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL, M

@@ -181,6 +181,50 @@ def test_device_entry_points_reject_shapes_before_any_device_work():
     assert L.gbb_gemm_mixed_w_batched_workspace(0, Ns, Ks, 1) == 0
 
 
+@pytest.mark.parametrize("b", ALLOWED)
+def test_pack_64x64_uniform_bits_bit_exact(b):
+    W = small(128, 256, 40 + b)
+    bits = np.full((2, 4), b, np.uint8)
+    img, s, z = gbb.pack_blocks(W, bits, block_cols=64)
+    d = oimg.read_block_image(img)
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    assert d["block_cols"] == 64 and np.array_equal(d["bits"], bits)
+    assert np.array_equal(d["q"], q)
+    assert np.array_equal(d["s16"].view(np.uint16), s16.view(np.uint16)) and np.array_equal(s, s16)
+    assert np.array_equal(d["z16"].view(np.uint16), z16.view(np.uint16)) and np.array_equal(z, z16)
+    assert len(img) == gbb.packed_bytes(bits, 128, 256, block_cols=64) == oimg.block_image_size(bits, 64)
+
+
+@pytest.mark.parametrize("N,K,seed", [(64, 64, 0), (192, 448, 1), (320, 1152, 2)])
+def test_pack_64x64_mixed_bits_bit_exact(N, K, seed):
+    W = small(N, K, seed)
+    bits = synth.random_bitmap64(N, K, ALLOWED, seed)
+    img, _, _ = gbb.pack_blocks(W, bits, block_cols=64)
+    d = oimg.read_block_image(img)
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    assert np.array_equal(d["q"], q)
+    assert np.array_equal(d["s16"].view(np.uint16), s16.view(np.uint16))
+    assert np.array_equal(d["z16"].view(np.uint16), z16.view(np.uint16))
+    gbb.check_image(img, N, K)
+
+
+def test_pack_64x64_given_scale_zero_and_errors():
+    W = small(128, 192, 9)
+    bits = synth.random_bitmap64(128, 192, ALLOWED, 9)
+    _, s, z = gbb.pack_blocks(W, bits, block_cols=64)
+    s_clip = (s.astype(np.float32) * np.float32(0.85)).astype(np.float16)
+    img, _, _ = gbb.pack_blocks(W, bits, s_clip, z, block_cols=64)
+    assert np.array_equal(oimg.read_block_image(img)["q"], bq.codes_with(W, bits, s_clip, z, block_cols=64))
+    expect_status(-2, gbb.pack_blocks, small(64, 96, 1), np.full((1, 1), 4, np.uint8), None, None, 64)
+    expect_status(-3, gbb.pack_blocks, small(64, 128, 1), np.array([[4, 7]], np.uint8), None, None, 64)
+    L = gbb.lib()
+    fake = 1 << 20
+    # K must be a multiple of 64; 64 but not 128 is fine for this entry point
+    assert L.gbb_gemm_mixed_w_64x64(fake, 64, 96, fake, fake + 8192, 1, None, 0, None) == -2
+    assert L.gbb_gemm_mixed_w(fake, 64, 192, fake, fake + 8192, 1, None, 0, None) == -2
+    assert L.gbb_gemm_mixed_w_64x64_workspace(64, 96, 1) == 0
+
+
 def test_check_image():
     W = small(128, 256, 3)
     bits = synth.random_bitmap(128, 256, ALLOWED, 3)
@@ -279,3 +323,16 @@ def test_workspace_follows_the_batch_route(N, K):
         if M % 32:
             want = max(want, gbb.gemm_mixed_w_workspace(N, K, M % 32))
         assert need == want, (M, need, want)
+
+
+def test_64x64_workspace_sizes():
+    """The 64x64 decode plan on the host (no device work): every shape with
+    whole 64-column blocks, down to a single block, gets a workspace of 0 or
+    12 bytes per output of the largest 32-token chunk."""
+    for N in (64, 128, 448, 8192):
+        for K in (64, 128, 192, 1216, 4096, 28672):
+            for M in (1, 2, 8, 16, 17, 32, 33, 70):
+                ws = gbb.gemm_mixed_w_64x64_workspace(N, K, M)
+                assert ws in (0, min(M, 32) * N * 12) or (M > 32 and ws % (N * 12) == 0 and ws <= 32 * N * 12), \
+                    (N, K, M, ws)
+    assert gbb.gemm_mixed_w_64x64_workspace(64, 96, 1) == 0      # not whole blocks
