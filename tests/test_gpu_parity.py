@@ -126,8 +126,11 @@ def test_decode_parity(N, K, M):
 # the last two have 384 tiles of 128 tokens x 512 rows: 48 per XCD, so each
 # XCD's last 16 tiles run as 64-token halves (with M = 1436 some second halves
 # start past the last token)
+# Large batches: one block column, 67 of them (the 64-column metadata window
+# reloads), a last row tile with one block row, and ragged token counts.
 PREFILL_CASES = [(64, 128, 33), (192, 384, 100), (128, 1280, 257), (320, 512, 129), (256, 4096, 600),
-                 (16384, 256, 1536), (16384, 256, 1436)]
+                 (16384, 256, 1536), (16384, 256, 1436), (576, 128, 1024), (576, 128 * 67, 1030),
+                 (320, 384, 2065)]
 
 
 @pytest.mark.parametrize("b", [1, 8])
