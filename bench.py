@@ -42,23 +42,30 @@ LAYER_COPIES_70B = 3      # 3 x 252 MB > 512 MiB
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode1_llama3_70b_layer_m1.md")
-DECODE_SOURCE = os.path.join(ROOT, "gemm_block_bit_amd", "csrc", "decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "gemm_block_bit_amd", "csrc", f) for f in ("decode.hip", "decode_common.h")]
+
+
+def decode_source_digest():
+    """sha256 over the decode kernel's sources (decode.hip, then decode_common.h)."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE
-    profile, or None when the decode kernel source has changed since."""
-    import hashlib
+    profile, or None when the decode kernel's sources have changed since."""
     try:
         fields = {}
         with open(TRAFFIC_PROFILE) as f:
             for line in f:
-                if ":" in line and line.startswith(("traffic_bytes_per_launch", "decode_hip_sha256")):
+                if ":" in line and line.startswith(("traffic_bytes_per_launch", "decode_source_sha256")):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        with open(DECODE_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-        if fields.get("decode_hip_sha256") != digest:
+        if fields.get("decode_source_sha256") != decode_source_digest():
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
