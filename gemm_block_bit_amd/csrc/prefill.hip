@@ -26,7 +26,6 @@
 // conflict-free 16-byte LDS read.  Workgroups are mapped XCD by XCD to
 // contiguous, grouped stretches of tiles so that each XCD's L2 sees the reuse
 // of activation rows and weight blocks.
-#include <atomic>
 
 #include "device.h"
 #include "internal.h"
@@ -286,16 +285,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-// Compute units of the current device, looked up once per device.
+// Compute units of the current device (the runtime answers from its cached
+// device properties, so this is cheap host work per launch).
 int compute_units() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v <= 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
   return v;
 }
 

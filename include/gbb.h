@@ -67,7 +67,9 @@ int gbb_version(void);
 /* ======================================================================== */
 
 /* Byte size of the packed image for an N x K matrix with the per-block
- * bitwidth map `bits` (host, uint8 [N/64][K/128], block-row major).  The size
+ * bitwidth map `bits` (host, uint8 [N/64][K/128], block-row major): the
+ * block-wise storage with a small per-block bitwidth record of the ScaleBITS
+ * explainer page, section 3.2, in the layout of layout.h.  The size
  * is a 64-byte header, then 256-byte aligned sections: one byte per block,
  * 4 * (blocks + 1) bytes of offsets, 256 bytes of scale/zero per block and
  * 64 * 128 * b / 8 = 1024 * b bytes of codes per block.  Returns 0 on a bad
@@ -126,10 +128,14 @@ gbb_status gbb_allocate_bits(const uint16_t* W, int N, int K, double target_bits
  * Errors: GBB_E_ARG. */
 gbb_status gbb_channel_order(const uint16_t* W, int N, int K, int32_t* row_order, int32_t* col_order);
 
-/* Check a host copy of an image header against N and K (GBB_E_FORMAT). */
+/* Check a host copy of an image header against N and K (GBB_E_FORMAT): the
+ * block-wise storage of the ScaleBITS explainer page, section 3.2 (version 1,
+ * 64x128 blocks) or its 64x64 variant of section 4.2 (version 2). */
 gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 
-/* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M); may be 0 (it is
+/* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M) (the fused product of
+ * the ScaleBITS explainer page, section 3.2, when its K range is split over
+ * workgroups); may be 0 (it is
  * M * N * 12 when K is split across workgroups: per output element an int64
  * fixed-point and an fp32 accumulator; for batches run as 32-token chunks,
  * that of the largest chunk).  The workspace must be zero-filled once before
@@ -237,8 +243,10 @@ gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, const uint16_t
                                  int path, void* stream);
 
 /* Debug exports over a device image, for bit-exactness tests.
- *   gbb_unpack_codes: q device uint8 [N][K], the codes.
- *   gbb_dequant: w32 device fp32 [N][K] = (q - z) * s (exact), and/or w16
+ *   gbb_unpack_codes: q device uint8 [N][K], the codes read back from the
+ *   block-wise storage (ScaleBITS explainer page, section 3.2).
+ *   gbb_dequant: the affine dequantization of the MixLLM page, section 2.1:
+ *   w32 device fp32 [N][K] = (q - z) * s (exact), and/or w16
  *   device fp16 [N][K] = its round-to-nearest-even (either may be NULL). */
 gbb_status gbb_unpack_codes(const void* image, int N, int K, uint8_t* q, void* stream);
 gbb_status gbb_dequant(const void* image, int N, int K, float* w32, uint16_t* w16,
@@ -269,7 +277,9 @@ gbb_status gbb_dequant_64x64(const void* image, int N, int K, float* w32, uint16
 /* Output-feature mixed format, W8 (symmetric) / W4 (asymmetric) x A8       */
 /* ======================================================================== */
 
-/* Byte size of the W4/W8 image for N x K with n8 8-bit rows (0 on error). */
+/* Byte size of the W4/W8 image for N x K with n8 8-bit rows (0 on error):
+ * the output-feature mixed format of the MixLLM page, sections 3.1.1 and
+ * 3.1.2, pre-packed as in section 3.3. */
 size_t gbb_w48_packed_bytes(int N, int K, int n8);
 
 /* Quantize and pack (host, synchronous, deterministic).

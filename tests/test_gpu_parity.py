@@ -375,6 +375,49 @@ def test_batched_independent_products(M):
         assert not torch.any(b._ws)
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_batched_graph_replays(M):
+    """A grouped launch captured in a HIP graph (as bench.py times it) and
+    replayed three times with eager work and synchronizations between the
+    replays: every replay equals the eager grouped call bit for bit and the
+    oracle within 2e-3; the shared workspace is clean after each."""
+    shapes = [(384, 1024), (1024, 4096), (256, 3584)]
+    calls, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        W = small(N, K, 110 + i)
+        bits = synth.random_bitmap(N, K, ALLOWED, 110 + i)
+        xh = rand_x(M, K, 120 + i)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev())
+        calls.append((packed(W, bits), N, K, to_dev(xh), y))
+        refs.append(bq.reference_gemm(xh, W, bits))
+    b = gbb.Batched(calls)
+    b.launch()
+    torch.cuda.synchronize()
+    eager = [c[4].clone() for c in calls]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        b.launch()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.launch()
+    for rep in range(3):
+        for c in calls:
+            c[4].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, N, K, _, y), e, ref in zip(calls, eager, refs):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16)), (rep, N, K)
+            assert rel_err(y, ref) <= TOL, (rep, N, K)
+        assert not torch.any(b._ws)
+        gbb.gemm_mixed_w(calls[1][0], calls[1][1], calls[1][2], calls[1][3])   # eager work between replays
+        torch.cuda.synchronize()
+    del g
+
+
 def test_batched_llama3_8b_layer_m1():
     """The Llama-3-8B layer's four launch groups (q|k|v, o, gate|up, down)
     as one grouped launch at M = 1, one checked row per block row."""
