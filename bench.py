@@ -414,13 +414,15 @@ def main():
             log(f"70B decode M={M}: {total_bytes / sm / 1e9:.0f} GB/s")
             del Lm
     host70 = L70.host
+    want_cpu = not args.quick and not args.no_cpu_baseline
+    oracle_inputs = {}   # host inputs of the extras, for the oracle timed beside them
     del L70
     torch.cuda.empty_cache()
 
     if "llama3_8b" in want:
         # ---------------- Llama-3-8B layers, decode M = 1 and 8 ----------------
         log("packing Llama-3-8B-shaped layer (qkv, o, gate_up, down)")
-        L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev)
+        L8 = DecodeLayerSet(torch, gbb, synth, synth.llama3_8b_proj, LAYER_COPIES_8B, 1, dev, keep_host=want_cpu)
         b8 = L8.layer_bytes * L8.copies
         s8, _, _ = time_graph(torch, lambda: L8.step(h()), args.steps, args.warmup)
         v8 = b8 / s8 / 1e9
@@ -440,6 +442,8 @@ def main():
         log(f"8B decode M=8: {b8 / s8b / 1e9:.0f} GB/s")
         del L8b
         extra["llama3_8b_layer_m1"] = e8
+        if want_cpu:
+            oracle_inputs["llama3_8b_layer"] = (L8.host, {1: s8 / L8.copies, 8: s8b / L8.copies})
 
         if "mixed_vs_uniform" in want:
             # ------- the same shapes with uniform 3- and 4-bit bitmaps, M = 1 -------
@@ -514,6 +518,8 @@ def main():
         extra["linear_4096_m1"] = {"us_per_launch": round(sl1 * 1e6 / len(lin), 2), "GBps": round(lb / sl1 / 1e9, 1),
                                    "weight_MB": round(weight_bytes(bits) / 1e6, 2)}
         log(f"4096x4096 M=1: {sl1 * 1e6 / len(lin):.2f} us/launch, {lb / sl1 / 1e9:.0f} GB/s")
+        if want_cpu:
+            oracle_inputs["linear_4096_m1"] = (img, bits, x1, sl1 / len(lin))
         del lin, d
         torch.cuda.empty_cache()
 
@@ -554,6 +560,9 @@ def main():
                            "fp16_library_gemm_on_dequantized_TFLOPs": round(fl / sl / 1e12, 1),
                            "moderate_batches": mid}
             log(f"prefill {p.name}: {fl / sp / 1e12:.0f} TFLOP/s (library fp16 GEMM {fl / sl / 1e12:.0f})")
+            if want_cpu:
+                oracle_inputs.setdefault("prefill_m2048", []).append(
+                    (p.name, p.N, p.K, img, synth.prefill_x(ORACLE_PREFILL_TOKENS, p.K, i), sp))
             del imgd, x, y, w16
             torch.cuda.empty_cache()
         extra["prefill_m2048_70b_mlp"] = pre
@@ -587,14 +596,17 @@ def main():
                             "frac_int8_peak": round(ops / sw / 1e12 / INT8_PEAK_TOPS, 3),
                             "weight_GBps": round(img.size / sw / 1e9, 1)}
             log(f"w44a8 M={M}: {w48[f'M{M}']}")
+            if want_cpu:
+                oracle_inputs.setdefault("w44a8", {"img": img})[M] = sw
         extra["w44a8_28672x8192"] = w48
         del imgd, rot
         torch.cuda.empty_cache()
 
     cpu = None
-    if not args.quick and not args.no_cpu_baseline:
+    if want_cpu:
         cpu = cpu_baseline(host70)
         extra["cpu_baseline_one_thread_o_proj_GBps"] = cpu_baseline_one_thread(host70)
+        extra["oracle_beside_extras"] = oracle_beside(oracle_inputs)
 
     out = {
         "metric": "fused dequant-GEMM: weight GB/s (%HBM peak) at M=1; TFLOP/s (%MFMA) at M=2048",
@@ -669,6 +681,97 @@ def cpu_baseline_one_thread(host):
         bq.gemm_fp64(x, w)
         t = time.perf_counter() - t0
     return round(weight_bytes(bits) / t / 1e9, 3)
+
+
+ORACLE_PREFILL_TOKENS = 256      # prefill: the oracle's product runs on this many of the 2048 tokens
+ORACLE_W48_SAMPLE = (256, 2048)  # W4.4A8: at most this many tokens x rows in the oracle's products
+
+
+def oracle_beside(inputs):
+    """The oracle timed beside each extra on its own inputs (host cores):
+    its unpack of the packed image and exact fp32 dequant (or, for W4.4A8,
+    its image reader and activation quantization) always in full, and its
+    fp64 / exact-integer products in full or on a stated sample scaled to
+    the whole call.  Each entry gives the oracle's seconds per call, the
+    GPU's, and their ratio."""
+    from oracle import blockquant as bq
+    from oracle import image as oimg
+    from oracle import w48 as ow
+
+    out = {}
+
+    def entry(t_oracle, t_gpu, sample):
+        return {"oracle_s": round(t_oracle, 3), "gpu_s": float(f"{t_gpu:.4g}"),
+                "gpu_speedup": round(t_oracle / t_gpu, 1), "sample": sample}
+
+    if "linear_4096_m1" in inputs:
+        img, bits, x1, t_gpu = inputs["linear_4096_m1"]
+        t0 = time.perf_counter()
+        d = oimg.read_block_image(img)
+        bq.gemm_fp64(x1, bq.dequant_fp32(d["q"], d["s16"], d["z16"]))
+        out["linear_4096_m1"] = entry(time.perf_counter() - t0, t_gpu, "the whole call")
+        log(f"oracle beside 4096x4096 M=1: {out['linear_4096_m1']}")
+    if "llama3_8b_layer" in inputs:
+        host, t_gpu = inputs["llama3_8b_layer"]
+        t_deq, t_mm = 0.0, {1: 0.0, 8: 0.0}
+        g = np.random.default_rng(7)
+        for (name, (N, K), img, bits) in host:
+            t0 = time.perf_counter()
+            d = oimg.read_block_image(img)
+            w = bq.dequant_fp32(d["q"], d["s16"], d["z16"])
+            t_deq += time.perf_counter() - t0
+            for M in (1, 8):
+                x = g.standard_normal((M, K)).astype(np.float16)
+                t0 = time.perf_counter()
+                bq.gemm_fp64(x, w)
+                t_mm[M] += time.perf_counter() - t0
+            del d, w
+        for M in (1, 8):
+            out[f"llama3_8b_layer_m{M}"] = entry(t_deq + t_mm[M], t_gpu[M],
+                                                 "one layer (q|k|v, o, gate|up, down), the whole call")
+            log(f"oracle beside 8B layer M={M}: {out[f'llama3_8b_layer_m{M}']}")
+    for (name, N, K, img, xs, t_gpu) in inputs.get("prefill_m2048", []):
+        t0 = time.perf_counter()
+        d = oimg.read_block_image(img)
+        w = bq.dequant_fp32(d["q"], d["s16"], d["z16"])
+        t_deq = time.perf_counter() - t0
+        del d
+        t0 = time.perf_counter()
+        bq.gemm_fp64(xs, w)
+        t_mm = (time.perf_counter() - t0) * (2048 / xs.shape[0])
+        del w
+        out[f"prefill_m2048_{name}"] = entry(t_deq + t_mm, t_gpu,
+                                             f"unpack + dequant in full; the fp64 product on {xs.shape[0]} of "
+                                             f"the 2048 tokens, scaled x{2048 // xs.shape[0]}")
+        log(f"oracle beside prefill {name}: {out[f'prefill_m2048_{name}']}")
+    if "w44a8" in inputs:
+        rec = inputs["w44a8"]
+        t0 = time.perf_counter()
+        qd = oimg.read_w48_image(rec["img"])
+        t_read = time.perf_counter() - t0
+        N, K = qd["N"], qd["K"]
+        Wz4 = qd["q4"].astype(np.int64) - np.repeat(qd["z4"].astype(np.int64), 128, axis=1)
+        for M in sorted(k for k in rec if isinstance(k, int)):
+            m_s, n_s = min(M, ORACLE_W48_SAMPLE[0]), ORACLE_W48_SAMPLE[1]
+            x = synth_activations(M, K)
+            t0 = time.perf_counter()
+            A_q, s_a = ow.quant_act(x)
+            t_q = time.perf_counter() - t0
+            n8s = max(1, n_s * qd["n8"] // N)
+            t0 = time.perf_counter()
+            ow.two_step(A_q[:m_s], s_a[:m_s], qd["q8"][:n8s].astype(np.int64), qd["s8"][:n8s])
+            ow.two_step(A_q[:m_s], s_a[:m_s], Wz4[:n_s - n8s], qd["s4"][:n_s - n8s])
+            t_mm = (time.perf_counter() - t0) * (M / m_s) * (N / n_s)
+            out[f"w44a8_m{M}"] = entry(t_read + t_q + t_mm, rec[M],
+                                       f"image read and activation quantization in full; the exact group products "
+                                       f"and scaling on {m_s} tokens x {n_s} rows, scaled to {M} x {N}")
+            log(f"oracle beside w44a8 M={M}: {out[f'w44a8_m{M}']}")
+    return out
+
+
+def synth_activations(M, K):
+    import synth
+    return synth.activations(M, K, synth.WL_W44A8, 0)
 
 
 if __name__ == "__main__":
