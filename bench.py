@@ -494,6 +494,24 @@ def main():
                 f"M=8 {b64 / s64b / 1e9:.0f} GB/s ({s64b * 1e6:.1f} us/step)")
             del L64, L64b
             torch.cuda.empty_cache()
+            # prefill, M = 2048, on the gate projection (14336 x 4096) in both formats
+            pf = {}
+            for bc, gen in ((128, synth.llama3_8b_proj), (64, synth.llama3_8b_proj64)):
+                p, W, bits = gen(4)
+                img, _, _ = gbb.pack_blocks(W, bits, block_cols=bc)
+                del W
+                imgd = torch.from_numpy(img).to(dev)
+                rot = Rotation([imgd] + [imgd.clone() for _ in range(11)])   # 12 copies > 256 MiB
+                x = torch.from_numpy(synth.prefill_x(2048, p.K, 4)).to(dev)
+                y = torch.empty((2048, p.N), dtype=torch.float16, device=dev)
+                call = gbb.gemm_mixed_w if bc == 128 else gbb.gemm_mixed_w_64x64
+                sp = time_eager(torch, lambda: call(rot.next(), p.N, p.K, x, out=y), 30, 30)
+                pf[f"blocks_64x{bc}"] = {"ms": round(sp * 1e3, 3),
+                                         "TFLOPs": round(2.0 * 2048 * p.N * p.K / sp / 1e12, 1)}
+                del rot, imgd, x, y
+                torch.cuda.empty_cache()
+            extra["blocks_64x64_8b"]["prefill_m2048_gate_14336x4096"] = pf
+            log(f"8B gate prefill M=2048: {pf}")
         del L8
         torch.cuda.empty_cache()
 

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     dequant,
     gemm_mixed_w,
     gemm_mixed_w_64x64,
+    gemm_mixed_w_64x64_path,
     gemm_mixed_w_64x64_workspace,
     gemm_mixed_w_batched_workspace,
     gemm_mixed_w_noalloc,

@@ -41,6 +41,7 @@ _SIGS = {
     "gbb_pack_blocks_64x64": (_i, [_vp, _i, _i, _vp, _vp, _vp, _u, _vp, _sz]),
     "gbb_gemm_mixed_w_64x64_workspace": (_sz, [_i, _i, _i]),
     "gbb_gemm_mixed_w_64x64": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "gbb_gemm_mixed_w_64x64_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
     "gbb_unpack_codes_64x64": (_i, [_vp, _i, _i, _vp, _vp]),
     "gbb_dequant_64x64": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "gbb_allocate_bits": (_i, [_vp, _i, _i, ctypes.c_double, ctypes.c_double, _vp]),
@@ -397,20 +398,27 @@ def gemm_mixed_w_64x64_workspace(N: int, K: int, M: int) -> int:
     return lib().gbb_gemm_mixed_w_64x64_workspace(N, K, M)
 
 
-def gemm_mixed_w_64x64(image, N: int, K: int, x, out=None, workspace=None):
-    """y = x . dequant(W)^T over a 64x64-block image (fp16 [M][N])."""
+def gemm_mixed_w_64x64_path(image, N: int, K: int, x, path: int, out=None, workspace=None):
+    """y = x . dequant(W)^T over a 64x64-block image (fp16 [M][N]); path 0
+    the library's choice, 1 the decode kernel (M <= 32), 2 the prefill
+    kernel."""
     torch = _torch()
     M = x.shape[0]
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M][{K}]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
-    need = gemm_mixed_w_64x64_workspace(N, K, M)
+    need = gemm_mixed_w_64x64_workspace(N, K, M) if path != 2 else 0
     ws = workspace if workspace is not None else _workspace(x.device, need)
-    _check(lib().gbb_gemm_mixed_w_64x64(
+    _check(lib().gbb_gemm_mixed_w_64x64_path(
         _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),
         _dev_ptr(y, torch.float16, "y"), M, ws.data_ptr() if ws is not None else None,
-        ws.numel() if ws is not None else 0, _stream(x)))
+        ws.numel() if ws is not None else 0, path, _stream(x)))
     return y
+
+
+def gemm_mixed_w_64x64(image, N: int, K: int, x, out=None, workspace=None):
+    """y = x . dequant(W)^T over a 64x64-block image (fp16 [M][N])."""
+    return gemm_mixed_w_64x64_path(image, N, K, x, 0, out, workspace)
 
 
 def quant_act_i8(x, ga: int | None = None):

@@ -107,8 +107,8 @@ extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
 }
 
 gbb_status gbb::check_gemm_args(const void* image, int N, int K, const uint16_t* x, const uint16_t* y, int M,
-                                int path) {
-  gbb_status st = check_block_args(image, N, K, M);
+                                int path, int bc) {
+  gbb_status st = check_block_args(image, N, K, M, bc);
   if (st != GBB_OK) return st;
   if (M == 0) return GBB_OK;
   if (!x || !y) return fail(GBB_E_ARG, "x and y must not be NULL");
@@ -275,6 +275,7 @@ namespace {
 
 size_t workspace64(int N, int K, int M) {
   if (M <= 32) return decode_plan64(N, K, M).ws_bytes;
+  if (!decode_in_chunks(N, M)) return 0;   // the prefill kernel
   size_t need = decode_plan64(N, K, 32).ws_bytes;   // 32-token chunks
   if (M % 32) need = std::max(need, decode_plan64(N, K, M % 32).ws_bytes);
   return need;
@@ -287,30 +288,37 @@ extern "C" size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M) {
   return workspace64(N, K, M);
 }
 
+extern "C" gbb_status gbb_gemm_mixed_w_64x64_path(const void* image, int N, int K, const uint16_t* x, uint16_t* y,
+                                                  int M, void* workspace, size_t ws_bytes, int path, void* stream) {
+  gbb_status st = check_gemm_args(image, N, K, x, y, M, path, 64);
+  if (st != GBB_OK || M == 0) return st;
+  const BlockImageView v = block_view(image, N, K, 64);
+  const bool chunks = path == 0 && decode_in_chunks(N, M);
+  const bool decode = path == 1 || (path == 0 && M <= 32);
+  if (chunks || decode) {
+    const size_t need = decode ? decode_plan64(N, K, M).ws_bytes : workspace64(N, K, M);
+    if (need) {
+      if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
+      if (ws_bytes < need) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+      if (!aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
+    }
+    for (int m0 = 0; m0 < M; m0 += 32) {   // one launch for M <= 32
+      const int mc = M - m0 < 32 ? M - m0 : 32;
+      st = device_status(launch_decode64(v, x + size_t(m0) * K, y + size_t(m0) * N, mc, workspace,
+                                         decode_plan64(N, K, mc), stream),
+                         "decode launch");
+      if (st != GBB_OK) return st;
+    }
+    return GBB_OK;
+  }
+  if (size_t(M) * size_t(K) >= (size_t(1) << 31))
+    return fail(GBB_E_SHAPE, "the prefill kernel takes M * K < 2^31 (M=%d K=%d)", M, K);
+  return device_status(launch_prefill(v, x, y, M, stream), "prefill launch");
+}
+
 extern "C" gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x, uint16_t* y, int M,
                                              void* workspace, size_t ws_bytes, void* stream) {
-  gbb_status st = check_block_args(image, N, K, M, 64);
-  if (st != GBB_OK || M == 0) return st;
-  if (!x || !y) return fail(GBB_E_ARG, "x and y must not be NULL");
-  if (!aligned16(x) || !aligned16(y)) return fail(GBB_E_ALIGN, "x and y must be 16-byte aligned");
-  const char* xb = reinterpret_cast<const char*>(x);
-  const char* yb = reinterpret_cast<const char*>(y);
-  if (xb < yb + size_t(M) * N * 2 && yb < xb + size_t(M) * K * 2) return fail(GBB_E_ARG, "x and y overlap");
-  const size_t need = workspace64(N, K, M);
-  if (need) {
-    if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
-    if (ws_bytes < need) return fail(GBB_E_SPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-    if (!aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
-  }
-  const BlockImageView v = block_view(image, N, K, 64);
-  for (int m0 = 0; m0 < M; m0 += 32) {   // one launch for M <= 32
-    const int mc = M - m0 < 32 ? M - m0 : 32;
-    st = device_status(launch_decode64(v, x + size_t(m0) * K, y + size_t(m0) * N, mc, workspace,
-                                       decode_plan64(N, K, mc), stream),
-                       "decode launch");
-    if (st != GBB_OK) return st;
-  }
-  return GBB_OK;
+  return gbb_gemm_mixed_w_64x64_path(image, N, K, x, y, M, workspace, ws_bytes, 0, stream);
 }
 
 extern "C" gbb_status gbb_unpack_codes_64x64(const void* image, int N, int K, uint8_t* q, void* stream) {

@@ -14,7 +14,7 @@ gbb_status ok();
 // Argument checks of gbb_gemm_mixed_w_path (path 0 = automatic), shared by
 // the entry points that run it.
 gbb_status check_gemm_args(const void* image, int N, int K, const uint16_t* x, const uint16_t* y, int M,
-                           int path);
+                           int path, int bc = 128);
 
 // IEEE binary16 <-> binary64, round-to-nearest-even (host).
 double half_to_double(uint16_t h);

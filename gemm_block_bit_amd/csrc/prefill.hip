@@ -285,6 +285,200 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64x64 blocks (version-2 image, the other GPU block size of the ScaleBITS
+// explainer page, section 4.2).  The same workgroup and tile as above; K
+// advances one 64-column block column per step.  A plane of width W is W
+// half-slots of 512 bytes: lane l's 8 bytes of half-slot j are two words d
+// whose field f holds the column pair c = 2 d + f / P of tile
+// u = 4 kt + rt = j P + f % P (P = 8 / W, kt = 0, 1).  So the B operand of
+// tile u takes words 0, 0, 1, 1 of half-slot u / P at fields u % P,
+// u % P + P, u % P, u % P + P.  Per wave the stage holds a block's codes
+// (up to eight half-slots, 4 KiB) and its scale/zero entries (1 KiB).
+constexpr int kStage64 = 5 * 64;   // u32x4 per wave
+
+template <int MT, class Refill>
+__device__ __forceinline__ void kstep64(int b, const u32x4* __restrict__ st, const u32x4* __restrict__ xb, int lane,
+                                        f32x4 (&acc)[MT][4], Refill&& refill) {
+  const int W0 = b == 3 ? 2 : (b >= 4 ? 4 : b);
+  const int W1 = b == 3 ? 1 : (b == 6 ? 2 : (b == 8 ? 4 : 0));
+  const int L0 = W0 == 4 ? 1 : (W0 == 2 ? 2 : 3);   // log2(8 / W0)
+  const int L1 = W1 == 4 ? 1 : (W1 == 2 ? 2 : 3);
+  const uint32_t M0 = ((1u << W0) - 1u) * 0x00010001u;
+  const uint32_t M1 = (((1u << W1) - 1u) * 0x00010001u) << W0;
+  const uint2* st2 = reinterpret_cast<const uint2*>(st);   // half-slot j: st2[64 j + lane]
+  const u32x4 sz = st[256 + lane];
+  half2v s2[4], z2[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const uint32_t e = sz[rt];
+    s2[rt] = as_half2((e & 0xffffu) * 0x00010001u);
+    const _Float16 nz = -((_Float16)1024.0f + __builtin_bit_cast(_Float16, (unsigned short)(e >> 16)));
+    z2[rt] = half2v{nz, nz};   // exact: an integer below 2048
+  }
+  auto deq = [&](int kt, u32x4 (&B)[4]) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int u = 4 * kt + rt;
+      const int P0 = 1 << L0, P1 = 1 << L1;
+      const uint2 w = st2[64 * (u >> L0) + lane];
+      const uint2 h = st2[64 * (W0 + (u >> L1)) + lane];
+      const uint32_t s0 = uint32_t(W0 * (u & (P0 - 1)));          // fields of column pairs 0 and 2
+      const uint32_t s0b = s0 + uint32_t(W0 * P0);                // 1 and 3 (8 bits higher)
+      const uint32_t r1 = uint32_t(W1 * (u & (P1 - 1)) - W0) & 31u;
+      const uint32_t r1b = uint32_t(W1 * (u & (P1 - 1)) + W1 * P1 - W0) & 31u;
+      const uint32_t src0[4] = {w.x, w.x, w.y, w.y}, src1[4] = {h.x, h.x, h.y, h.y};
+      const uint32_t sh0[4] = {s0, s0b, s0, s0b}, sh1[4] = {r1, r1b, r1, r1b};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = ((src0[k] >> sh0[k]) & M0) | kMagicPair;
+        const uint32_t q = (__builtin_amdgcn_alignbit(src1[k], src1[k], sh1[k]) & M1) | lo;
+        o[k] = as_u32((as_half2(q) + z2[rt]) * s2[rt]);
+      }
+      B[rt] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+  u32x4 B[2][4];
+  deq(0, B[0]);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    if (kt == 0) {
+      deq(1, B[1]);
+      refill();   // every code slot of the block has been read
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const half8 A = __builtin_bit_cast(half8, xb[(2 * mt + kt) * 64 + lane]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = mfma16(A, __builtin_bit_cast(half8, B[kt][rt]), acc[mt][rt]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+    }
+  }
+}
+
+// One tile of MT 16-token tiles (tokens m0 ...) x 512 rows of a 64x64 image.
+template <int MT>
+__device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int tn, u32x4 (*xs)[kMT * 2 * 64],
+                                               u32x4 (*stage)[kStage64]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const bool has_rows = tn * kWaves + wave < a.nbr;
+  const int br = min(tn * kWaves + wave, a.nbr - 1);
+
+  // activation fragments of one 64-column step: (mt, kt) at 1 KiB (2 mt + kt)
+  constexpr int kFrag = MT * 2 / kWaves;
+  uint32_t xoff[kFrag];
+#pragma unroll
+  for (int f = 0; f < kFrag; ++f) {
+    const int fr = kFrag * wave + f, mt = fr >> 1, kt = fr & 1;
+    const int m = min(m0 + 16 * mt + r16, a.M - 1);
+    xoff[f] = uint32_t((size_t(m) * a.K + 32 * kt + 8 * g) * 2);
+  }
+  const uint32_t xs_lds = lds_addr(&xs[0][0]);
+  auto load_x = [&](int bc, int buf) {
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+      dma16(a.x, xoff[f] + uint32_t(bc) * 128,
+            xs_lds + uint32_t(buf) * (kMT * 2 * 1024) + uint32_t(kFrag * wave + f) * 1024);
+  };
+
+  const size_t row_blk = size_t(br) * a.nbc;
+  int bvec = 0, ovec = 0;
+  auto load_meta = [&](int col0) {
+    const int c = min(col0 + lane, a.nbc - 1);
+    bvec = int(a.bits[row_blk + c]);
+    ovec = int(a.offs[row_blk + c]);
+  };
+  const uint32_t st_lds = uint32_t(uniform(int(lds_addr(&stage[wave][0]))));
+  auto load_block = [&](int bc) {   // codes (b half-slots) and scale/zero of block (br, bc)
+    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
+    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc & 63))) * 512;
+    for (int q = 0; q + 1 < bj; q += 2) dma16(cb + 512 * q, 16 * lane, st_lds + 512 * q);   // two half-slots
+    if (bj & 1) {   // the last half-slot: 512 bytes from the first 32 lanes
+      if (lane < 32) dma16(cb + 512 * (bj - 1), 16 * lane, st_lds + 512 * (bj - 1));
+    }
+    dma16(a.sz + (row_blk + bc) * 64, 16 * r16, st_lds + 4096);
+  };
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  load_meta(0);
+  load_x(0, 0);
+  load_block(0);
+  for (int bc = 0; bc < a.nbc; ++bc) {
+    const int buf = bc & 1;
+    wait_all_loads();   // this wave's fragments and block of step bc
+    __syncthreads();    // every wave's fragments of step bc are in LDS; step bc - 1's reads are done
+    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
+    const bool more = bc + 1 < a.nbc;
+    if (more) {
+      load_x(bc + 1, buf ^ 1);
+      if (((bc + 1) & 63) == 0) load_meta(bc + 1);
+    }
+    auto refill = [&]() {
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        load_block(bc + 1);
+      }
+    };
+    kstep64<MT>(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
+  }
+  if (!has_rows) return;
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 16 * mt + 4 * g + v;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) a.y[size_t(m) * a.N + br * 64 + 16 * rt + r16] = (_Float16)acc[mt][rt][v];
+    }
+}
+
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill64_kernel(
+    PrefillArgs a) {
+  __shared__ u32x4 xs[2][kMT * 2 * 64];        // activations, double buffered: 16 KiB per 64-column step
+  __shared__ u32x4 stage[kWaves][kStage64];     // per wave: codes (4 KiB) + scale/zero (1 KiB)
+  const int bid = blockIdx.x;
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, bid & 7);
+  const int j = bid >> 3, whole = w.count - w.split;
+  int t, half = -1;
+  if (j < whole) {
+    t = w.first + j;
+  } else {
+    const int v = j - whole;
+    if (v >= 2 * w.split) return;
+    t = w.first + whole + (v >> 1);
+    half = v & 1;
+  }
+  const int gsize = kGroupM * a.tiles_n;
+  const int first_m = (t / gsize) * kGroupM;
+  const int gm = min(kGroupM, a.tiles_m - first_m);
+  const int tm = first_m + (t % gsize) % gm;
+  const int tn = (t % gsize) / gm;
+  if (half < 0 && a.M > kBM / 2) {
+    prefill64_tile<kMT>(a, tm * kBM, tn, xs, stage);
+  } else if (half < 0) {
+    prefill64_tile<kMT / 2>(a, tm * kBM, tn, xs, stage);
+  } else {
+    const int m0 = tm * kBM + half * (kBM / 2);
+    if (m0 >= a.M) return;
+    prefill64_tile<kMT / 2>(a, m0, tn, xs, stage);
+  }
+}
+
 // Compute units of the current device (the runtime answers from its cached
 // device properties, so this is cheap host work per launch).
 int compute_units() {
@@ -325,7 +519,10 @@ int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int
     items = max(items, w.count + w.split);
   }
   const dim3 grid(unsigned(8 * items)), block(kWaves * 64);
-  hipLaunchKernelGGL(prefill_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
+  if (im.bc == 64)
+    hipLaunchKernelGGL(prefill64_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(prefill_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }
 

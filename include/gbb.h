@@ -263,12 +263,20 @@ size_t gbb_packed_bytes_64x64(const uint8_t* bits, int N, int K);
 gbb_status gbb_pack_blocks_64x64(const uint16_t* W, int N, int K, const uint8_t* bits,
                                  uint16_t* scale, uint16_t* zero, unsigned flags,
                                  void* image, size_t image_cap);
-/* M <= 32 runs the decode kernels on 64x64 blocks; larger M runs them in
- * 32-token chunks (one launch each). */
+/* y = x . dequant(W)^T over a version-2 image, with the arguments, layout,
+ * workspace rules and errors of gbb_gemm_mixed_w / gbb_gemm_mixed_w_path
+ * (K % 64 == 0).  M <= 32 runs the 64x64 decode kernels; larger M runs the
+ * 64x64 prefill kernel (M * K < 2^31), or the decode kernels in 32-token
+ * chunks where the prefill grid would leave most compute units idle (the
+ * same rule as for 64x128 blocks).  path: 0 that choice, 1 the decode
+ * kernel (M <= 32), 2 the prefill kernel. */
 size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M);
 gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x,
                                   uint16_t* y, int M, void* workspace, size_t ws_bytes,
                                   void* stream);
+gbb_status gbb_gemm_mixed_w_64x64_path(const void* image, int N, int K, const uint16_t* x,
+                                       uint16_t* y, int M, void* workspace, size_t ws_bytes,
+                                       int path, void* stream);
 gbb_status gbb_unpack_codes_64x64(const void* image, int N, int K, uint8_t* q, void* stream);
 gbb_status gbb_dequant_64x64(const void* image, int N, int K, float* w32, uint16_t* w16,
                              void* stream);

@@ -907,3 +907,49 @@ def test_64x64_llama3_8b_layer_decode(i):
         y = gbb.gemm_mixed_w_64x64(img, p.N, p.K, to_dev(x)).cpu().numpy()
         ref = bq.reference_rows(x, W, bits, rows, block_cols=64)
         assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL, M
+
+
+# the 64x64 prefill kernel, forced: ragged shapes, one block column, 67 block
+# columns (the 64-column metadata window reloads), and 16384 x 128 at
+# M = 1436 (each XCD's last tiles run as 64-token halves, some past the end)
+PREFILL64_CASES = [(64, 64, 33), (192, 320, 100), (128, 1280, 257), (320, 4096, 130), (576, 64 * 67, 600),
+                   (16384, 128, 1436)]
+
+
+@pytest.mark.parametrize("N,K,M", PREFILL64_CASES)
+def test_64x64_prefill_parity(N, K, M):
+    W = small(N, K, N * 3 + K)
+    bits = synth.random_bitmap64(N, K, ALLOWED, N + 5 * M)
+    x = rand_x(M, K, M + 11)
+    y = gbb.gemm_mixed_w_64x64_path(packed64(W, bits), N, K, to_dev(x), 2)
+    assert rel_err(y, bq.reference_gemm(x, W, bits, block_cols=64)) <= TOL
+
+
+def test_64x64_prefill_one_hot_exact():
+    """One-hot activations through the 64x64 prefill kernel give fp16(w')
+    exactly (every bitwidth, both halves of each word)."""
+    N, K, M = 192, 1216, 100
+    W = small(N, K, 33)
+    bits = synth.random_bitmap64(N, K, ALLOWED, 33)
+    ks = np.random.default_rng(5).choice(K, size=M, replace=False)
+    x = np.zeros((M, K), np.float16)
+    x[np.arange(M), ks] = 1
+    y = gbb.gemm_mixed_w_64x64_path(packed64(W, bits), N, K, to_dev(x), 2).cpu().numpy()
+    q, s16, z16 = bq.quantize_blocks(W, bits, block_cols=64)
+    w16 = bq.dequant_fp16(q, s16, z16)
+    assert np.array_equal(y.view(np.uint16), w16[:, ks].T.view(np.uint16))
+
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_64x64_llama3_8b_prefill(i):
+    """Llama-3-8B q, gate and down projections with the mixed 64x64 bitmap at
+    M = 2048 (the prefill kernel by the library's own choice), one checked
+    row per block row."""
+    p, W, bits = synth.llama3_8b_proj64(i)
+    img = packed64(W, bits)
+    rows = one_row_per_block_row(p.N, 7 + i)
+    x = synth.prefill_x(2048, p.K, i)
+    assert gbb.gemm_mixed_w_64x64_workspace(p.N, p.K, 2048) == 0   # not decode chunks
+    y = gbb.gemm_mixed_w_64x64(img, p.N, p.K, to_dev(x)).cpu().numpy()
+    ref = bq.reference_rows(x, W, bits, rows, block_cols=64)
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
