@@ -42,6 +42,8 @@ _SIGS = {
     "gbb_gemm_mixed_w_64x64_workspace": (_sz, [_i, _i, _i]),
     "gbb_gemm_mixed_w_64x64": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "gbb_gemm_mixed_w_64x64_path": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _sz, _i, _vp]),
+    "gbb_gemm_mixed_w_path_workspace": (_sz, [_i, _i, _i, _i]),
+    "gbb_gemm_mixed_w_64x64_path_workspace": (_sz, [_i, _i, _i, _i]),
     "gbb_unpack_codes_64x64": (_i, [_vp, _i, _i, _vp, _vp]),
     "gbb_dequant_64x64": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "gbb_allocate_bits": (_i, [_vp, _i, _i, ctypes.c_double, ctypes.c_double, _vp]),
@@ -257,7 +259,7 @@ def gemm_mixed_w_path(image, N: int, K: int, x, path: int, out=None, workspace=N
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M][{K}]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
-    need = gemm_mixed_w_workspace(N, K, M) if path != 2 else 0   # 0 when the call needs none
+    need = lib().gbb_gemm_mixed_w_path_workspace(N, K, M, path)   # 0 when the call needs none
     ws = workspace if workspace is not None else _workspace(x.device, need)
     _check(lib().gbb_gemm_mixed_w_path(
         _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),
@@ -407,7 +409,7 @@ def gemm_mixed_w_64x64_path(image, N: int, K: int, x, path: int, out=None, works
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [M][{K}]")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
-    need = gemm_mixed_w_64x64_workspace(N, K, M) if path != 2 else 0
+    need = lib().gbb_gemm_mixed_w_64x64_path_workspace(N, K, M, path)
     ws = workspace if workspace is not None else _workspace(x.device, need)
     _check(lib().gbb_gemm_mixed_w_64x64_path(
         _dev_ptr(image, torch.uint8, "image"), N, K, _dev_ptr(x, torch.float16, "x"),

@@ -76,15 +76,17 @@ W48ImageView w48_view(const void* image, int N, int K, int n8) {
 }
 
 // For 32 < M the prefill kernel gives each CU one tile of 128 tokens x 512
-// rows over the whole of K and does not split K, so few tiles leave most CUs
-// idle (the Llama-3-70B down projection, 8192 x 28672, has 16 tiles at
-// M <= 128: ~0.8 ms whatever M is).  When ceil(M / 32) chunks of the prefill
-// grid still fit in one wave of CUs, the decode kernels run the batch in
-// 32-token chunks instead; each chunk rereads the weights, but at 48 us per
-// chunk on that shape that is far cheaper.
-bool decode_in_chunks(int N, int M) {
+// rows, and when the tiles would fill at most half of the CUs it cuts each
+// tile's K range into segments (prefill_plan).  Only when even the split
+// grid fills at most half of the CUs (small matrices: few block rows and a
+// short K) does the batch run as ceil(M / 32) decode launches of 32 tokens
+// instead.  The split prefill wins on every Llama-3 shape measured (70B
+// down projection: M = 64, 128, 256 in 71, 95, 156 us against 112, 230,
+// 432 us as decode chunks).
+bool decode_in_chunks(int N, int K, int M, int bc) {
   if (M <= 32) return false;
-  return size_t((M + 31) / 32) * size_t(prefill_tiles(N, M)) <= size_t(device_compute_units());
+  const PrefillPlan p = prefill_plan(N, K, M, bc, SIZE_MAX);
+  return size_t(2) * size_t(p.tiles) * size_t(p.kseg) <= size_t(device_compute_units());
 }
 
 // Workspace of the decode launches of a batch of M tokens run as 32-token
@@ -95,15 +97,33 @@ size_t chunked_workspace(int N, int K, int M) {
   return need;
 }
 
+// The prefill kernel, with the K split that the caller's workspace holds (none
+// without one: the call then runs unsplit, as it would on any workspace too
+// small for the split).
+gbb_status run_prefill(const BlockImageView& v, const uint16_t* x, uint16_t* y, int M, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  const PrefillPlan plan = prefill_plan(v.N, v.K, M, v.bc, workspace && aligned16(workspace) ? ws_bytes : 0);
+  return device_status(launch_prefill(v, x, y, M, workspace, plan, stream), "prefill launch");
+}
+
 }  // namespace
 
 extern "C" int gbb_version(void) { return 100; }
 
 extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
   if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % kGroup) return 0;
-  if (M > 32) return decode_in_chunks(N, M) ? chunked_workspace(N, K, M) : 0;
+  if (M > 32)
+    return decode_in_chunks(N, K, M, kGroup) ? chunked_workspace(N, K, M) : prefill_plan(N, K, M, kGroup, SIZE_MAX).ws_bytes;
   const DecodePlan p = decode_plan(N, K, M);
   return p.ws_bytes;
+}
+
+extern "C" size_t gbb_gemm_mixed_w_path_workspace(int N, int K, int M, int path) {
+  if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % kGroup) return 0;
+  if (path == 0) return gbb_gemm_mixed_w_workspace(N, K, M);
+  if (path == 1) return M <= 32 ? decode_plan(N, K, M).ws_bytes : 0;
+  if (path == 2) return prefill_plan(N, K, M, kGroup, SIZE_MAX).ws_bytes;
+  return 0;
 }
 
 gbb_status gbb::check_gemm_args(const void* image, int N, int K, const uint16_t* x, const uint16_t* y, int M,
@@ -126,7 +146,7 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
   gbb_status st = check_gemm_args(image, N, K, x, y, M, path);
   if (st != GBB_OK || M == 0) return st;
   const BlockImageView v = block_view(image, N, K);
-  if (path == 0 && decode_in_chunks(N, M)) {
+  if (path == 0 && decode_in_chunks(N, K, M, kGroup)) {
     const size_t need = chunked_workspace(N, K, M);
     if (need) {
       if (!workspace) return fail(GBB_E_ARG, "workspace of %zu bytes is required", need);
@@ -155,7 +175,7 @@ extern "C" gbb_status gbb_gemm_mixed_w_path(const void* image, int N, int K, con
   }
   if (size_t(M) * size_t(K) >= (size_t(1) << 31))
     return fail(GBB_E_SHAPE, "the prefill kernel takes M * K < 2^31 (M=%d K=%d)", M, K);
-  return device_status(launch_prefill(v, x, y, M, stream), "prefill launch");
+  return run_prefill(v, x, y, M, workspace, ws_bytes, stream);
 }
 
 extern "C" gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x, uint16_t* y, int M,
@@ -275,7 +295,7 @@ namespace {
 
 size_t workspace64(int N, int K, int M) {
   if (M <= 32) return decode_plan64(N, K, M).ws_bytes;
-  if (!decode_in_chunks(N, M)) return 0;   // the prefill kernel
+  if (!decode_in_chunks(N, K, M, 64)) return prefill_plan(N, K, M, 64, SIZE_MAX).ws_bytes;   // the prefill kernel
   size_t need = decode_plan64(N, K, 32).ws_bytes;   // 32-token chunks
   if (M % 32) need = std::max(need, decode_plan64(N, K, M % 32).ws_bytes);
   return need;
@@ -288,12 +308,20 @@ extern "C" size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M) {
   return workspace64(N, K, M);
 }
 
+extern "C" size_t gbb_gemm_mixed_w_64x64_path_workspace(int N, int K, int M, int path) {
+  if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % 64) return 0;
+  if (path == 0) return workspace64(N, K, M);
+  if (path == 1) return M <= 32 ? decode_plan64(N, K, M).ws_bytes : 0;
+  if (path == 2) return prefill_plan(N, K, M, 64, SIZE_MAX).ws_bytes;
+  return 0;
+}
+
 extern "C" gbb_status gbb_gemm_mixed_w_64x64_path(const void* image, int N, int K, const uint16_t* x, uint16_t* y,
                                                   int M, void* workspace, size_t ws_bytes, int path, void* stream) {
   gbb_status st = check_gemm_args(image, N, K, x, y, M, path, 64);
   if (st != GBB_OK || M == 0) return st;
   const BlockImageView v = block_view(image, N, K, 64);
-  const bool chunks = path == 0 && decode_in_chunks(N, M);
+  const bool chunks = path == 0 && decode_in_chunks(N, K, M, 64);
   const bool decode = path == 1 || (path == 0 && M <= 32);
   if (chunks || decode) {
     const size_t need = decode ? decode_plan64(N, K, M).ws_bytes : workspace64(N, K, M);
@@ -313,7 +341,7 @@ extern "C" gbb_status gbb_gemm_mixed_w_64x64_path(const void* image, int N, int 
   }
   if (size_t(M) * size_t(K) >= (size_t(1) << 31))
     return fail(GBB_E_SHAPE, "the prefill kernel takes M * K < 2^31 (M=%d K=%d)", M, K);
-  return device_status(launch_prefill(v, x, y, M, stream), "prefill launch");
+  return run_prefill(v, x, y, M, workspace, ws_bytes, stream);
 }
 
 extern "C" gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x, uint16_t* y, int M,

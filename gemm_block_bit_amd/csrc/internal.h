@@ -52,7 +52,15 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
 constexpr int kMaxBatch = 32;
 int launch_decode_batch(int n, const BlockImageView* ims, const uint16_t* const* x, uint16_t* const* y, int M,
                         const DecodePlan* plans, void* const* workspaces, void* stream);
-int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream);
+struct PrefillPlan {
+  int kseg, seg_cols, tiles;
+  size_t ws_bytes;   // kseg fp32 partials of y when kseg > 1
+};
+// The prefill launch for (N, K, M) on blocks of bc columns with a workspace
+// of ws_bytes (a K split only when its counts and partials fit).
+PrefillPlan prefill_plan(int N, int K, int M, int bc, size_t ws_bytes);
+int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* workspace,
+                   const PrefillPlan& plan, void* stream);
 // 64x64-block images, M <= 32: the plan (seg_cols and nbc in 64-column
 // blocks, one block row per workgroup) and the launch.
 DecodePlan decode_plan64(int N, int K, int M);

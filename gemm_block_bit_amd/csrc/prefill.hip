@@ -48,7 +48,9 @@ struct PrefillArgs {
   const uint8_t* codes;
   const _Float16* x;
   _Float16* y;
+  float* part;       // K split: fp32 partial y per segment [kseg][M][N] (zero between calls)
   int N, K, M, nbr, nbc, tiles_m, tiles_n, per_xcd, cus_xcd;
+  int kseg, seg_cols;   // K segments per tile (1: no split) and block columns per segment
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -154,11 +156,87 @@ __host__ __device__ inline XcdWork xcd_work(int ntiles, int per_xcd, int cus_xcd
   return w;
 }
 
+// The results of one wave (block row br, tokens m0 + 16 mt + 4 g + v) of a
+// tile: rounded to fp16 and stored, or with a K split stored as this
+// segment's fp32 partials (split_reduce_kernel adds them afterwards).
+template <int MT>
+__device__ __forceinline__ void tile_epilogue(const PrefillArgs& a, const f32x4 (&acc)[MT][4], int m0, int br,
+                                              bool has_rows, int seg) {
+  if (!has_rows) return;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  float* pp = a.part + size_t(seg) * size_t(a.M) * size_t(a.N);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 16 * mt + 4 * g + v;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const size_t o = size_t(m) * a.N + br * 64 + 16 * rt + r16;
+        if (a.kseg == 1)
+          a.y[o] = (_Float16)acc[mt][rt][v];
+        else
+          pp[o] = acc[mt][rt][v];
+      }
+    }
+}
+
+// y = the sum of the kseg partials, in segment order (so the result does not
+// depend on the order the segments ran in), rounded once; the partials are
+// cleared, so the workspace is zero again after the call.  Four outputs per
+// thread (N is a multiple of 64).
+__global__ __launch_bounds__(256) void split_reduce_kernel(float* part, _Float16* y, size_t quads, int kseg) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= quads) return;
+  f32x4* p4 = reinterpret_cast<f32x4*>(part);
+  f32x4 t = p4[i];
+  p4[i] = f32x4{0, 0, 0, 0};
+  for (int sg = 1; sg < kseg; ++sg) {
+    t += p4[size_t(sg) * quads + i];
+    p4[size_t(sg) * quads + i] = f32x4{0, 0, 0, 0};
+  }
+  typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+  reinterpret_cast<half4v*>(y)[i] = half4v{(_Float16)t[0], (_Float16)t[1], (_Float16)t[2], (_Float16)t[3]};
+}
+
+// Work item j of XCD x: a whole tile (t, seg) of the K split, or one 64-token
+// half of a tile of the last round (no K split then).  Returns false for
+// items past the XCD's work.
+struct WorkItem {
+  int tm, tn, m0, seg, tile, half;
+};
+__device__ __forceinline__ bool work_item(const PrefillArgs& a, int bid, int bm, WorkItem& it) {
+  const int ntiles = a.tiles_m * a.tiles_n * a.kseg;
+  const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, bid & 7);
+  const int j = bid >> 3, whole = w.count - (a.kseg == 1 ? w.split : 0);
+  int t;
+  it.half = -1;
+  if (j < whole) {
+    t = w.first + j;
+  } else {
+    const int v = j - whole;
+    if (a.kseg != 1 || v >= 2 * w.split) return false;
+    t = w.first + whole + (v >> 1);
+    it.half = v & 1;
+  }
+  it.seg = t % a.kseg;
+  t /= a.kseg;
+  it.tile = t;
+  const int gsize = kGroupM * a.tiles_n;
+  const int first_m = (t / gsize) * kGroupM;
+  const int gm = min(kGroupM, a.tiles_m - first_m);
+  it.tm = first_m + (t % gsize) % gm;
+  it.tn = (t % gsize) / gm;
+  it.m0 = it.tm * bm + (it.half > 0 ? bm / 2 : 0);
+  return it.half < 0 || it.m0 < a.M;
+}
+
 // One tile of MT 16-token tiles (tokens m0 ...) x 512 rows (block rows
 // 8 tn ...): wave w owns block row 8 tn + w.
 template <int MT>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int tn, u32x4 (*xs)[kMT * 4 * 64],
-                                             u32x4 (*stage)[9 * 64]) {
+                                             u32x4 (*stage)[9 * 64], int seg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const bool has_rows = tn * kWaves + wave < a.nbr;
@@ -186,6 +264,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int t
   };
 
   // this wave's block row: bitwidths and code offsets 64 columns at a time
+  // this workgroup's K segment: block columns [bc0, bc1); bitwidths and
+  // offsets come 64 block columns at a time from window base wb
+  const int bc0 = seg * a.seg_cols, bc1 = min(a.nbc, bc0 + a.seg_cols);
+  int wb = bc0;
   const size_t row_blk = size_t(br) * a.nbc;
   int bvec = 0, ovec = 0;
   auto load_meta = [&](int col0) {
@@ -195,8 +277,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int t
   };
   const uint32_t st_lds = uint32_t(uniform(int(lds_addr(&stage[wave][0]))));
   auto load_block = [&](int bc) {   // codes and scale/zero of block (br, bc) into the stage
-    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
-    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc & 63))) * 1024;
+    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc - wb));
+    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc - wb))) * 1024;
     for (int q = 0; q < bj; ++q) dma16(cb + 1024 * q, 16 * lane, st_lds + 1024 * q);
     dma16(a.sz + (row_blk + bc) * 64, 16 * r16, st_lds + 8192);
   };
@@ -207,18 +289,21 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int t
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  load_meta(0);
-  load_x(0, 0);
-  load_block(0);
-  for (int bc = 0; bc < a.nbc; ++bc) {
-    const int buf = bc & 1;
+  load_meta(wb);
+  load_x(bc0, 0);
+  load_block(bc0);
+  for (int bc = bc0; bc < bc1; ++bc) {
+    const int buf = (bc - bc0) & 1;
     wait_all_loads();   // this wave's fragments and block of step bc
     __syncthreads();    // every wave's fragments of step bc are in LDS; step bc - 1's reads are done
-    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));   // before the next 64 columns' metadata
-    const bool more = bc + 1 < a.nbc;
+    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc - wb));   // before the next window
+    const bool more = bc + 1 < bc1;
     if (more) {
       load_x(bc + 1, buf ^ 1);
-      if (((bc + 1) & 63) == 0) load_meta(bc + 1);
+      if (bc + 1 - wb == 64) {
+        wb += 64;
+        load_meta(wb);
+      }
     }
     // the next block's codes go into the stage as soon as this block's last
     // code slot has been read (inside the step, before its last MFMAs)
@@ -231,18 +316,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int m0, int t
     };
     kstep<MT>(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
   }
-  if (!has_rows) return;
-
-  // lane holds D[token 4 g + v][row r16] of each 16x16 tile
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + 16 * mt + 4 * g + v;
-      if (m >= a.M) continue;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a.y[size_t(m) * a.N + br * 64 + 16 * rt + r16] = (_Float16)acc[mt][rt][v];
-    }
+  tile_epilogue<MT>(a, acc, m0, br, has_rows, seg);
 }
 
 
@@ -254,34 +328,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
   // XCD-aware tile order: the hardware deals workgroups round robin to the 8
   // XCDs, so workgroup i runs on XCD i % 8; give each XCD a contiguous range
-  // of tiles, walked in groups of kGroupM token tiles, whole tiles first and
-  // the split halves (if any) last.
-  const int bid = blockIdx.x;
-  const int ntiles = a.tiles_m * a.tiles_n;
-  const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, bid & 7);
-  const int j = bid >> 3, whole = w.count - w.split;
-  int t, half = -1;
-  if (j < whole) {
-    t = w.first + j;
-  } else {
-    const int v = j - whole;
-    if (v >= 2 * w.split) return;
-    t = w.first + whole + (v >> 1);
-    half = v & 1;
-  }
-  const int gsize = kGroupM * a.tiles_n;
-  const int first_m = (t / gsize) * kGroupM;
-  const int gm = min(kGroupM, a.tiles_m - first_m);
-  const int tm = first_m + (t % gsize) % gm;
-  const int tn = (t % gsize) / gm;
-  if (half < 0 && a.M > kBM / 2) {
-    prefill_tile<kMT>(a, tm * kBM, tn, xs, stage);
-  } else if (half < 0) {   // at most 64 tokens: the tile's first half holds them all
-    prefill_tile<kMT / 2>(a, tm * kBM, tn, xs, stage);
-  } else {
-    const int m0 = tm * kBM + half * (kBM / 2);
-    if (m0 >= a.M) return;
-    prefill_tile<kMT / 2>(a, m0, tn, xs, stage);
+  // of work items (tiles, or K segments of tiles), walked in groups of
+  // kGroupM token tiles, whole tiles first and the split halves (if any)
+  // last.
+  WorkItem it;
+  if (!work_item(a, int(blockIdx.x), kBM, it)) return;
+  // the item is the same for the whole workgroup: keep it in scalar registers
+  const int m0 = uniform(it.m0), tn = uniform(it.tn), seg = uniform(it.seg);
+  if (it.half < 0 && a.M - m0 > kBM / 2) {
+    prefill_tile<kMT>(a, m0, tn, xs, stage, seg);
+  } else {   // a 64-token half, or a tile whose tokens fit in its first half
+    prefill_tile<kMT / 2>(a, m0, tn, xs, stage, seg);
   }
 }
 
@@ -364,7 +421,7 @@ __device__ __forceinline__ void kstep64(int b, const u32x4* __restrict__ st, con
 // One tile of MT 16-token tiles (tokens m0 ...) x 512 rows of a 64x64 image.
 template <int MT>
 __device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int tn, u32x4 (*xs)[kMT * 2 * 64],
-                                               u32x4 (*stage)[kStage64]) {
+                                               u32x4 (*stage)[kStage64], int seg) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const bool has_rows = tn * kWaves + wave < a.nbr;
@@ -387,6 +444,10 @@ __device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int
             xs_lds + uint32_t(buf) * (kMT * 2 * 1024) + uint32_t(kFrag * wave + f) * 1024);
   };
 
+  // this workgroup's K segment: block columns [bc0, bc1); bitwidths and
+  // offsets come 64 block columns at a time from window base wb
+  const int bc0 = seg * a.seg_cols, bc1 = min(a.nbc, bc0 + a.seg_cols);
+  int wb = bc0;
   const size_t row_blk = size_t(br) * a.nbc;
   int bvec = 0, ovec = 0;
   auto load_meta = [&](int col0) {
@@ -396,8 +457,8 @@ __device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int
   };
   const uint32_t st_lds = uint32_t(uniform(int(lds_addr(&stage[wave][0]))));
   auto load_block = [&](int bc) {   // codes (b half-slots) and scale/zero of block (br, bc)
-    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
-    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc & 63))) * 512;
+    const int bj = uniform(__builtin_amdgcn_readlane(bvec, bc - wb));
+    const uint8_t* cb = a.codes + size_t(uniform(__builtin_amdgcn_readlane(ovec, bc - wb))) * 512;
     for (int q = 0; q + 1 < bj; q += 2) dma16(cb + 512 * q, 16 * lane, st_lds + 512 * q);   // two half-slots
     if (bj & 1) {   // the last half-slot: 512 bytes from the first 32 lanes
       if (lane < 32) dma16(cb + 512 * (bj - 1), 16 * lane, st_lds + 512 * (bj - 1));
@@ -411,18 +472,21 @@ __device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  load_meta(0);
-  load_x(0, 0);
-  load_block(0);
-  for (int bc = 0; bc < a.nbc; ++bc) {
-    const int buf = bc & 1;
+  load_meta(wb);
+  load_x(bc0, 0);
+  load_block(bc0);
+  for (int bc = bc0; bc < bc1; ++bc) {
+    const int buf = (bc - bc0) & 1;
     wait_all_loads();   // this wave's fragments and block of step bc
     __syncthreads();    // every wave's fragments of step bc are in LDS; step bc - 1's reads are done
-    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc & 63));
-    const bool more = bc + 1 < a.nbc;
+    const int b = uniform(__builtin_amdgcn_readlane(bvec, bc - wb));   // before the next window
+    const bool more = bc + 1 < bc1;
     if (more) {
       load_x(bc + 1, buf ^ 1);
-      if (((bc + 1) & 63) == 0) load_meta(bc + 1);
+      if (bc + 1 - wb == 64) {
+        wb += 64;
+        load_meta(wb);
+      }
     }
     auto refill = [&]() {
       if (more) {
@@ -433,49 +497,20 @@ __device__ __forceinline__ void prefill64_tile(const PrefillArgs& a, int m0, int
     };
     kstep64<MT>(b, &stage[wave][0], &xs[buf][0], lane, acc, refill);
   }
-  if (!has_rows) return;
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + 16 * mt + 4 * g + v;
-      if (m >= a.M) continue;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a.y[size_t(m) * a.N + br * 64 + 16 * rt + r16] = (_Float16)acc[mt][rt][v];
-    }
+  tile_epilogue<MT>(a, acc, m0, br, has_rows, seg);
 }
 
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill64_kernel(
     PrefillArgs a) {
   __shared__ u32x4 xs[2][kMT * 2 * 64];        // activations, double buffered: 16 KiB per 64-column step
   __shared__ u32x4 stage[kWaves][kStage64];     // per wave: codes (4 KiB) + scale/zero (1 KiB)
-  const int bid = blockIdx.x;
-  const int ntiles = a.tiles_m * a.tiles_n;
-  const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, bid & 7);
-  const int j = bid >> 3, whole = w.count - w.split;
-  int t, half = -1;
-  if (j < whole) {
-    t = w.first + j;
+  WorkItem it;
+  if (!work_item(a, int(blockIdx.x), kBM, it)) return;
+  const int m0 = uniform(it.m0), tn = uniform(it.tn), seg = uniform(it.seg);
+  if (it.half < 0 && a.M - m0 > kBM / 2) {
+    prefill64_tile<kMT>(a, m0, tn, xs, stage, seg);
   } else {
-    const int v = j - whole;
-    if (v >= 2 * w.split) return;
-    t = w.first + whole + (v >> 1);
-    half = v & 1;
-  }
-  const int gsize = kGroupM * a.tiles_n;
-  const int first_m = (t / gsize) * kGroupM;
-  const int gm = min(kGroupM, a.tiles_m - first_m);
-  const int tm = first_m + (t % gsize) % gm;
-  const int tn = (t % gsize) / gm;
-  if (half < 0 && a.M > kBM / 2) {
-    prefill64_tile<kMT>(a, tm * kBM, tn, xs, stage);
-  } else if (half < 0) {
-    prefill64_tile<kMT / 2>(a, tm * kBM, tn, xs, stage);
-  } else {
-    const int m0 = tm * kBM + half * (kBM / 2);
-    if (m0 >= a.M) return;
-    prefill64_tile<kMT / 2>(a, m0, tn, xs, stage);
+    prefill64_tile<kMT / 2>(a, m0, tn, xs, stage, seg);
   }
 }
 
@@ -495,7 +530,28 @@ int prefill_tiles(int N, int M) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) 
 
 int device_compute_units() { return compute_units(); }
 
-int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* stream) {
+// K split: when the tile grid would fill at most half of the CUs, each tile
+// is cut into up to 16 K segments of at least 1024 columns, as many as fill
+// the CUs once, and as many as the caller's workspace holds (kseg fp32
+// partials of y).
+PrefillPlan prefill_plan(int N, int K, int M, int bc, size_t ws_bytes) {
+  PrefillPlan p;
+  const int nbc = K / bc, nbr = N / 64;
+  const int tiles = ((M + kBM - 1) / kBM) * ((nbr * 64 + kBN - 1) / kBN);
+  const int cus = compute_units();
+  int k = 1;
+  if (2 * tiles <= cus) k = min(min(cus / tiles, 16), max(1, nbc / (1024 / bc)));
+  auto need = [&](int kk) { return kk > 1 ? size_t(kk) * size_t(M) * size_t(N) * 4 : size_t(0); };
+  while (k > 1 && need(k) > ws_bytes) --k;
+  p.seg_cols = (nbc + k - 1) / k;
+  p.kseg = (nbc + p.seg_cols - 1) / p.seg_cols;
+  p.ws_bytes = need(p.kseg);
+  p.tiles = tiles;
+  return p;
+}
+
+int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* workspace,
+                   const PrefillPlan& plan, void* stream) {
   PrefillArgs a;
   a.bits = im.bits;
   a.offs = im.offs;
@@ -508,21 +564,30 @@ int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int
   a.M = M;
   a.nbr = im.nbr;
   a.nbc = im.nbc;
+  a.kseg = plan.kseg;
+  a.seg_cols = plan.kseg > 1 ? plan.seg_cols : im.nbc;
+  a.part = plan.kseg > 1 ? static_cast<float*>(workspace) : nullptr;
   a.tiles_m = (M + kBM - 1) / kBM;
   a.tiles_n = (im.nbr * 64 + kBN - 1) / kBN;
-  const int ntiles = a.tiles_m * a.tiles_n;
+  const int ntiles = a.tiles_m * a.tiles_n * a.kseg;
   a.per_xcd = (ntiles + 7) / 8;
   a.cus_xcd = max(1, compute_units() / 8);
   int items = 0;
   for (int x = 0; x < 8; ++x) {
     const XcdWork w = xcd_work(ntiles, a.per_xcd, a.cus_xcd, x);
-    items = max(items, w.count + w.split);
+    items = max(items, w.count + (a.kseg == 1 ? w.split : 0));
   }
   const dim3 grid(unsigned(8 * items)), block(kWaves * 64);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (im.bc == 64)
-    hipLaunchKernelGGL(prefill64_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL(prefill64_kernel, grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_kernel, grid, block, 0, static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL(prefill_kernel, grid, block, 0, s, a);
+  if (plan.kseg > 1) {
+    const size_t quads = size_t(M) * size_t(im.N) / 4;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0, s, a.part, a.y, quads,
+                       plan.kseg);
+  }
   return int(hipGetLastError());
 }
 

@@ -142,6 +142,17 @@ gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
  * its first use; every call leaves it zero-filled again.  Calls that run at
  * the same time need separate workspaces. */
 size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
+/* The same for gbb_gemm_mixed_w_path with a given path (0 equals
+ * gbb_gemm_mixed_w_workspace).  For the prefill kernel (path 2, or path 0
+ * when it takes the batch) the workspace holds the K split: when the tile
+ * grid of 128 tokens x 512 rows fills at most half of the compute units,
+ * each tile's K range is cut into up to 16 segments of at least 1024
+ * columns, whose fp32 partials live in the workspace (segments * M * N * 4
+ * bytes) until a second launch of the same call adds them in segment order
+ * and clears them.  A prefill call whose
+ * workspace is smaller (or NULL) takes as many segments as fit, down to
+ * none; it never fails for lack of workspace. */
+size_t gbb_gemm_mixed_w_path_workspace(int N, int K, int M, int path);
 
 /* y = x . dequant(W)^T over a packed block image (ScaleBITS explainer page,
  * section 3.2: the weight is dequantized inside the matrix product, one
@@ -274,6 +285,7 @@ size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M);
 gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x,
                                   uint16_t* y, int M, void* workspace, size_t ws_bytes,
                                   void* stream);
+size_t gbb_gemm_mixed_w_64x64_path_workspace(int N, int K, int M, int path);
 gbb_status gbb_gemm_mixed_w_64x64_path(const void* image, int N, int K, const uint16_t* x,
                                        uint16_t* y, int M, void* workspace, size_t ws_bytes,
                                        int path, void* stream);

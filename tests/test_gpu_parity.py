@@ -161,6 +161,38 @@ def test_prefill_parity(N, K, M):
     assert rel_err(y, bq.reference_gemm(x, W, bits)) <= TOL
 
 
+# the last case has 16 segments of 65 block columns: each crosses a
+# 64-column window of bitwidths and offsets
+@pytest.mark.parametrize("N,K,M,bc", [(1024, 8192, 300, 128), (512, 128 * 70, 1100, 128), (1024, 8192, 200, 64),
+                                      (64, 128 * 1040, 40, 128)])
+def test_prefill_split_k(N, K, M, bc):
+    """The prefill kernel with its K split (a tile grid that fills at most half
+    of the CUs, the workspace the path-aware query asks for): three calls
+    on one workspace are bit-identical (the partials are added in segment
+    order, whatever finishes last), within 2e-3 of the oracle, and leave
+    the workspace zero."""
+    lib = gbb.lib()
+    need = (lib.gbb_gemm_mixed_w_path_workspace if bc == 128 else lib.gbb_gemm_mixed_w_64x64_path_workspace)(N, K, M, 2)
+    assert need > 0   # the split is taken
+    W = small(N, K, N + K + bc)
+    x = rand_x(M, K, M + bc)
+    if bc == 128:
+        bits = synth.random_bitmap(N, K, ALLOWED, M)
+        img, call = packed(W, bits), gbb.gemm_mixed_w_path
+    else:
+        bits = synth.random_bitmap64(N, K, ALLOWED, M)
+        img, call = packed64(W, bits), gbb.gemm_mixed_w_64x64_path
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    first = None
+    for _ in range(3):
+        y = call(img, N, K, to_dev(x), 2, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.any(ws)
+        first = y.clone() if first is None else first
+        assert torch.equal(y.view(torch.int16), first.view(torch.int16))
+    assert rel_err(first, bq.reference_gemm(x, W, bits, block_cols=bc)) <= TOL
+
+
 def test_workspace_reuse_across_shapes():
     """One zero-filled workspace serves split-K calls of different shapes: a
     call with few row groups followed by one with more than 64 of them."""
@@ -949,7 +981,9 @@ def test_64x64_llama3_8b_prefill(i):
     img = packed64(W, bits)
     rows = one_row_per_block_row(p.N, 7 + i)
     x = synth.prefill_x(2048, p.K, i)
-    assert gbb.gemm_mixed_w_64x64_workspace(p.N, p.K, 2048) == 0   # not decode chunks
+    lib = gbb.lib()   # the library's route is the prefill kernel, not decode chunks
+    assert lib.gbb_gemm_mixed_w_64x64_path_workspace(p.N, p.K, 2048, 0) == \
+        lib.gbb_gemm_mixed_w_64x64_path_workspace(p.N, p.K, 2048, 2)
     y = gbb.gemm_mixed_w_64x64(img, p.N, p.K, to_dev(x)).cpu().numpy()
     ref = bq.reference_rows(x, W, bits, rows, block_cols=64)
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL

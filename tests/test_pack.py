@@ -303,36 +303,65 @@ def test_graph_wrapper_rejects_mismatched_shapes():
         gbb.Graph([])
 
 
+def _prefill_split(N, K, M, bc, cus):
+    """The documented K split of the prefill kernel: when the 128 x 512 tile
+    grid fills at most half the CUs, up to 16 segments of at least 1024
+    columns, as many as fill the CUs once.  Returns (tiles, segments,
+    workspace bytes: the segments' fp32 partials)."""
+    nbc = K // bc
+    tiles = -(-M // 128) * -(-N // 512)
+    k = min(cus // tiles, 16, max(1, nbc // (1024 // bc))) if 2 * tiles <= cus else 1
+    seg = -(-nbc // k)
+    kseg = -(-nbc // seg)
+    return tiles, kseg, (kseg * M * N * 4 if kseg > 1 else 0)
+
+
 @pytest.mark.parametrize("N,K", [(8192, 28672), (28672, 8192), (4096, 4096), (64, 128)])
 def test_workspace_follows_the_batch_route(N, K):
-    """Host side of the dispatch: above 32 tokens a workspace is asked for
-    exactly when the batch runs as 32-token decode chunks, that is when
-    ceil(M/32) prefill grids of 128x512 tiles fit in one wave of the CUs
-    (256 when the library finds no device), and it is then the larger of the
-    full and the ragged last chunk's needs."""
+    """Host side of the dispatch: above 32 tokens the batch runs as 32-token
+    decode chunks only when the prefill grid, K split included, fills at
+    most half of the CUs (256 when the library finds no device); the
+    workspace is then the larger of the full and the ragged last chunk's
+    needs, and otherwise the prefill kernel's K split.  The path-aware
+    query gives the same for path 0 and the split for a forced prefill."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    lib = gbb.lib()
     for M in (33, 64, 65, 96, 128, 200, 256, 512, 1024, 2048):
-        tiles = -(-M // 128) * -(-N // 512)
-        chunked = -(-M // 32) * tiles <= cus
+        tiles, kseg, split_ws = _prefill_split(N, K, M, 128, cus)
+        chunked = 2 * tiles * kseg <= cus
         need = gbb.gemm_mixed_w_workspace(N, K, M)
+        assert lib.gbb_gemm_mixed_w_path_workspace(N, K, M, 0) == need
+        assert lib.gbb_gemm_mixed_w_path_workspace(N, K, M, 2) == split_ws
+        assert lib.gbb_gemm_mixed_w_path_workspace(N, K, M, 1) == 0   # the decode kernel takes M <= 32
         if not chunked:
-            assert need == 0, (M, need)
+            assert need == split_ws, (M, need)
             continue
         want = gbb.gemm_mixed_w_workspace(N, K, 32)
         if M % 32:
             want = max(want, gbb.gemm_mixed_w_workspace(N, K, M % 32))
         assert need == want, (M, need, want)
+    if K % 64 == 0:
+        for M in (512, 2048):
+            assert lib.gbb_gemm_mixed_w_64x64_path_workspace(N, K, M, 2) == _prefill_split(N, K, M, 64, cus)[2]
 
 
 def test_64x64_workspace_sizes():
-    """The 64x64 decode plan on the host (no device work): every shape with
-    whole 64-column blocks, down to a single block, gets a workspace of 0 or
-    12 bytes per output of the largest 32-token chunk."""
+    """The 64x64 plans on the host (no device work): every shape with whole
+    64-column blocks, down to a single block, gets a workspace of 0 or 12
+    bytes per output of the decode launch (of the largest 32-token chunk),
+    or above 32 tokens the prefill kernel's K split when that is the
+    route."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
     for N in (64, 128, 448, 8192):
         for K in (64, 128, 192, 1216, 4096, 28672):
             for M in (1, 2, 8, 16, 17, 32, 33, 70):
                 ws = gbb.gemm_mixed_w_64x64_workspace(N, K, M)
+                tiles, kseg, split_ws = _prefill_split(N, K, M, 64, cus)
+                if M > 32 and 2 * tiles * kseg > cus:
+                    assert ws == split_ws, (N, K, M, ws)
+                    continue
                 assert ws in (0, min(M, 32) * N * 12) or (M > 32 and ws % (N * 12) == 0 and ws <= 32 * N * 12), \
                     (N, K, M, ws)
     assert gbb.gemm_mixed_w_64x64_workspace(64, 96, 1) == 0      # not whole blocks
