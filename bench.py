@@ -16,7 +16,7 @@ Also reported: p10/p50/p90 of single step replays, each launch group alone
 shapes with uniform 3- and 4-bit bitmaps (the cost of mixing bitwidths), one
 4096 x 4096 matrix at M = 1, the M = 2048 prefill GEMM (TFLOP/s against the
 2.5 PFLOP/s fp16 dense peak) with an fp16 library GEMM on the dequantized
-weights for context, the W4.4A8 layer (M = 32 ... 4096) and the oracle timed
+weights for context, the same matrices at M = 64 ... 1024 (K split), the W4.4A8 layer (M = 32 ... 4096) and the oracle timed
 on the host cores over one copy of the headline layer (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--extras a,b,...]
@@ -559,16 +559,25 @@ def main():
             # matrix-core-bound launches reach steady clocks only after some
             # tens of milliseconds of such work: warm up for ~30 launches
             sp = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, x, out=y), 30, 30)
-            # moderate batches: the library's own choice between the prefill
-            # kernel and 32-token decode chunks, against the prefill kernel forced
+            # moderate batches: the library's own choice (the K-split prefill
+            # kernel, or 32-token decode chunks where even the split grid
+            # would leave most compute units idle), against the prefill
+            # kernel with no K split (a workspace too small for one)
             mid = {}
-            for Mm in (64, 256):
+            no_split_ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+            for Mm in (64, 128, 256, 512, 1024):
                 xm = x[:Mm].contiguous()
                 ym = y[:Mm]
                 sa = time_eager(torch, lambda: gbb.gemm_mixed_w(rot.next(), p.N, p.K, xm, out=ym), 30, 12)
-                sf = time_eager(torch, lambda: gbb.gemm_mixed_w_path(rot.next(), p.N, p.K, xm, 2, out=ym), 30, 12)
-                mid[f"M{Mm}"] = {"us": round(sa * 1e6, 1), "prefill_kernel_us": round(sf * 1e6, 1)}
-                log(f"prefill {p.name} M={Mm}: {sa * 1e6:.1f} us (prefill kernel alone {sf * 1e6:.1f} us)")
+                sf = time_eager(torch, lambda: gbb.gemm_mixed_w_path(rot.next(), p.N, p.K, xm, 2, out=ym,
+                                                                     workspace=no_split_ws), 30, 12)
+                flm = 2.0 * Mm * p.N * p.K
+                mid[f"M{Mm}"] = {"us": round(sa * 1e6, 1), "TFLOPs": round(flm / sa / 1e12, 1),
+                                 "prefill_kernel_no_k_split_us": round(sf * 1e6, 1),
+                                 "workspace_MB": round(gbb.gemm_mixed_w_workspace(p.N, p.K, Mm) / 1e6, 1)}
+                log(f"prefill {p.name} M={Mm}: {sa * 1e6:.1f} us, {flm / sa / 1e12:.0f} TFLOP/s "
+                    f"(no K split {sf * 1e6:.1f} us)")
+            del no_split_ws
             del rot
             w32, w16 = gbb.dequant(imgd, p.N, p.K)
             del w32

@@ -118,6 +118,14 @@ extern "C" size_t gbb_gemm_mixed_w_workspace(int N, int K, int M) {
   return p.ws_bytes;
 }
 
+// The least workspace gbb_gemm_mixed_w runs (N, K, M) with: the decode
+// launches' accumulators, for the whole batch or its 32-token chunks.  The
+// prefill kernel splits K only as far as the workspace it is given holds.
+size_t gbb::required_workspace(int N, int K, int M) {
+  if (M > 32 && !decode_in_chunks(N, K, M, kGroup)) return 0;
+  return gbb_gemm_mixed_w_workspace(N, K, M);
+}
+
 extern "C" size_t gbb_gemm_mixed_w_path_workspace(int N, int K, int M, int path) {
   if (N <= 0 || K <= 0 || M <= 0 || N % kBlockRows || K % kGroup) return 0;
   if (path == 0) return gbb_gemm_mixed_w_workspace(N, K, M);

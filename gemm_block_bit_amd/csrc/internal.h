@@ -59,6 +59,9 @@ struct PrefillPlan {
 // The prefill launch for (N, K, M) on blocks of bc columns with a workspace
 // of ws_bytes (a K split only when its counts and partials fit).
 PrefillPlan prefill_plan(int N, int K, int M, int bc, size_t ws_bytes);
+// The least workspace a 64x128 block call of (N, K, M) runs with (the decode
+// accumulators; 0 on the prefill route, whose K split fits what it is given).
+size_t required_workspace(int N, int K, int M);
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* workspace,
                    const PrefillPlan& plan, void* stream);
 // 64x64-block images, M <= 32: the plan (seg_cols and nbc in 64-column

@@ -82,7 +82,8 @@ extern "C" gbb_status gbb_gemm_mixed_w_noalloc(const void* image, int N, int K, 
                                                int M, void* stream) {
   gbb_status st = gbb::check_gemm_args(image, N, K, x, y, M, 0);
   if (st != GBB_OK || M == 0) return st;
-  const size_t need = gbb_gemm_mixed_w_workspace(N, K, M);
+  // the prefill route's K split takes as many segments as the array holds
+  const size_t need = gbb::required_workspace(N, K, M);
   if (need > kScratchBytes)
     return gbb::fail(GBB_E_SPACE, "N=%d K=%d M=%d needs %zu bytes of split-K workspace, above the %zu bytes of "
                      "the allocation-free entry point (use gbb_gemm_mixed_w with a workspace)",

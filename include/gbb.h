@@ -135,12 +135,15 @@ gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 
 /* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M) (the fused product of
  * the ScaleBITS explainer page, section 3.2, when its K range is split over
- * workgroups); may be 0 (it is
- * M * N * 12 when K is split across workgroups: per output element an int64
- * fixed-point and an fp32 accumulator; for batches run as 32-token chunks,
- * that of the largest chunk).  The workspace must be zero-filled once before
- * its first use; every call leaves it zero-filled again.  Calls that run at
- * the same time need separate workspaces. */
+ * workgroups); may be 0.  On the decode route it is M * N * 12 when K is
+ * split across workgroups (per output element an int64 fixed-point and an
+ * fp32 accumulator; for batches run as 32-token chunks, that of the largest
+ * chunk), and a smaller workspace is an error.  On the prefill route it is
+ * the fp32 partials of the K split described under
+ * gbb_gemm_mixed_w_path_workspace, and a smaller workspace only shortens the
+ * split.  The workspace must be zero-filled once before its first use; every
+ * call leaves it zero-filled again.  Calls that run at the same time need
+ * separate workspaces. */
 size_t gbb_gemm_mixed_w_workspace(int N, int K, int M);
 /* The same for gbb_gemm_mixed_w_path with a given path (0 equals
  * gbb_gemm_mixed_w_workspace).  For the prefill kernel (path 2, or path 0
@@ -162,12 +165,17 @@ size_t gbb_gemm_mixed_w_path_workspace(int N, int K, int M, int path);
  *          round-to-nearest-even at the end).
  *   M >= 1.  M <= 32 runs the decode kernels (weights streamed once, matrix
  *   cores for the dot products).  Larger M runs the tiled prefill kernel,
- *   unless its grid of 128-token x 512-row tiles, ceil(M / 32) times over,
- *   still fits in one wave of the device's compute units: then the decode
- *   kernels run the batch in 32-token chunks, one launch each, which keeps
- *   every CU busy where the prefill kernel would leave most of them idle.
+ *   with its K range split into segments when its grid of 128-token x
+ *   512-row tiles is small (see gbb_gemm_mixed_w_path_workspace), unless
+ *   twice the split grid still fits in the device's compute units: then the
+ *   decode kernels run the batch in 32-token chunks, one launch each, which
+ *   keeps every CU busy where the prefill kernel would leave most of them
+ *   idle.
  *   workspace/ws_bytes  device memory of gbb_gemm_mixed_w_workspace(N, K, M)
- *          bytes (NULL allowed when that is 0).
+ *          bytes (NULL allowed when that is 0).  On the prefill route the
+ *          number of K segments follows ws_bytes, and with it the order of
+ *          the fp32 sums: for one ws_bytes the result is the same on every
+ *          call, across sizes it may differ in the last bits.
  * Errors: GBB_E_ARG (NULL image/x/y, N or K <= 0, M < 0, x and y overlap,
  * missing workspace), GBB_E_SHAPE (N % 64, K % 128, N or K above 2^20, or
  * M * K >= 2^31 on the prefill kernel), GBB_E_ALIGN, GBB_E_SPACE (workspace
@@ -188,9 +196,12 @@ gbb_status gbb_gemm_mixed_w(const void* image, int N, int K, const uint16_t* x,
  * GPU's array, so calls that may overlap on one GPU (several streams or
  * threads, graphs replayed concurrently) race and give wrong results.  The
  * call allocates and frees nothing.
- * Errors: those of gbb_gemm_mixed_w; GBB_E_SPACE when the shape needs more
- * than GBB_NOALLOC_SCRATCH_BYTES of workspace (gbb_gemm_mixed_w_workspace;
- * no shape the block entry points accept needs more than 12 MiB);
+ * The prefill route's K split takes as many segments as the array holds, so
+ * the result equals gbb_gemm_mixed_w's with ws_bytes =
+ * GBB_NOALLOC_SCRATCH_BYTES.
+ * Errors: those of gbb_gemm_mixed_w; GBB_E_SPACE when the decode route
+ * needs more than GBB_NOALLOC_SCRATCH_BYTES of workspace (no shape the block
+ * entry points accept needs more than 12 MiB);
  * GBB_E_DEVICE when the array's address cannot be obtained. */
 #define GBB_NOALLOC_SCRATCH_BYTES (16u << 20)
 gbb_status gbb_gemm_mixed_w_noalloc(const void* image, int N, int K, const uint16_t* x,
@@ -277,9 +288,10 @@ gbb_status gbb_pack_blocks_64x64(const uint16_t* W, int N, int K, const uint8_t*
 /* y = x . dequant(W)^T over a version-2 image, with the arguments, layout,
  * workspace rules and errors of gbb_gemm_mixed_w / gbb_gemm_mixed_w_path
  * (K % 64 == 0).  M <= 32 runs the 64x64 decode kernels; larger M runs the
- * 64x64 prefill kernel (M * K < 2^31), or the decode kernels in 32-token
- * chunks where the prefill grid would leave most compute units idle (the
- * same rule as for 64x128 blocks).  path: 0 that choice, 1 the decode
+ * 64x64 prefill kernel (M * K < 2^31; K split into segments of at least
+ * 1024 columns as for 64x128 blocks), or the decode kernels in 32-token
+ * chunks where the split prefill grid would leave most compute units idle
+ * (the same rule as for 64x128 blocks).  path: 0 that choice, 1 the decode
  * kernel (M <= 32), 2 the prefill kernel. */
 size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M);
 gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x,

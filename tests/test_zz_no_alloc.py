@@ -39,8 +39,9 @@ def run_noalloc(img, N, K, xd, M):
 
 
 def run_with_workspace(img, N, K, xd, M):
-    need = gbb.gemm_mixed_w_workspace(N, K, M)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=xd.device)
+    # the size of the allocation-free array: a prefill K split then takes the
+    # same number of segments on both entry points
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device=xd.device)
     y = torch.empty((M, N), dtype=torch.float16, device=xd.device)
     st = gbb.lib().gbb_gemm_mixed_w(img.data_ptr(), N, K, xd.data_ptr(), y.data_ptr(), M, ws.data_ptr(),
                                     ws.numel(), torch.cuda.current_stream(xd.device).cuda_stream)
@@ -49,19 +50,21 @@ def run_with_workspace(img, N, K, xd, M):
 
 
 # pairs of calls in a row, the second on a smaller input: split-K decode at
-# M = 1 and 8, the two-row kernel at M = 32, 32-token decode chunks (M = 64)
-# and the prefill kernel (no workspace)
+# M = 1 and 8, the two-row kernel at M = 32, 32-token decode chunks (M = 64),
+# the prefill kernel with no K split (2048 x 1024, M = 600) and with a K split
+# whose full size (67 MB) the array does not hold (2048 x 16384, M = 512:
+# 4 segments instead of 16), followed by decode chunks
 PAIRS = [((2048, 8192, 8), (1024, 4096, 1)),
          ((1024, 4096, 32), (256, 1024, 3)),
          ((4096, 4096, 64), (1024, 2048, 33)),
-         ((2048, 1024, 600), (1024, 4096, 16))]
+         ((2048, 1024, 600), (1024, 4096, 16)),
+         ((2048, 16384, 512), (512, 8192, 300))]
 
 
 @pytest.mark.parametrize("first,second", PAIRS)
 def test_noalloc_matches_workspace_entry_point(first, second):
     for i, (N, K, M) in enumerate((first, second)):
         W, bits, img, xd, x = case(N, K, M, N + K + M + i)
-        assert gbb.gemm_mixed_w_workspace(N, K, M) <= (16 << 20)
         a = run_noalloc(img, N, K, xd, M)
         b = run_with_workspace(img, N, K, xd, M)
         again = run_noalloc(img, N, K, xd, M)
