@@ -16,8 +16,10 @@ Also reported: p10/p50/p90 of single step replays, each launch group alone
 shapes with uniform 3- and 4-bit bitmaps (the cost of mixing bitwidths), one
 4096 x 4096 matrix at M = 1, the M = 2048 prefill GEMM (TFLOP/s against the
 2.5 PFLOP/s fp16 dense peak) with an fp16 library GEMM on the dequantized
-weights for context, the same matrices at M = 64 ... 1024 (K split), the W4.4A8 layer (M = 32 ... 4096) and the oracle timed
-on the host cores over one copy of the headline layer (cpu_baseline).
+weights for context, the same matrices at M = 64 ... 1024 (K split), the
+W4.4A8 layer (M = 32 ... 4096) and its down-projection shape 8192 x 28672
+at M = 1 ... 96 (K split), and the oracle timed on the host cores over one
+copy of the headline layer (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--extras a,b,...]
 """
@@ -626,6 +628,32 @@ def main():
             if want_cpu:
                 oracle_inputs.setdefault("w44a8", {"img": img})[M] = sw
         extra["w44a8_28672x8192"] = w48
+        del imgd, rot
+        torch.cuda.empty_cache()
+
+        # ---------------- W4.4A8 8192 x 28672 (down projection), small batches ----------------
+        # 129 row blocks for 256 CUs: the stream kernel splits K (6 segments
+        # for the 8-bit row blocks, 3 for the 4-bit ones), against the same
+        # kernel unsplit
+        W, rows8 = synth.w44a8_8192x28672()
+        img, _, _ = gbb.pack_w48(W, rows8)
+        del W
+        imgd = torch.from_numpy(img).to(dev)
+        rot = Rotation([imgd] + [imgd.clone() for _ in range(3)])
+        down = {}
+        for M in (1, 16, 32, 64, 96):
+            x = torch.from_numpy(synth.activations(M, 28672, synth.WL_W44A8, 2)).to(dev)
+            xq, xs = gbb.quant_act_i8(x)
+            y = torch.empty((M, 8192), dtype=torch.float16, device=dev)
+            ss = time_eager(torch, lambda: gbb.gemm_w48a8(rot.next(), 8192, 28672, rows8.size, xq, xs, out=y), 30, 30)
+            su = time_eager(torch, lambda: gbb.gemm_w48a8(rot.next(), 8192, 28672, rows8.size, xq, xs, out=y,
+                                                          split=False), 30, 30)
+            down[f"M{M}"] = {"us": round(ss * 1e6, 1), "weight_GBps": round(img.size / ss / 1e9, 1),
+                             "frac_hbm": round(img.size / ss / 1e9 / HBM_PEAK_GBS, 3),
+                             "no_k_split_us": round(su * 1e6, 1),
+                             "workspace_MB": round(gbb.gemm_w48a8_workspace(8192, 28672, rows8.size, M) / 1e6, 2)}
+            log(f"w44a8 8192x28672 M={M}: {down[f'M{M}']}")
+        extra["w44a8_8192x28672"] = down
         del imgd, rot
         torch.cuda.empty_cache()
 

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     gemm_mixed_w_path,
     gemm_mixed_w_workspace,
     gemm_w48a8,
+    gemm_w48a8_workspace,
     lib,
     pack_blocks,
     pack_w48,

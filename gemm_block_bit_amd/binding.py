@@ -63,6 +63,8 @@ _SIGS = {
     "gbb_pack_w48": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _sz]),
     "gbb_quant_act_i8": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "gbb_gemm_w48a8": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp]),
+    "gbb_gemm_w48a8_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "gbb_gemm_w48a8_split": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "gbb_w48_group_acc": (_i, [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]),
 }
 EXPORTS = tuple(_SIGS)
@@ -435,14 +437,27 @@ def quant_act_i8(x, ga: int | None = None):
     return xq, xs
 
 
-def gemm_w48a8(image, N: int, K: int, n8: int, xq, xs, ga: int | None = None, out=None):
+def gemm_w48a8_workspace(N: int, K: int, n8: int, M: int, ga: int | None = None) -> int:
+    return lib().gbb_gemm_w48a8_workspace(N, K, n8, M, K if ga is None else ga)
+
+
+def gemm_w48a8(image, N: int, K: int, n8: int, xq, xs, ga: int | None = None, out=None, workspace=None,
+               split: bool = True):
+    """y = dequant(xq) . dequant(W)^T (fp16 [M][N]) on torch's current
+    stream.  split: gbb_gemm_w48a8_split over `workspace` (default: the
+    binding's per-stream buffer), else gbb_gemm_w48a8."""
     torch = _torch()
     M = xq.shape[0]
     ga = K if ga is None else ga
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=xq.device)
-    _check(lib().gbb_gemm_w48a8(_dev_ptr(image, torch.uint8, "image"), N, K, n8,
-                                _dev_ptr(xq, torch.int8, "xq"), _dev_ptr(xs, torch.float16, "xs"), ga,
-                                _dev_ptr(y, torch.float16, "y"), M, _stream(xq)))
+    args = (_dev_ptr(image, torch.uint8, "image"), N, K, n8, _dev_ptr(xq, torch.int8, "xq"),
+            _dev_ptr(xs, torch.float16, "xs"), ga, _dev_ptr(y, torch.float16, "y"), M)
+    if not split:
+        _check(lib().gbb_gemm_w48a8(*args, _stream(xq)))
+        return y
+    ws = workspace if workspace is not None else _workspace(xq.device, gemm_w48a8_workspace(N, K, n8, M, ga))
+    _check(lib().gbb_gemm_w48a8_split(*args, ws.data_ptr() if ws is not None else None,
+                                      ws.numel() if ws is not None else 0, _stream(xq)))
     return y
 
 

@@ -224,7 +224,30 @@ extern "C" gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, co
   if (!xq || !xs || !y) return fail(GBB_E_ARG, "xq, xs and y must not be NULL");
   if (ga != K && ga != 128) return fail(GBB_E_ARG, "ga must be K or 128 (ga=%d)", ga);
   if (!aligned16(xq)) return fail(GBB_E_ALIGN, "xq must be 16-byte aligned");
-  return device_status(launch_w48(w48_view(image, N, K, n8), xq, xs, ga, y, M, stream), "w48 launch");
+  return device_status(launch_w48(w48_view(image, N, K, n8), xq, xs, ga, y, M, nullptr, 0, stream), "w48 launch");
+}
+
+extern "C" size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga) {
+  if (N <= 0 || K <= 0 || K % kGroup || n8 < 0 || n8 > N || M <= 0 || (ga != K && ga != 128)) return 0;
+  const W48Layout l = w48_layout(N, K, n8);
+  if (!w48_streams(l.T8, l.T4, M, ga)) return 0;
+  return w48_split(N, K, l.T8, l.T4, M < 64 ? M : 64, SIZE_MAX).ws_bytes;
+}
+
+extern "C" gbb_status gbb_gemm_w48a8_split(const void* image, int N, int K, int n8, const int8_t* xq,
+                                           const uint16_t* xs, int ga, uint16_t* y, int M, void* workspace,
+                                           size_t ws_bytes, void* stream) {
+  gbb_status st = check_w48_args(image, N, K, n8);
+  if (st != GBB_OK) return st;
+  if (M < 0) return fail(GBB_E_ARG, "M must not be negative (M=%d)", M);
+  if (M == 0) return GBB_OK;
+  if (!xq || !xs || !y) return fail(GBB_E_ARG, "xq, xs and y must not be NULL");
+  if (ga != K && ga != 128) return fail(GBB_E_ARG, "ga must be K or 128 (ga=%d)", ga);
+  if (!aligned16(xq)) return fail(GBB_E_ALIGN, "xq must be 16-byte aligned");
+  if (workspace && !aligned16(workspace)) return fail(GBB_E_ALIGN, "workspace is not 16-byte aligned");
+  return device_status(launch_w48(w48_view(image, N, K, n8), xq, xs, ga, y, M, workspace, workspace ? ws_bytes : 0,
+                                  stream),
+                       "w48 launch");
 }
 
 extern "C" gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq, int ga,

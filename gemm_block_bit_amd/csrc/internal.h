@@ -84,8 +84,19 @@ struct W48ImageView {
   int N, K, n8, n4, T8, T4;
 };
 int launch_quant_act(const uint16_t* x, int M, int K, int ga, int8_t* xq, uint16_t* xs, void* stream);
+// The stream kernel's K split: kseg8 (kseg4) segments of seg8 (seg4)
+// 128-column groups for the 8-bit (4-bit) row blocks, whose fp32 partials
+// take ws_bytes (0 without a split).
+struct W48Split {
+  int kseg8, seg8, kseg4, seg4;
+  size_t ws_bytes;
+};
+W48Split w48_split(int N, int K, int T8, int T4, int M, size_t ws_bytes);
+bool w48_streams(int T8, int T4, int M, int ga);
+// workspace (16-byte aligned, zero at rest) of ws_bytes bounds the stream
+// kernel's K split; NULL runs it unsplit.
 int launch_w48(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
-               int M, void* stream);
+               int M, void* workspace, size_t ws_bytes, void* stream);
 int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int ga, int32_t* acc, int M, void* stream);
 
 // Returns a message for a HIP error code, or nullptr for success.

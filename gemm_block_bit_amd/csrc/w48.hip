@@ -115,7 +115,13 @@ struct W48Args {
   const _Float16* xs;
   _Float16* y;
   int32_t* acc_out;  // debug: int32 [M][N][G] group products, else null
+  // The stream kernel's K split: kseg8 (kseg4) segments of seg8 (seg4)
+  // 128-column groups, the last one shorter, for the 8-bit (4-bit) row
+  // blocks.  With a split, every row's partial sums go to part, fp32
+  // [segment][M][packed row] (zero between calls).
+  float* part;
   int N, K, M, T8, T4, ga;
+  int kseg8, seg8, kseg4, seg4;
 };
 
 constexpr int kNT = 2;  // 16-row weight tiles per wave
@@ -527,7 +533,8 @@ struct StreamCfg {
 // One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.  ACC:
 // store each group's exact int32 sums to a.acc_out instead of scaling them.
 template <int TM, bool Q4, bool ACC>
-__device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend) {
+__device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend, int seg,
+                                             int seg_groups) {
   using C = StreamCfg<TM>;
   constexpr int kStages = C::kStages;
   constexpr int kLoads = Q4 ? C::kLoads4 : C::kLoads8;
@@ -536,10 +543,13 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
   const int g = lane >> 4, r16 = lane & 15;
   const int t = min(t0 + wave, tend - 1);   // this wave's tile (clamped; results discarded)
   const int G = a.K / 128, KT = a.K / 64;
+  // this workgroup's K segment: groups g0 ... g0 + ng - 1
+  const int g0 = seg * seg_groups, ng = min(G - g0, seg_groups);
 
-  auto stage = [&](int grp) { return (grp % kStages) * C::kStage; };
-  auto issue = [&](int grp) {
-    const uint32_t st = lbase + stage(grp);
+  auto stage = [&](int j) { return (j % kStages) * C::kStage; };
+  auto issue = [&](int j) {
+    const int grp = g0 + j;
+    const uint32_t st = lbase + stage(j);
 #pragma unroll
     for (int q = 0; q < C::NA; ++q) {
       const int f = wave + 4 * q, i = min(f >> 1, TM - 1), h = f & 1;
@@ -577,12 +587,13 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     if (t0 + wave < tend) n_acc = a.rows[16 * (t0 + wave) + r16];
     wait_vm<0>();
   }
-  for (int p = 0; p < kStages - 1 && p < G; ++p) issue(p);
-  for (int grp = 0; grp < G; ++grp) {
-    // this wave's loads of group grp have landed once at most the loads of the
-    // (up to kStages - 2) later groups are in flight
+  for (int p = 0; p < kStages - 1 && p < ng; ++p) issue(p);
+  for (int j = 0; j < ng; ++j) {
+    const int grp = g0 + j;
+    // this wave's loads of step j have landed once at most the loads of the
+    // (up to kStages - 2) later steps are in flight
     static_assert(kStages - 2 <= 3, "wait cases");
-    const int later = min(G - 1 - grp, kStages - 2);
+    const int later = min(ng - 1 - j, kStages - 2);
     if (later >= 3)
       wait_vm<3 * kLoads>();
     else if (later == 2)
@@ -591,10 +602,10 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
       wait_vm<kLoads>();
     else
       wait_vm<0>();
-    __syncthreads();   // every wave's loads of grp landed; every wave is done with grp - 1
-    if (grp + kStages - 1 < G) issue(grp + kStages - 1);   // into grp - 1's stage
+    __syncthreads();   // every wave's loads of step j landed; every wave is done with j - 1
+    if (j + kStages - 1 < ng) issue(j + kStages - 1);   // into step j - 1's stage
     // every LDS read of the step first, then one wait
-    const uint8_t* st = base + stage(grp);
+    const uint8_t* st = base + stage(j);
     const uint8_t* B = st + C::kA + wave * 2048;
     i32x4 av[TM][2];
 #pragma unroll
@@ -651,6 +662,20 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
   if (t0 + wave >= tend) return;
   const int n = a.rows[16 * (t0 + wave) + r16];
   if (n < 0) return;
+  if (a.part) {
+    // this segment's partial sums, at the packed row; w48_reduce_kernel adds
+    // the segments, applies the activation scale and scatters
+    const int P = 16 * (a.T8 + a.T4), pr = 16 * (t0 + wave) + r16;
+    float* pp = a.part + size_t(seg) * size_t(a.M) * size_t(P);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * i + 4 * g + v;
+        if (m < a.M) pp[size_t(m) * P + pr] = tot[i][v];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -666,11 +691,47 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
   static_assert(2 * C::kStages * C::kStage <= 160 * 1024, "two workgroups per CU");
   __shared__ u32x4 lds[C::kStages * C::kStage / 16];
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
-  const int nb8 = (a.T8 + 3) / 4;
-  if (int(blockIdx.x) < nb8)
-    stream_tiles<TM, false, ACC>(a, base, int(blockIdx.x) * 4, a.T8);
-  else
-    stream_tiles<TM, true, ACC>(a, base, a.T8 + (int(blockIdx.x) - nb8) * 4, a.T8 + a.T4);
+  // workgroup = (K segment, row block): the 8-bit row blocks' kseg8
+  // segments first, then the 4-bit row blocks' kseg4
+  const int nb8 = (a.T8 + 3) / 4, nb4 = (a.T4 + 3) / 4, w8 = nb8 * a.kseg8, b = int(blockIdx.x);
+  if (b < w8) {
+    stream_tiles<TM, false, ACC>(a, base, (b % nb8) * 4, a.T8, b / nb8, a.seg8);
+  } else {
+    const int c = b - w8;
+    stream_tiles<TM, true, ACC>(a, base, a.T8 + (c % nb4) * 4, a.T8 + a.T4, c / nb4, a.seg4);
+  }
+}
+
+// For every token m and packed row p of original row n = rows[p] >= 0:
+// y[m][n] = fp16(s_a[m] * (the partial sums of [m][p] over the row's
+// segments -- kseg8 for the 8-bit rows (p < P8), kseg4 for the others --
+// added in segment order, so the result does not depend on the order the
+// segments ran in)).  The partials read are cleared, which leaves the
+// workspace zero.  One element per thread; the row index, the scale and all
+// of the partials are loaded before anything waits (a padding row's
+// partials are in bounds and zero), so the loads overlap.
+__global__ __launch_bounds__(256) void w48_reduce_kernel(float* part, const int32_t* rows, const _Float16* xs,
+                                                         _Float16* y, int M, int N, int P, int P8, int kseg8,
+                                                         int kseg4) {
+  const size_t plane = size_t(M) * size_t(P);
+  const size_t e = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= plane) return;
+  const int m = int(e / size_t(P)), p = int(e % size_t(P));
+  const int k = p < P8 ? kseg8 : kseg4;
+  const int n = rows[p];
+  const float sa = (float)xs[m];
+  float v[16];
+#pragma unroll
+  for (int sg = 0; sg < 16; ++sg) v[sg] = sg < k ? part[size_t(sg) * plane + e] : 0.0f;
+  if (n < 0) return;
+  float t = v[0];
+#pragma unroll
+  for (int sg = 1; sg < 16; ++sg)
+    if (sg < k) t += v[sg];
+#pragma unroll
+  for (int sg = 0; sg < 16; ++sg)
+    if (sg < k) part[size_t(sg) * plane + e] = 0.0f;
+  y[size_t(m) * size_t(N) + n] = (_Float16)(t * sa);
 }
 
 W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,
@@ -691,18 +752,27 @@ W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, 
   a.T8 = im.T8;
   a.T4 = im.T4;
   a.ga = ga;
+  a.part = nullptr;
+  a.kseg8 = a.kseg4 = 1;
+  a.seg8 = a.seg4 = im.K / 128;
   return a;
 }
 
 template <bool ACC>
 void launch_stream(const W48Args& a, hipStream_t s) {
-  const dim3 grid(unsigned((a.T8 + 3) / 4 + (a.T4 + 3) / 4));
+  const dim3 grid(unsigned((a.T8 + 3) / 4 * a.kseg8 + (a.T4 + 3) / 4 * a.kseg4));
   if (a.M <= 16)
     hipLaunchKernelGGL((w48_stream_kernel<1, ACC>), grid, dim3(256), 0, s, a);
   else if (a.M <= 32)
     hipLaunchKernelGGL((w48_stream_kernel<2, ACC>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((w48_stream_kernel<4, ACC>), grid, dim3(256), 0, s, a);
+  if (!ACC && a.part) {
+    const int P = 16 * (a.T8 + a.T4);
+    const size_t total = size_t(a.M) * size_t(P);
+    hipLaunchKernelGGL(w48_reduce_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a.part, a.rows,
+                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4);
+  }
 }
 
 template <bool ACC>
@@ -716,20 +786,73 @@ void launch_tile(const W48Args& a, hipStream_t s) {
     hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
 }
 
+}  // namespace
+
+// The stream kernel's K split for a pass of M <= 64 tokens.  An 8-bit row
+// block streams twice the bytes of a 4-bit one.  Counting it twice, when the
+// row blocks fill at most one workgroup per CU, each row block's groups are
+// cut into segments of at least 8 groups (1024 columns), at most 16, so that
+// the workgroups, two per CU, stream about equal bytes: an 8-bit row block
+// takes twice the segments of a 4-bit one.  With fewer than ws_bytes for the
+// fp32 partials (segments x M x packed rows), fewer segments.
+W48Split w48_split(int N, int K, int T8, int T4, int M, size_t ws_bytes) {
+  (void)N;
+  const int nb8 = (T8 + 3) / 4, nb4 = (T4 + 3) / 4, G = K / 128, cus = device_compute_units();
+  const int kcap = max(1, min(16, G / 8));
+  int k8 = 1, k4 = 1;
+  if (2 * nb8 + nb4 <= cus) {
+    if (nb4) {
+      k4 = max(1, min(kcap, 2 * cus / (2 * nb8 + nb4)));
+      k8 = nb8 ? min(kcap, 2 * k4) : 1;
+    } else {
+      k8 = max(1, min(kcap, 2 * cus / nb8));
+    }
+  }
+  const size_t P = size_t(16) * size_t(T8 + T4);
+  auto need = [&](int kk) { return kk > 1 ? size_t(kk) * size_t(M) * P * 4 : size_t(0); };
+  int kmax = max(k8, k4);
+  while (kmax > 1 && need(kmax) > ws_bytes) {
+    k8 = min(k8, kmax - 1);
+    k4 = min(k4, kmax - 1);
+    kmax = max(k8, k4);
+  }
+  W48Split p;
+  p.seg8 = (G + k8 - 1) / k8;
+  p.kseg8 = (G + p.seg8 - 1) / p.seg8;
+  p.seg4 = (G + k4 - 1) / k4;
+  p.kseg4 = (G + p.seg4 - 1) / p.seg4;
+  p.ws_bytes = need(max(p.kseg8, p.kseg4));
+  return p;
+}
+
+// Whether (M, ga) runs the stream kernel, in one pass (M <= 64) or in 64-token
+// passes (M <= 128 where the tile kernel's single row of workgroups would
+// leave CUs idle).
+bool w48_streams(int T8, int T4, int M, int ga) {
+  if (ga == 128 || M > 128) return false;
+  return M <= 64 || (T8 + 3) / 4 + (T4 + 7) / 8 <= device_compute_units();
+}
+
+namespace {
+
 // Picks the kernel for (M, ga).  A call with a.acc_out set takes the same
 // route with the kernel's group-sum store in place of its scaling step, so
-// the exported int32 sums are those of the kernel that runs the product.
-int launch(const W48Args& a, void* stream) {
+// the exported int32 sums are those of the kernel that runs the product; it
+// takes the K split of a call with workspace enough for it (the group sums do
+// not depend on the split, but the segment bounds are then exercised).
+int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
+  W48Args a = a0;
   const int T = a.T8 + a.T4;
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool acc = a.acc_out != nullptr;
-  const int tile_rows = (a.T8 + 3) / 4 + (a.T4 + 7) / 8;   // row blocks of the tile kernel
-  if (a.M > 64 && a.M <= 128 && a.ga != 128 && tile_rows <= device_compute_units()) {
-    // Neither kernel splits K.  Here the tile kernel's single row of
+  if (a.M > 64 && w48_streams(a.T8, a.T4, a.M, a.ga)) {
+    // The tile kernel does not split K, and here its single row of
     // workgroups leaves CUs idle while each walks all of K, so two 64-token
-    // passes of the stream kernel, which reads the weights at HBM speed, are
-    // faster.  Per-token scales make a token range a self-contained call.
+    // passes of the stream kernel, which reads the weights at HBM speed (and
+    // splits K where its own grid is small), are faster.  Per-token scales
+    // make a token range a self-contained call; the passes run one after the
+    // other on the stream, so they share the workspace.
     W48Args c = a;
     for (int m0 = 0; m0 < a.M; m0 += 64) {
       c.M = a.M - m0 < 64 ? a.M - m0 : 64;
@@ -737,12 +860,18 @@ int launch(const W48Args& a, void* stream) {
       c.xs = a.xs ? a.xs + m0 : nullptr;
       c.y = a.y ? a.y + size_t(m0) * size_t(a.N) : nullptr;
       c.acc_out = acc ? a.acc_out + size_t(m0) * size_t(a.N) * size_t(a.K / 128) : nullptr;
-      const int rc = launch(c, stream);
+      const int rc = launch(c, workspace, ws_bytes, stream);
       if (rc != 0) return rc;
     }
     return 0;
   }
   if (a.M <= 64 && a.ga != 128) {
+    const W48Split sp = w48_split(a.N, a.K, a.T8, a.T4, a.M, acc ? SIZE_MAX : workspace ? ws_bytes : 0);
+    a.kseg8 = sp.kseg8;
+    a.seg8 = sp.seg8;
+    a.kseg4 = sp.kseg4;
+    a.seg4 = sp.seg4;
+    if (!acc && (sp.kseg8 > 1 || sp.kseg4 > 1)) a.part = static_cast<float*>(workspace);
     if (acc)
       launch_stream<true>(a, s);
     else
@@ -769,12 +898,12 @@ int launch_quant_act(const uint16_t* x, int M, int K, int ga, int8_t* xq, uint16
 }
 
 int launch_w48(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y, int M,
-               void* stream) {
-  return launch(make_args(im, xq, xs, ga, y, nullptr, M), stream);
+               void* workspace, size_t ws_bytes, void* stream) {
+  return launch(make_args(im, xq, xs, ga, y, nullptr, M), workspace, ws_bytes, stream);
 }
 
 int launch_w48_acc(const W48ImageView& im, const int8_t* xq, int ga, int32_t* acc, int M, void* stream) {
-  return launch(make_args(im, xq, nullptr, ga, nullptr, acc, M), stream);
+  return launch(make_args(im, xq, nullptr, ga, nullptr, acc, M), nullptr, 0, stream);
 }
 
 }  // namespace gbb

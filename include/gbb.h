@@ -344,6 +344,36 @@ gbb_status gbb_quant_act_i8(const uint16_t* x, int M, int K, int ga, int8_t* xq,
 gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, const int8_t* xq,
                           const uint16_t* xs, int ga, uint16_t* y, int M, void* stream);
 
+/* Workspace bytes for gbb_gemm_w48a8_split (0 when the call does not split
+ * K, or on invalid arguments): the fp32 partial sums of the K split,
+ * segments x M x padded rows x 4 bytes (M at most 64, the tokens of one pass
+ * of the streaming kernel; padded rows: each of the two row sets rounded up
+ * to a multiple of 16). */
+size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga);
+
+/* gbb_gemm_w48a8 with a caller workspace, for small batches on matrices with
+ * few output rows per compute unit (MixLLM page, section 3.3: the same
+ * two-step product over a K range cut into segments).  Where the streaming
+ * kernel (M <= 64 per pass, per-token activation scales) has row blocks for
+ * at most one workgroup per compute unit, an 8-bit row block counted twice,
+ * each row block's 128-column groups are cut into up to 16 segments of at
+ * least 8 groups, an 8-bit row block into twice as many as a 4-bit one, so
+ * that every workgroup streams about the same bytes.  Each segment writes
+ * its fp32 sum of s_w-scaled group products for every output to the
+ * workspace; a second launch adds the segments in order, multiplies by s_a,
+ * rounds to fp16, writes each output to its original row and clears the
+ * workspace.  With a workspace smaller than gbb_gemm_w48a8_workspace(N, K,
+ * n8, M, ga) (or NULL) the call takes as many segments as fit, down to none
+ * (then it equals gbb_gemm_w48a8).  The segment counts fix the order of the
+ * fp32 sums: for one ws_bytes the result is the same on every call.
+ *   workspace/ws_bytes  device memory, 16-byte aligned, zero-filled before
+ *          its first use (every call leaves it zero); calls that may overlap
+ *          need separate workspaces.
+ * Errors: those of gbb_gemm_w48a8; GBB_E_ALIGN for a misaligned workspace. */
+gbb_status gbb_gemm_w48a8_split(const void* image, int N, int K, int n8, const int8_t* xq,
+                                const uint16_t* xs, int ga, uint16_t* y, int M, void* workspace,
+                                size_t ws_bytes, void* stream);
+
 /* Debug export of the first step of the two-step dequantization (MixLLM
  * page, section 3.3: per group an exact integer product of the int8
  * activations and the int8 weight codes (q - z), before any scale):
@@ -351,8 +381,9 @@ gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, const int8_t*
  * original row n (device int32 [M][N][K/128]), for bit-exact tests.  The call
  * runs the kernel gbb_gemm_w48a8 runs for the same M and ga (K or 128), with
  * that kernel's scaling step replaced by a store of the group sums, so the
- * integers checked are those the product path forms.  Errors as
- * gbb_gemm_w48a8. */
+ * integers checked are those the product path forms; the streaming kernel
+ * runs with the K segments that gbb_gemm_w48a8_split takes with a full
+ * workspace.  Errors as gbb_gemm_w48a8. */
 gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq, int ga,
                              int32_t* acc, int M, void* stream);
 

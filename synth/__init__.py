@@ -248,6 +248,13 @@ def w44a8_28672x8192() -> Tuple[np.ndarray, np.ndarray]:
     return W, salient_rows_by_l2(W, 0.10)
 
 
+def w44a8_8192x28672() -> Tuple[np.ndarray, np.ndarray]:
+    """The same recipe at the down projection's shape (8192x28672): the
+    819 rows with the largest L2 norm are the 8-bit set."""
+    W = weight_heavy_rows(8192, 28672, WL_W44A8, 1)
+    return W, salient_rows_by_l2(W, 0.10)
+
+
 # Launch groups of a decoder layer: projections that read the same input are
 # stacked along the output rows into one matrix, as serving stacks do
 # (q|k|v and gate|up), so a layer is four products.

@@ -864,6 +864,97 @@ def test_w44a8_28672x8192_group_acc_bit_exact(M):
     assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows))
 
 
+def w48_split_call(img, N, K, n8, xq, xs, ws, ga=None):
+    """gbb_gemm_w48a8_split through the C ABI with the workspace ws (a
+    uint8 device tensor, or None)."""
+    M = xq.shape[0]
+    y = torch.full((M, N), float("nan"), dtype=torch.float16, device=xq.device)
+    st = gbb.lib().gbb_gemm_w48a8_split(img.data_ptr(), N, K, n8, xq.data_ptr(), xs.data_ptr(),
+                                        K if ga is None else ga, y.data_ptr(), M,
+                                        ws.data_ptr() if ws is not None else None,
+                                        ws.numel() if ws is not None else 0,
+                                        torch.cuda.current_stream().cuda_stream)
+    assert st == 0, gbb.lib().gbb_last_error().decode()
+    return y
+
+
+# (N, K, M): the stream kernel's K split.  2048 x 16384 (10 % 8-bit rows) has
+# 4 8-bit and 29 4-bit row blocks: 16 segments of 8 groups for the former,
+# 13 of 10 groups (the last one 8) for the latter; M = 96 runs two 64-token
+# passes through one workspace; 4096 x 4096 at M = 1 has 4 segments of 8
+# groups for both.
+W48_SPLIT_CASES = [(2048, 16384, 1), (2048, 16384, 17), (2048, 16384, 64), (2048, 16384, 96), (4096, 4096, 1)]
+
+
+@pytest.mark.parametrize("N,K,M", W48_SPLIT_CASES)
+def test_w48_split_k(N, K, M):
+    """The K-split stream kernel against the oracle (one row per 16-row
+    tile), the same on every call, the workspace zero afterwards; a smaller
+    workspace takes fewer segments and stays within the tolerance; without a
+    workspace the call equals gbb_gemm_w48a8 bit for bit."""
+    W = small(N, K, 7 * N + M)
+    rows8 = synth.salient_rows_by_l2(W, 0.1)
+    img = to_dev(gbb.pack_w48(W, rows8)[0])
+    x = rand_x(M, K, 5 * N + M)
+    xq, xs = gbb.quant_act_i8(to_dev(x))
+    need = gbb.gemm_w48a8_workspace(N, K, rows8.size, M)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    ys = [w48_split_call(img, N, K, rows8.size, xq, xs, ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws) == 0
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    rows = one_row_per(packed_rows(N, rows8), 16, N + M)
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0])
+    assert bq.rel_inf_err(ys[0].cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
+    half = torch.zeros(need // 2 + 16, dtype=torch.uint8, device=dev())
+    yh = w48_split_call(img, N, K, rows8.size, xq, xs, half)
+    y0 = w48_split_call(img, N, K, rows8.size, xq, xs, None)
+    y1 = gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, split=False)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(half) == 0
+    assert bq.rel_inf_err(yh.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert bq.rel_inf_err(y0.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
+    with pytest.raises(gbb.GbbError):
+        gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, workspace=ws[4:])
+
+
+@functools.lru_cache(maxsize=1)
+def w44a8_down_image():
+    W, rows8 = synth.w44a8_8192x28672()
+    img, _, _ = gbb.pack_w48(W, rows8)
+    return W, rows8, to_dev(img)
+
+
+@pytest.mark.parametrize("M", [1, 32, 64, 96])
+def test_w44a8_8192x28672(M):
+    """The 8192 x 28672 (down projection) layer in the launches the benchmark
+    times, with the K split: one checked row in every 16-row tile."""
+    W, rows8, img = w44a8_down_image()
+    assert rows8.size == 819
+    x = synth.activations(M, 28672, synth.WL_W44A8, 2)
+    xq, xs = gbb.quant_act_i8(to_dev(x))
+    y = gbb.gemm_w48a8(img, 8192, 28672, rows8.size, xq, xs).cpu().numpy()
+    rows = one_row_per(packed_rows(8192, rows8), 16, M)
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0])
+    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+
+
+def test_w44a8_8192x28672_group_acc_bit_exact():
+    """Exact int32 group sums of the K-split stream kernel on the 8192 x
+    28672 layer at 32 tokens (every segment's groups), one row per tile."""
+    W, rows8, img = w44a8_down_image()
+    x = synth.activations(32, 28672, synth.WL_W44A8, 3)
+    xq, _ = gbb.quant_act_i8(to_dev(x))
+    rows = one_row_per(packed_rows(8192, rows8), 16, 7)
+    acc = gbb.w48_group_acc(img, 8192, 28672, rows8.size, xq)
+    got = acc[:, torch.from_numpy(rows).to(acc.device)].cpu().numpy().astype(np.int64)
+    del acc
+    assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows))
+
+
 # ----------------------------------------------------------------------------
 # 64x64 blocks
 # ----------------------------------------------------------------------------

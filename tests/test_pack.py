@@ -365,3 +365,38 @@ def test_64x64_workspace_sizes():
                 assert ws in (0, min(M, 32) * N * 12) or (M > 32 and ws % (N * 12) == 0 and ws <= 32 * N * 12), \
                     (N, K, M, ws)
     assert gbb.gemm_mixed_w_64x64_workspace(64, 96, 1) == 0      # not whole blocks
+
+
+@pytest.mark.parametrize("N,K,frac", [(8192, 28672, 0.1), (28672, 8192, 0.1), (2048, 16384, 0.1), (4096, 4096, 0.1),
+                                      (48, 256, 0.1), (300, 1024, 1.0)])
+def test_w48_split_workspace(N, K, frac):
+    """Host side of the W4.4A8 K split: the streaming kernel (per-token
+    scales, M <= 64 per pass, and 64-token passes up to 128 tokens where the
+    tile kernel has at most one row block per CU) splits K when its row
+    blocks, an 8-bit one counted twice, fill at most one workgroup per CU:
+    segments of at least 8 groups, at most 16, an 8-bit row block taking
+    twice the segments of a 4-bit one, so that two workgroups per CU stream
+    about equal bytes.  The workspace is the fp32 partials over the padded
+    rows (the larger segment count x the pass's tokens x 16 (T8 + T4) x 4
+    bytes), 0 everywhere else."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    n8 = int(np.floor(frac * N + 0.5))
+    T8, T4 = -(-n8 // 16), -(-(N - n8) // 16)
+    nb8, nb4, G = -(-T8 // 4), -(-T4 // 4), K // 128
+    kcap = max(1, min(16, G // 8))
+    k8 = k4 = 1
+    if 2 * nb8 + nb4 <= cus:
+        if nb4:
+            k4 = max(1, min(kcap, 2 * cus // (2 * nb8 + nb4)))
+            k8 = min(kcap, 2 * k4) if nb8 else 1
+        else:
+            k8 = max(1, min(kcap, 2 * cus // nb8))
+    kseg = lambda k: -(-G // -(-G // k))
+    kmax = max(kseg(k8), kseg(k4))
+    for M in (1, 16, 32, 64, 65, 96, 128, 129, 512):
+        for ga in (K, 128):
+            streams = ga == K and (M <= 64 or (M <= 128 and nb8 + -(-T4 // 8) <= cus))
+            want = kmax * min(M, 64) * 16 * (T8 + T4) * 4 if streams and kmax > 1 else 0
+            assert gbb.gemm_w48a8_workspace(N, K, n8, M, ga) == want, (M, ga)
+    assert gbb.gemm_w48a8_workspace(N, K, n8, 0, K) == 0
