@@ -78,6 +78,30 @@ def measured_traffic():
 EXTRAS = ("llama3_70b_batch", "llama3_8b", "mixed_vs_uniform", "blocks_64x64", "linear_4096", "prefill", "w44a8")
 
 
+def gpu_max_clock_mhz():
+    """The GPU agent's maximum engine clock as rocminfo reports it (None if
+    rocminfo is unavailable); the peaks used here are the published figures,
+    which assume 2400 MHz on 256 CUs."""
+    import subprocess
+    if any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ):
+        return None   # under a profiler, whose library has already opened the GPU in this process
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    gpu = False
+    for line in out.splitlines():
+        line = line.strip()
+        if line.startswith("Name:") and "gfx" in line:
+            gpu = True
+        elif gpu and line.startswith("Max Clock Freq. (MHz):"):
+            try:
+                return int(line.split(":")[1].split()[0])
+            except (IndexError, ValueError):
+                return None
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -333,6 +357,8 @@ def main():
               "(the path would shard by output rows or by K; that is not built here); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    max_clock = gpu_max_clock_mhz()   # before this process opens the GPU
+
     import torch
 
     import gemm_block_bit_amd as gbb
@@ -354,7 +380,8 @@ def main():
 
     device_info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
-                   "memory_GiB": round(props.total_memory / 2**30, 1)}
+                   "memory_GiB": round(props.total_memory / 2**30, 1),
+                   "max_clock_MHz": max_clock}
     h = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
 
     # ---------------- headline: Llama-3-70B layers, decode M = 1 ----------------
