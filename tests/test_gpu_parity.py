@@ -450,6 +450,71 @@ def test_batched_graph_replays(M):
     del g
 
 
+def test_split_k_graph_replays():
+    """The two K-split paths captured in one HIP graph -- the prefill kernel
+    with split_reduce_kernel (2048 x 16384, M = 300: 3 token tiles x 4 row
+    tiles, 16 segments) and the W4.4A8 stream kernel with w48_reduce_kernel
+    (2048 x 16384, M = 32) -- and replayed three times with eager work and
+    synchronizations between the replays: every replay equals the eager calls
+    bit for bit and the oracle within 2e-3, and the workspaces are zero after
+    each."""
+    N1, K1, M1 = 2048, 16384, 300
+    W1 = small(N1, K1, 131)
+    bits1 = synth.random_bitmap(N1, K1, ALLOWED, 131)
+    img1 = packed(W1, bits1)
+    x1h = rand_x(M1, K1, 132)
+    x1 = to_dev(x1h)
+    need1 = gbb.gemm_mixed_w_workspace(N1, K1, M1)
+    assert need1 == 16 * M1 * N1 * 4
+    ws1 = torch.zeros(need1, dtype=torch.uint8, device=dev())
+    y1 = torch.empty((M1, N1), dtype=torch.float16, device=dev())
+    N2, K2, M2 = 2048, 16384, 32
+    W2 = small(N2, K2, 133)
+    rows8 = synth.salient_rows_by_l2(W2, 0.1)
+    img2 = to_dev(gbb.pack_w48(W2, rows8)[0])
+    x2h = rand_x(M2, K2, 134)
+    xq, xs = gbb.quant_act_i8(to_dev(x2h))
+    need2 = gbb.gemm_w48a8_workspace(N2, K2, rows8.size, M2)
+    assert need2 > 0
+    ws2 = torch.zeros(need2, dtype=torch.uint8, device=dev())
+    y2 = torch.empty((M2, N2), dtype=torch.float16, device=dev())
+
+    def calls():
+        gbb.gemm_mixed_w(img1, N1, K1, x1, out=y1, workspace=ws1)
+        gbb.gemm_w48a8(img2, N2, K2, rows8.size, xq, xs, out=y2, workspace=ws2)
+
+    calls()
+    torch.cuda.synchronize()
+    e1, e2 = y1.clone(), y2.clone()
+    rows1 = sample_rows(N1, 135)
+    ref1 = bq.reference_rows(x1h, W1, bits1, rows1)
+    assert bq.rel_inf_err(e1.cpu().numpy()[:, rows1].astype(np.float64), ref1) <= TOL
+    rows2 = one_row_per(packed_rows(N2, rows8), 16, 136)
+    ref2 = ow48.reference(x2h, W2[rows2], np.nonzero(np.isin(rows2, rows8))[0])
+    assert bq.rel_inf_err(e2.cpu().numpy()[:, rows2].astype(np.float64), ref2) <= TOL
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        y1.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), e1.view(torch.int16)), rep
+        assert torch.equal(y2.view(torch.int16), e2.view(torch.int16)), rep
+        assert not torch.any(ws1) and not torch.any(ws2), rep
+        gbb.gemm_mixed_w(img1, N1, K1, x1[:64].contiguous())   # eager work between replays
+        torch.cuda.synchronize()
+    del g
+
+
 def test_batched_llama3_8b_layer_m1():
     """The Llama-3-8B layer's four launch groups (q|k|v, o, gate|up, down)
     as one grouped launch at M = 1, one checked row per block row."""
