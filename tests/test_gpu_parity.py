@@ -170,7 +170,8 @@ def test_prefill_split_k(N, K, M, bc):
     of the CUs, the workspace the path-aware query asks for): three calls
     on one workspace are bit-identical (the partials are added in segment
     order, whatever finishes last), within 2e-3 of the oracle, and leave
-    the workspace zero."""
+    the workspace zero.  With half that workspace the call takes fewer
+    segments, with none it runs unsplit; both stay within 2e-3."""
     lib = gbb.lib()
     need = (lib.gbb_gemm_mixed_w_path_workspace if bc == 128 else lib.gbb_gemm_mixed_w_64x64_path_workspace)(N, K, M, 2)
     assert need > 0   # the split is taken
@@ -190,7 +191,15 @@ def test_prefill_split_k(N, K, M, bc):
         assert not torch.any(ws)
         first = y.clone() if first is None else first
         assert torch.equal(y.view(torch.int16), first.view(torch.int16))
-    assert rel_err(first, bq.reference_gemm(x, W, bits, block_cols=bc)) <= TOL
+    ref = bq.reference_gemm(x, W, bits, block_cols=bc)
+    assert rel_err(first, ref) <= TOL
+    half = torch.zeros(need // 2 + 16, dtype=torch.uint8, device=dev())
+    yh = call(img, N, K, to_dev(x), 2, workspace=half)
+    y0 = call(img, N, K, to_dev(x), 2, workspace=torch.zeros(256, dtype=torch.uint8, device=dev()))
+    torch.cuda.synchronize()
+    assert not torch.any(half)
+    assert rel_err(yh, ref) <= TOL
+    assert rel_err(y0, ref) <= TOL
 
 
 def test_workspace_reuse_across_shapes():
