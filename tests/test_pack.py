@@ -400,3 +400,22 @@ def test_w48_split_workspace(N, K, frac):
             want = kmax * min(M, 64) * 16 * (T8 + T4) * 4 if streams and kmax > 1 else 0
             assert gbb.gemm_w48a8_workspace(N, K, n8, M, ga) == want, (M, ga)
     assert gbb.gemm_w48a8_workspace(N, K, n8, 0, K) == 0
+
+
+def test_w48_split_argument_errors():
+    """gbb_gemm_w48a8_split rejects bad arguments before touching the device
+    (the pointers are never dereferenced: every call fails a check first)."""
+    L = gbb.lib()
+    A = 4096   # a 16-byte aligned fake device address
+    N, K, n8 = 64, 256, 8
+    assert L.gbb_gemm_w48a8_split(None, N, K, n8, A, A, K, A, 4, A, 256, None) == -1      # no image
+    assert L.gbb_gemm_w48a8_split(A, N, 200, n8, A, A, 200, A, 4, A, 256, None) == -2     # K % 128
+    assert L.gbb_gemm_w48a8_split(A, N, K, N + 1, A, A, K, A, 4, A, 256, None) == -2      # n8 > N
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, A, A, K, A, -1, A, 256, None) == -1        # M < 0
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, A, A, K, A, 0, A, 256, None) == 0          # M == 0: nothing
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, None, A, K, A, 4, A, 256, None) == -1      # no xq
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, A, A, 64, A, 4, A, 256, None) == -1        # ga neither K nor 128
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, A + 2, A, K, A, 4, A, 256, None) == -4     # xq misaligned
+    assert L.gbb_gemm_w48a8_split(A, N, K, n8, A, A, K, A, 4, A + 4, 256, None) == -4     # workspace misaligned
+    assert L.gbb_gemm_w48a8_workspace(N, K, n8, 4, 64) == 0                               # invalid ga: 0
+    assert L.gbb_gemm_w48a8_workspace(N, 200, n8, 4, 200) == 0                            # invalid K: 0
