@@ -231,7 +231,7 @@ extern "C" size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga) 
   if (N <= 0 || K <= 0 || K % kGroup || n8 < 0 || n8 > N || M <= 0 || (ga != K && ga != 128)) return 0;
   const W48Layout l = w48_layout(N, K, n8);
   if (!w48_streams(l.T8, l.T4, M, ga)) return 0;
-  return w48_split(N, K, l.T8, l.T4, M < 64 ? M : 64, SIZE_MAX).ws_bytes;
+  return w48_split(K, l.T8, l.T4, M < 64 ? M : 64, SIZE_MAX).ws_bytes;
 }
 
 extern "C" gbb_status gbb_gemm_w48a8_split(const void* image, int N, int K, int n8, const int8_t* xq,

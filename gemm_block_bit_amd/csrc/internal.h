@@ -91,7 +91,7 @@ struct W48Split {
   int kseg8, seg8, kseg4, seg4;
   size_t ws_bytes;
 };
-W48Split w48_split(int N, int K, int T8, int T4, int M, size_t ws_bytes);
+W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes);
 bool w48_streams(int T8, int T4, int M, int ga);
 // workspace (16-byte aligned, zero at rest) of ws_bytes bounds the stream
 // kernel's K split; NULL runs it unsplit.

@@ -795,8 +795,7 @@ void launch_tile(const W48Args& a, hipStream_t s) {
 // the workgroups, two per CU, stream about equal bytes: an 8-bit row block
 // takes twice the segments of a 4-bit one.  With fewer than ws_bytes for the
 // fp32 partials (segments x M x packed rows), fewer segments.
-W48Split w48_split(int N, int K, int T8, int T4, int M, size_t ws_bytes) {
-  (void)N;
+W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
   const int nb8 = (T8 + 3) / 4, nb4 = (T4 + 3) / 4, G = K / 128, cus = device_compute_units();
   const int kcap = max(1, min(16, G / 8));
   int k8 = 1, k4 = 1;
@@ -866,7 +865,7 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
     return 0;
   }
   if (a.M <= 64 && a.ga != 128) {
-    const W48Split sp = w48_split(a.N, a.K, a.T8, a.T4, a.M, acc ? SIZE_MAX : workspace ? ws_bytes : 0);
+    const W48Split sp = w48_split(a.K, a.T8, a.T4, a.M, acc ? SIZE_MAX : workspace ? ws_bytes : 0);
     a.kseg8 = sp.kseg8;
     a.seg8 = sp.seg8;
     a.kseg4 = sp.kseg4;
