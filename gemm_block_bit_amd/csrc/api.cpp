@@ -75,18 +75,29 @@ W48ImageView w48_view(const void* image, int N, int K, int n8) {
   return v;
 }
 
-// For 32 < M the prefill kernel gives each CU one tile of 128 tokens x 512
-// rows, and when the tiles would fill at most half of the CUs it cuts each
-// tile's K range into segments (prefill_plan).  Only when even the split
-// grid fills at most half of the CUs (small matrices: few block rows and a
-// short K) does the batch run as ceil(M / 32) decode launches of 32 tokens
-// instead.  The split prefill wins on every Llama-3 shape measured (70B
-// down projection: M = 64, 128, 256 in 71, 95, 156 us against 112, 230,
-// 432 us as decode chunks).
+// For 32 < M: ceil(M / 32) decode launches of 32 tokens each stream the
+// whole matrix, so their cost grows with the chunk count, while the prefill
+// kernel (one tile of 128 tokens x 512 rows per CU, K cut into segments when
+// the tiles fill at most half of the CUs: prefill_plan) costs about the same
+// for any M up to its tile and grows slowly beyond.  The batch runs as
+// chunks when
+//     chunks x max(CUs / 4, g) <= 3/4 CUs,
+// g the split prefill's workgroups and a ragged last chunk counted as half
+// (a decode launch of few tokens costs about half one of 32): chunks win
+// on small matrices up to about three chunks, on matrices whose prefill
+// grid is larger only for a 32-token chunk plus a short one, and never
+// when the prefill grid fills the CUs.  Measured on Llama-3 shapes in
+// graphs: 70B q 8192 x 8192 at M = 64 / 128 in 49 / 97 us as chunks against
+// 37 / 50 us as split prefill; 70B k 1024 x 8192 at M = 96 in 33 us as
+// chunks against 41 us; 70B down projection at M = 64 in 60 us as split
+// prefill against 117 us as chunks.
 bool decode_in_chunks(int N, int K, int M, int bc) {
   if (M <= 32) return false;
   const PrefillPlan p = prefill_plan(N, K, M, bc, SIZE_MAX);
-  return size_t(2) * size_t(p.tiles) * size_t(p.kseg) <= size_t(device_compute_units());
+  const size_t cus = size_t(device_compute_units());
+  const size_t g = size_t(p.tiles) * size_t(p.kseg);
+  const size_t halves = size_t(2) * size_t(M / 32) + (M % 32 ? 1 : 0);   // chunks, in halves
+  return size_t(2) * halves * std::max(cus / 4, g) <= 3 * cus;
 }
 
 // Workspace of the decode launches of a batch of M tokens run as 32-token

@@ -166,11 +166,11 @@ size_t gbb_gemm_mixed_w_path_workspace(int N, int K, int M, int path);
  *   M >= 1.  M <= 32 runs the decode kernels (weights streamed once, matrix
  *   cores for the dot products).  Larger M runs the tiled prefill kernel,
  *   with its K range split into segments when its grid of 128-token x
- *   512-row tiles is small (see gbb_gemm_mixed_w_path_workspace), unless
- *   twice the split grid still fits in the device's compute units: then the
- *   decode kernels run the batch in 32-token chunks, one launch each, which
- *   keeps every CU busy where the prefill kernel would leave most of them
- *   idle.
+ *   512-row tiles is small (see gbb_gemm_mixed_w_path_workspace), or the
+ *   decode kernels in 32-token chunks, one launch each, when the chunks are
+ *   few against the prefill grid: chunks x max(CUs / 4, split prefill
+ *   workgroups) <= 3/4 of the device's compute units, a ragged last chunk
+ *   counted as half.
  *   workspace/ws_bytes  device memory of gbb_gemm_mixed_w_workspace(N, K, M)
  *          bytes (NULL allowed when that is 0).  On the prefill route the
  *          number of K segments follows ws_bytes, and with it the order of
@@ -290,8 +290,7 @@ gbb_status gbb_pack_blocks_64x64(const uint16_t* W, int N, int K, const uint8_t*
  * (K % 64 == 0).  M <= 32 runs the 64x64 decode kernels; larger M runs the
  * 64x64 prefill kernel (M * K < 2^31; K split into segments of at least
  * 1024 columns as for 64x128 blocks), or the decode kernels in 32-token
- * chunks where the split prefill grid would leave most compute units idle
- * (the same rule as for 64x128 blocks).  path: 0 that choice, 1 the decode
+ * chunks under the same rule as for 64x128 blocks.  path: 0 that choice, 1 the decode
  * kernel (M <= 32), 2 the prefill kernel. */
 size_t gbb_gemm_mixed_w_64x64_workspace(int N, int K, int M);
 gbb_status gbb_gemm_mixed_w_64x64(const void* image, int N, int K, const uint16_t* x,

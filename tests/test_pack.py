@@ -316,20 +316,31 @@ def _prefill_split(N, K, M, bc, cus):
     return tiles, kseg, (kseg * M * N * 4 if kseg > 1 else 0)
 
 
-@pytest.mark.parametrize("N,K", [(8192, 28672), (28672, 8192), (4096, 4096), (64, 128)])
+def _chunked(N, K, M, bc, cus):
+    """The documented choice of 32-token decode chunks for M > 32: the
+    chunk count (a ragged last chunk counted as half) times the larger of
+    CUs / 4 and the split prefill's workgroups is at most 3/4 of the CUs."""
+    tiles, kseg, _ = _prefill_split(N, K, M, bc, cus)
+    halves = 2 * (M // 32) + (1 if M % 32 else 0)
+    return M > 32 and 2 * halves * max(cus // 4, tiles * kseg) <= 3 * cus
+
+
+@pytest.mark.parametrize("N,K", [(8192, 28672), (28672, 8192), (4096, 4096), (8192, 8192), (1024, 8192),
+                                 (14336, 4096), (64, 128)])
 def test_workspace_follows_the_batch_route(N, K):
     """Host side of the dispatch: above 32 tokens the batch runs as 32-token
-    decode chunks only when the prefill grid, K split included, fills at
-    most half of the CUs (256 when the library finds no device); the
-    workspace is then the larger of the full and the ragged last chunk's
-    needs, and otherwise the prefill kernel's K split.  The path-aware
-    query gives the same for path 0 and the split for a forced prefill."""
+    decode chunks when few chunks would each cost less than the prefill
+    kernel on its (split) grid (256 CUs when the library finds no device);
+    the workspace is then the larger of the full and the ragged last
+    chunk's needs, and otherwise the prefill kernel's K split.  The
+    path-aware query gives the same for path 0 and the split for a forced
+    prefill."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
     lib = gbb.lib()
-    for M in (33, 64, 65, 96, 128, 200, 256, 512, 1024, 2048):
+    for M in (33, 64, 65, 96, 97, 128, 200, 256, 512, 1024, 2048):
         tiles, kseg, split_ws = _prefill_split(N, K, M, 128, cus)
-        chunked = 2 * tiles * kseg <= cus
+        chunked = _chunked(N, K, M, 128, cus)
         need = gbb.gemm_mixed_w_workspace(N, K, M)
         assert lib.gbb_gemm_mixed_w_path_workspace(N, K, M, 0) == need
         assert lib.gbb_gemm_mixed_w_path_workspace(N, K, M, 2) == split_ws
@@ -359,7 +370,7 @@ def test_64x64_workspace_sizes():
             for M in (1, 2, 8, 16, 17, 32, 33, 70):
                 ws = gbb.gemm_mixed_w_64x64_workspace(N, K, M)
                 tiles, kseg, split_ws = _prefill_split(N, K, M, 64, cus)
-                if M > 32 and 2 * tiles * kseg > cus:
+                if M > 32 and not _chunked(N, K, M, 64, cus):
                     assert ws == split_ws, (N, K, M, ws)
                     continue
                 assert ws in (0, min(M, 32) * N * 12) or (M > 32 and ws % (N * 12) == 0 and ws <= 32 * N * 12), \
