@@ -18,7 +18,7 @@ shapes with uniform 3- and 4-bit bitmaps (the cost of mixing bitwidths), one
 2.5 PFLOP/s fp16 dense peak) with an fp16 library GEMM on the dequantized
 weights for context, the same matrices at M = 64 ... 1024 (K split), the
 W4.4A8 layer (M = 32 ... 4096) and its down-projection shape 8192 x 28672
-at M = 1 ... 96 (K split), and the oracle timed on the host cores over one
+at M = 1 ... 256 (K split), and the oracle timed on the host cores over one
 copy of the headline layer (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--extras a,b,...]
@@ -660,15 +660,15 @@ def main():
 
         # ---------------- W4.4A8 8192 x 28672 (down projection), small batches ----------------
         # 129 row blocks for 256 CUs: the stream kernel splits K (6 segments
-        # for the 8-bit row blocks, 3 for the 4-bit ones), against the same
-        # kernel unsplit
+        # for the 8-bit row blocks, 3 for the 4-bit ones), and at M = 256 the
+        # tile kernel (2 and 4 segments), against the same kernels unsplit
         W, rows8 = synth.w44a8_8192x28672()
         img, _, _ = gbb.pack_w48(W, rows8)
         del W
         imgd = torch.from_numpy(img).to(dev)
         rot = Rotation([imgd] + [imgd.clone() for _ in range(3)])
         down = {}
-        for M in (1, 16, 32, 64, 96):
+        for M in (1, 16, 32, 64, 96, 256):
             x = torch.from_numpy(synth.activations(M, 28672, synth.WL_W44A8, 2)).to(dev)
             xq, xs = gbb.quant_act_i8(x)
             y = torch.empty((M, 8192), dtype=torch.float16, device=dev)

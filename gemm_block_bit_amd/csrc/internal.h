@@ -92,6 +92,8 @@ struct W48Split {
   size_t ws_bytes;
 };
 W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes);
+// The tile kernel's K split (M > 64), the same layout of partials.
+W48Split w48_tile_split(int K, int T8, int T4, int M, int ga, size_t ws_bytes);
 bool w48_streams(int T8, int T4, int M, int ga);
 // workspace (16-byte aligned, zero at rest) of ws_bytes bounds the stream
 // kernel's K split; NULL runs it unsplit.

@@ -331,7 +331,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // int32 group sums to a.acc_out instead of scaling them (the integer step of
 // this kernel, checked bit for bit).
 template <bool Q4, bool GA, bool ACC>
-__device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m0, int t0) {
+__device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m0, int t0, int seg) {
   using C = TileCfg<Q4>;
   constexpr int S = C::kStages, NJ = C::NJ;
   const uint32_t lbase = lds_u32(base);
@@ -340,6 +340,9 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
   const int tend = Q4 ? a.T8 + a.T4 : a.T8;   // end of this row set's packed tiles
   const int tw = t0 + NJ * wave;              // this wave's first packed tile
   const int G = a.K / 128, KT = a.K / 64;
+  // this workgroup's K segment: groups g0 ... gend - 1
+  const int sg = Q4 ? a.seg4 : a.seg8;
+  const int g0 = seg * sg, gend = min(G, g0 + sg);
 
   // Loads of group grp into its stage.  Tokens and tiles past the end are
   // clamped to the last valid one (read, then discarded).
@@ -379,11 +382,11 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 #pragma unroll
     for (int j = 0; j < NJ; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
 
-  issue(0);
-  for (int grp = 0; grp < G; ++grp) {
+  issue(g0);
+  for (int grp = g0; grp < gend; ++grp) {
     wait_vm<0>();      // this wave's loads of group grp have landed
     __syncthreads();   // everyone's have; every wave is done with grp - 1's stage
-    if (grp + 1 < G) issue(grp + 1);   // into grp - 1's stage
+    if (grp + 1 < gend) issue(grp + 1);   // into grp - 1's stage
     const uint8_t* st = base + (grp % S) * C::kStage;
     const uint8_t* B = st + C::kA + wave * C::kBw;
     const _Float16* Sv = reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256);
@@ -459,6 +462,25 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
   }
   if constexpr (ACC) return;
 
+  if (a.part) {
+    // K split: this segment's sums at the packed rows; w48_reduce_kernel
+    // adds the segments, applies the per-token scale and scatters
+    const int P = 16 * (a.T8 + a.T4);
+    float* pp = a.part + size_t(seg) * size_t(a.M) * size_t(P);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int tt = tw + j;
+      if (tt >= tend || a.rows[16 * tt + r16] < 0) continue;   // padding rows: no partials
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + 16 * i + 4 * g + v;
+          if (m < a.M) pp[size_t(m) * P + 16 * tt + r16] = tot[i][j][v];
+        }
+    }
+    return;
+  }
   // per-token scale, fused scatter to the original rows
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -490,18 +512,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ?
     W48Args a, int ntm, int nrb8, int nrb4, int per_xcd) {
   __shared__ u32x4 lds[kTileLds / 16];
   // workgroup i runs on XCD i % 8, which owns tiles [x per_xcd, (x + 1) per_xcd)
+  // with a K split, each row block stands for kseg8 (kseg4) consecutive
+  // (row block, K segment) units of the order
   const int bid = int(blockIdx.x);
   const int t = (bid & 7) * per_xcd + (bid >> 3);
-  const int nrb = nrb8 + nrb4;
+  const int nu8 = nrb8 * a.kseg8, nrb = nu8 + nrb4 * a.kseg4;
   if (t >= ntm * nrb) return;
   const int q = t / (kGroupRows * ntm), r = t - q * (kGroupRows * ntm);
-  const int gr = min(kGroupRows, nrb - q * kGroupRows);   // row blocks in this group
-  const int tm = r / gr, rb = q * kGroupRows + (r - tm * gr);
+  const int gr = min(kGroupRows, nrb - q * kGroupRows);   // row units in this group
+  const int tm = r / gr, ru = q * kGroupRows + (r - tm * gr);
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
-  if (rb < nrb8)
-    tile_body<false, GA, ACC>(a, base, tm * kTB, rb * 4);
-  else
-    tile_body<true, GA, ACC>(a, base, tm * kTB, a.T8 + (rb - nrb8) * 8);
+  if (ru < nu8) {
+    tile_body<false, GA, ACC>(a, base, tm * kTB, (ru / a.kseg8) * 4, ru % a.kseg8);
+  } else {
+    const int r4 = ru - nu8;
+    tile_body<true, GA, ACC>(a, base, tm * kTB, a.T8 + (r4 / a.kseg4) * 8, r4 % a.kseg4);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -712,14 +738,14 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
 // partials are in bounds and zero), so the loads overlap.
 __global__ __launch_bounds__(256) void w48_reduce_kernel(float* part, const int32_t* rows, const _Float16* xs,
                                                          _Float16* y, int M, int N, int P, int P8, int kseg8,
-                                                         int kseg4) {
+                                                         int kseg4, int per_token) {
   const size_t plane = size_t(M) * size_t(P);
   const size_t e = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (e >= plane) return;
   const int m = int(e / size_t(P)), p = int(e % size_t(P));
   const int k = p < P8 ? kseg8 : kseg4;
   const int n = rows[p];
-  const float sa = (float)xs[m];
+  const float sa = per_token ? (float)xs[m] : 1.0f;   // per-group scales are inside the partials
   float v[16];
 #pragma unroll
   for (int sg = 0; sg < 16; ++sg) v[sg] = sg < k ? part[size_t(sg) * plane + e] : 0.0f;
@@ -771,42 +797,36 @@ void launch_stream(const W48Args& a, hipStream_t s) {
     const int P = 16 * (a.T8 + a.T4);
     const size_t total = size_t(a.M) * size_t(P);
     hipLaunchKernelGGL(w48_reduce_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a.part, a.rows,
-                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4);
+                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4, 1);
   }
 }
 
 template <bool ACC>
 void launch_tile(const W48Args& a, hipStream_t s) {
   const int ntm = (a.M + kTB - 1) / kTB, nrb8 = (a.T8 + 3) / 4, nrb4 = (a.T4 + 7) / 8;
-  const int per_xcd = (ntm * (nrb8 + nrb4) + 7) / 8;
+  const int per_xcd = (ntm * (nrb8 * a.kseg8 + nrb4 * a.kseg4) + 7) / 8;
   const dim3 grid(unsigned(8 * per_xcd));
   if (a.ga == 128)
     hipLaunchKernelGGL((w48_tile_kernel<true, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   else
     hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+  if (!ACC && a.part) {
+    const int P = 16 * (a.T8 + a.T4);
+    const size_t total = size_t(a.M) * size_t(P);
+    hipLaunchKernelGGL(w48_reduce_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a.part, a.rows,
+                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4, a.ga == 128 ? 0 : 1);
+  }
 }
 
 }  // namespace
 
-// The stream kernel's K split for a pass of M <= 64 tokens.  An 8-bit row
-// block streams twice the bytes of a 4-bit one.  Counting it twice, when the
-// row blocks fill at most one workgroup per CU, each row block's groups are
-// cut into segments of at least 8 groups (1024 columns), at most 16, so that
-// the workgroups, two per CU, stream about equal bytes: an 8-bit row block
-// takes twice the segments of a 4-bit one.  With fewer than ws_bytes for the
-// fp32 partials (segments x M x packed rows), fewer segments.
-W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
-  const int nb8 = (T8 + 3) / 4, nb4 = (T4 + 3) / 4, G = K / 128, cus = device_compute_units();
-  const int kcap = max(1, min(16, G / 8));
-  int k8 = 1, k4 = 1;
-  if (2 * nb8 + nb4 <= cus) {
-    if (nb4) {
-      k4 = max(1, min(kcap, 2 * cus / (2 * nb8 + nb4)));
-      k8 = nb8 ? min(kcap, 2 * k4) : 1;
-    } else {
-      k8 = max(1, min(kcap, 2 * cus / nb8));
-    }
-  }
+namespace {
+
+// Segment sizes for k8 (k4) segments of the 8-bit (4-bit) row blocks, with
+// fewer segments when ws_bytes cannot hold the fp32 partials (segments x M
+// x packed rows).
+W48Split split_for(int k8, int k4, int K, int T8, int T4, int M, size_t ws_bytes) {
+  const int G = K / 128;
   const size_t P = size_t(16) * size_t(T8 + T4);
   auto need = [&](int kk) { return kk > 1 ? size_t(kk) * size_t(M) * P * 4 : size_t(0); };
   int kmax = max(k8, k4);
@@ -822,6 +842,59 @@ W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
   p.kseg4 = (G + p.seg4 - 1) / p.seg4;
   p.ws_bytes = need(max(p.kseg8, p.kseg4));
   return p;
+}
+
+}  // namespace
+
+// The stream kernel's K split for a pass of M <= 64 tokens.  An 8-bit row
+// block streams twice the bytes of a 4-bit one.  Counting it twice, when the
+// row blocks number at most 3/4 of the CUs, each row block's groups are cut
+// into segments of at least 8 groups (1024 columns), at most 16, so that the
+// workgroups, two per CU, stream about equal bytes: an 8-bit row block takes
+// twice the segments of a 4-bit one.  (With more row blocks the second
+// launch costs more than the extra workgroups gain: 14336 x 4096 at M = 64,
+// 248 units, ran 25 us split against 22 us.)  With fewer than ws_bytes for
+// the fp32 partials (segments x M x packed rows), fewer segments.
+W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
+  const int nb8 = (T8 + 3) / 4, nb4 = (T4 + 3) / 4, G = K / 128, cus = device_compute_units();
+  const int kcap = max(1, min(16, G / 8));
+  int k8 = 1, k4 = 1;
+  if (4 * (2 * nb8 + nb4) <= 3 * cus) {
+    if (nb4) {
+      k4 = max(1, min(kcap, 2 * cus / (2 * nb8 + nb4)));
+      k8 = nb8 ? min(kcap, 2 * k4) : 1;
+    } else {
+      k8 = max(1, min(kcap, 2 * cus / nb8));
+    }
+  }
+  return split_for(k8, k4, K, T8, T4, M, ws_bytes);
+}
+
+// The tile kernel's K split (M > 64).  A 4-bit row block (128 rows) does
+// twice the matrix-core work of an 8-bit one (64 rows).  Counting it twice,
+// when the token tiles x row blocks fill at most half of the resident
+// workgroup slots (three per CU, two with per-group activation scales),
+// each row block's groups are cut into segments of at least 8 groups, at
+// most 16, about enough to fill those slots, a 4-bit row block into twice
+// as many as an 8-bit one.  (Above half, the partials' round trip through
+// memory costs more than the extra workgroups gain: 14336 x 4096 at M = 256
+// ran 64 us split against 56 us.)  With fewer than ws_bytes for the
+// partials, fewer segments.
+W48Split w48_tile_split(int K, int T8, int T4, int M, int ga, size_t ws_bytes) {
+  const int ntm = (M + kTB - 1) / kTB, nrb8 = (T8 + 3) / 4, nrb4 = (T4 + 7) / 8, G = K / 128;
+  const int slots = (ga == 128 ? 2 : 3) * device_compute_units();
+  const int kcap = max(1, min(16, G / 8));
+  const int u = ntm * (nrb8 + 2 * nrb4);
+  int k8 = 1, k4 = 1;
+  if (2 * u <= slots) {
+    if (nrb8) {
+      k8 = max(1, min(kcap, slots / u));
+      k4 = min(kcap, 2 * k8);
+    } else {
+      k4 = max(1, min(kcap, slots / (ntm * nrb4)));
+    }
+  }
+  return split_for(k8, k4, K, T8, T4, M, ws_bytes);
 }
 
 // Whether (M, ga) runs the stream kernel, in one pass (M <= 64) or in 64-token
@@ -876,6 +949,12 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
     else
       launch_stream<false>(a, s);
   } else if (a.M > 64) {
+    const W48Split sp = w48_tile_split(a.K, a.T8, a.T4, a.M, a.ga, acc ? SIZE_MAX : workspace ? ws_bytes : 0);
+    a.kseg8 = sp.kseg8;
+    a.seg8 = sp.seg8;
+    a.kseg4 = sp.kseg4;
+    a.seg4 = sp.seg4;
+    if (!acc && (sp.kseg8 > 1 || sp.kseg4 > 1)) a.part = static_cast<float*>(workspace);
     if (acc)
       launch_tile<true>(a, s);
     else

@@ -345,21 +345,25 @@ gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, const int8_t*
 
 /* Workspace bytes for gbb_gemm_w48a8_split (0 when the call does not split
  * K, or on invalid arguments): the fp32 partial sums of the K split,
- * segments x M x padded rows x 4 bytes (M at most 64, the tokens of one pass
- * of the streaming kernel; padded rows: each of the two row sets rounded up
+ * segments x M x padded rows x 4 bytes (M at most 64, the tokens of one pass,
+ * on the streaming kernel; padded rows: each of the two row sets rounded up
  * to a multiple of 16). */
 size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga);
 
-/* gbb_gemm_w48a8 with a caller workspace, for small batches on matrices with
- * few output rows per compute unit (MixLLM page, section 3.3: the same
- * two-step product over a K range cut into segments).  Where the streaming
- * kernel (M <= 64 per pass, per-token activation scales) has row blocks for
- * at most one workgroup per compute unit, an 8-bit row block counted twice,
- * each row block's 128-column groups are cut into up to 16 segments of at
- * least 8 groups, an 8-bit row block into twice as many as a 4-bit one, so
- * that every workgroup streams about the same bytes.  Each segment writes
- * its fp32 sum of s_w-scaled group products for every output to the
- * workspace; a second launch adds the segments in order, multiplies by s_a,
+/* gbb_gemm_w48a8 with a caller workspace, for batches on matrices with few
+ * output rows per compute unit (MixLLM page, section 3.3: the same
+ * two-step product over a K range cut into segments).  The streaming kernel
+ * (M <= 64 per pass, per-token activation scales) splits K where its row
+ * blocks, an 8-bit one counted twice, number at most 3/4 of the compute
+ * units; each row block's 128-column groups are cut into up to 16
+ * segments of at least 8 groups, an 8-bit row block into twice as many as a
+ * 4-bit one, so that every workgroup streams about the same bytes.  The tile
+ * kernel (larger M) splits K where its token tiles x row blocks fill at most
+ * half of its resident workgroups, a 4-bit row block (twice the rows)
+ * counted twice and cut into twice the segments.  Each segment writes its
+ * fp32 sum of s_w-scaled group products (with per-group activation scales,
+ * of s_a s_w-scaled ones) for every output to the workspace; a second
+ * launch adds the segments in order, multiplies by the per-token s_a,
  * rounds to fp16, writes each output to its original row and clears the
  * workspace.  With a workspace smaller than gbb_gemm_w48a8_workspace(N, K,
  * n8, M, ga) (or NULL) the call takes as many segments as fit, down to none

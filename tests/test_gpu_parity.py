@@ -953,47 +953,50 @@ def w48_split_call(img, N, K, n8, xq, xs, ws, ga=None):
     return y
 
 
-# (N, K, M): the stream kernel's K split.  2048 x 16384 (10 % 8-bit rows) has
-# 4 8-bit and 29 4-bit row blocks: 16 segments of 8 groups for the former,
-# 13 of 10 groups (the last one 8) for the latter; M = 96 runs two 64-token
+# (N, K, M, ga): the K splits.  2048 x 16384 (10 % 8-bit rows) has 4 8-bit
+# and 29 4-bit stream row blocks: 16 segments of 8 groups for the former, 13
+# of 10 groups (the last one 8) for the latter; M = 96 runs two 64-token
 # passes through one workspace; 4096 x 4096 at M = 1 has 4 segments of 8
-# groups for both.
-W48_SPLIT_CASES = [(2048, 16384, 1), (2048, 16384, 17), (2048, 16384, 64), (2048, 16384, 96), (4096, 4096, 1)]
+# groups for both.  M = 129 and 300 run the tile kernel (4 8-bit and 15
+# 4-bit row blocks per token tile), with per-token and per-group scales.
+W48_SPLIT_CASES = [(2048, 16384, 1, None), (2048, 16384, 17, None), (2048, 16384, 64, None),
+                   (2048, 16384, 96, None), (4096, 4096, 1, None), (2048, 16384, 129, None),
+                   (2048, 16384, 300, None), (2048, 16384, 300, 128), (4096, 4096, 256, None)]
 
 
-@pytest.mark.parametrize("N,K,M", W48_SPLIT_CASES)
-def test_w48_split_k(N, K, M):
-    """The K-split stream kernel against the oracle (one row per 16-row
-    tile), the same on every call, the workspace zero afterwards; a smaller
-    workspace takes fewer segments and stays within the tolerance; without a
-    workspace the call equals gbb_gemm_w48a8 bit for bit."""
+@pytest.mark.parametrize("N,K,M,ga", W48_SPLIT_CASES)
+def test_w48_split_k(N, K, M, ga):
+    """The K-split stream and tile kernels against the oracle (one row per
+    16-row tile), the same on every call, the workspace zero afterwards; a
+    smaller workspace takes fewer segments and stays within the tolerance;
+    without a workspace the call equals gbb_gemm_w48a8 bit for bit."""
     W = small(N, K, 7 * N + M)
     rows8 = synth.salient_rows_by_l2(W, 0.1)
     img = to_dev(gbb.pack_w48(W, rows8)[0])
     x = rand_x(M, K, 5 * N + M)
-    xq, xs = gbb.quant_act_i8(to_dev(x))
-    need = gbb.gemm_w48a8_workspace(N, K, rows8.size, M)
+    xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+    need = gbb.gemm_w48a8_workspace(N, K, rows8.size, M, ga)
     assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
-    ys = [w48_split_call(img, N, K, rows8.size, xq, xs, ws) for _ in range(3)]
+    ys = [w48_split_call(img, N, K, rows8.size, xq, xs, ws, ga) for _ in range(3)]
     torch.cuda.synchronize()
     assert torch.count_nonzero(ws) == 0
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
     rows = one_row_per(packed_rows(N, rows8), 16, N + M)
-    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0])
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0], act_group=ga)
     assert bq.rel_inf_err(ys[0].cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
     half = torch.zeros(need // 2 + 16, dtype=torch.uint8, device=dev())
-    yh = w48_split_call(img, N, K, rows8.size, xq, xs, half)
-    y0 = w48_split_call(img, N, K, rows8.size, xq, xs, None)
-    y1 = gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, split=False)
+    yh = w48_split_call(img, N, K, rows8.size, xq, xs, half, ga)
+    y0 = w48_split_call(img, N, K, rows8.size, xq, xs, None, ga)
+    y1 = gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, ga, split=False)
     torch.cuda.synchronize()
     assert torch.count_nonzero(half) == 0
     assert bq.rel_inf_err(yh.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     assert bq.rel_inf_err(y0.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
     with pytest.raises(gbb.GbbError):
-        gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, workspace=ws[4:])
+        gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, ga, workspace=ws[4:])
 
 
 @functools.lru_cache(maxsize=1)
@@ -1003,7 +1006,7 @@ def w44a8_down_image():
     return W, rows8, to_dev(img)
 
 
-@pytest.mark.parametrize("M", [1, 32, 64, 96])
+@pytest.mark.parametrize("M", [1, 32, 64, 96, 256])
 def test_w44a8_8192x28672(M):
     """The 8192 x 28672 (down projection) layer in the launches the benchmark
     times, with the K split: one checked row in every 16-row tile."""

@@ -381,34 +381,60 @@ def test_64x64_workspace_sizes():
 @pytest.mark.parametrize("N,K,frac", [(8192, 28672, 0.1), (28672, 8192, 0.1), (2048, 16384, 0.1), (4096, 4096, 0.1),
                                       (48, 256, 0.1), (300, 1024, 1.0)])
 def test_w48_split_workspace(N, K, frac):
-    """Host side of the W4.4A8 K split: the streaming kernel (per-token
+    """Host side of the W4.4A8 K split.  The streaming kernel (per-token
     scales, M <= 64 per pass, and 64-token passes up to 128 tokens where the
     tile kernel has at most one row block per CU) splits K when its row
-    blocks, an 8-bit one counted twice, fill at most one workgroup per CU:
+    blocks, an 8-bit one counted twice, number at most 3/4 of the CUs:
     segments of at least 8 groups, at most 16, an 8-bit row block taking
-    twice the segments of a 4-bit one, so that two workgroups per CU stream
-    about equal bytes.  The workspace is the fp32 partials over the padded
-    rows (the larger segment count x the pass's tokens x 16 (T8 + T4) x 4
-    bytes), 0 everywhere else."""
+    twice the segments of a 4-bit one.  The tile kernel (M > 64 otherwise)
+    splits K when its token tiles x row blocks, a 4-bit one counted twice,
+    fill at most half of its resident workgroups (three per CU, two with
+    group scales), a 4-bit row block taking twice the segments of an 8-bit
+    one.
+    The workspace is the fp32 partials over the padded rows (the larger
+    segment count x the call's (pass's) tokens x 16 (T8 + T4) x 4 bytes),
+    0 everywhere else."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
     n8 = int(np.floor(frac * N + 0.5))
     T8, T4 = -(-n8 // 16), -(-(N - n8) // 16)
     nb8, nb4, G = -(-T8 // 4), -(-T4 // 4), K // 128
+    nrb8, nrb4 = -(-T8 // 4), -(-T4 // 8)
     kcap = max(1, min(16, G // 8))
+    kseg = lambda k: -(-G // -(-G // k))
+    P = 16 * (T8 + T4)
     k8 = k4 = 1
-    if 2 * nb8 + nb4 <= cus:
+    if 4 * (2 * nb8 + nb4) <= 3 * cus:
         if nb4:
             k4 = max(1, min(kcap, 2 * cus // (2 * nb8 + nb4)))
             k8 = min(kcap, 2 * k4) if nb8 else 1
         else:
             k8 = max(1, min(kcap, 2 * cus // nb8))
-    kseg = lambda k: -(-G // -(-G // k))
-    kmax = max(kseg(k8), kseg(k4))
-    for M in (1, 16, 32, 64, 65, 96, 128, 129, 512):
+    stream_kmax = max(kseg(k8), kseg(k4))
+
+    def tile_kmax(M, ga):
+        ntm = -(-M // 128)
+        slots = (2 if ga == 128 else 3) * cus
+        u = ntm * (nrb8 + 2 * nrb4)
+        t8 = t4 = 1
+        if 2 * u <= slots:
+            if nrb8:
+                t8 = max(1, min(kcap, slots // u))
+                t4 = min(kcap, 2 * t8)
+            else:
+                t4 = max(1, min(kcap, slots // (ntm * nrb4)))
+        return max(kseg(t8), kseg(t4))
+
+    for M in (1, 16, 32, 64, 65, 96, 128, 129, 256, 512, 2048):
         for ga in (K, 128):
-            streams = ga == K and (M <= 64 or (M <= 128 and nb8 + -(-T4 // 8) <= cus))
-            want = kmax * min(M, 64) * 16 * (T8 + T4) * 4 if streams and kmax > 1 else 0
+            streams = ga == K and (M <= 64 or (M <= 128 and nrb8 + nrb4 <= cus))
+            if streams:
+                want = stream_kmax * min(M, 64) * P * 4 if stream_kmax > 1 else 0
+            elif M > 64:
+                km = tile_kmax(M, ga)
+                want = km * M * P * 4 if km > 1 else 0
+            else:
+                want = 0
             assert gbb.gemm_w48a8_workspace(N, K, n8, M, ga) == want, (M, ga)
     assert gbb.gemm_w48a8_workspace(N, K, n8, 0, K) == 0
 
