@@ -241,9 +241,9 @@ extern "C" gbb_status gbb_gemm_w48a8(const void* image, int N, int K, int n8, co
 extern "C" size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga) {
   if (N <= 0 || K <= 0 || K % kGroup || n8 < 0 || n8 > N || M <= 0 || (ga != K && ga != 128)) return 0;
   const W48Layout l = w48_layout(N, K, n8);
-  if (w48_streams(l.T8, l.T4, M, ga)) return w48_split(K, l.T8, l.T4, M < 64 ? M : 64, SIZE_MAX).ws_bytes;
+  if (w48_streams(K, l.T8, l.T4, M, ga)) return w48_split(K, l.T8, l.T4, M < 64 ? M : 64, SIZE_MAX).ws_bytes;
   if (M > 64) return w48_tile_split(K, l.T8, l.T4, M, ga, SIZE_MAX).ws_bytes;
-  return 0;   // group activation scales at M <= 64: the register-staged kernel, no split
+  return 0;   // group activation scales over an odd group count at M <= 64: the register-staged kernel
 }
 
 extern "C" gbb_status gbb_gemm_w48a8_split(const void* image, int N, int K, int n8, const int8_t* xq,

@@ -94,7 +94,7 @@ struct W48Split {
 W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes);
 // The tile kernel's K split (M > 64), the same layout of partials.
 W48Split w48_tile_split(int K, int T8, int T4, int M, int ga, size_t ws_bytes);
-bool w48_streams(int T8, int T4, int M, int ga);
+bool w48_streams(int K, int T8, int T4, int M, int ga);
 // workspace (16-byte aligned, zero at rest) of ws_bytes bounds the stream
 // kernel's K split; NULL runs it unsplit.
 int launch_w48(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, int ga, uint16_t* y,

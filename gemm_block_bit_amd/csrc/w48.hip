@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ?
 // weight fragments, scales and zero points), so every wait is a fixed vmcnt.
 // One barrier per group publishes the shared activation fragments.
 // ---------------------------------------------------------------------------
-template <int TM>   // token tiles: M <= 16 TM
+template <int TM, bool GA>   // token tiles: M <= 16 TM; GA: per-group activation scales
 struct StreamCfg {
   // Stages - 1 groups per workgroup are in flight, two workgroups per CU:
   // five stages still fit two workgroups in the LDS for M <= 32, four for
@@ -551,17 +551,22 @@ struct StreamCfg {
   static constexpr int kB = 4 * 2048;                   // weight fragments, 2 KiB per wave
   static constexpr int kS = 4 * 256;                    // scales, 256 B per wave
   static constexpr int kZ = 4 * 256;                    // zero points, 256 B per wave
-  static constexpr int kStage = kA + kB + kS + kZ;
-  static constexpr int kLoads8 = NA + 3;                // loads per wave per group, 8-bit rows
-  static constexpr int kLoads4 = NA + 3;                // 4-bit rows
+  static constexpr int kX = GA ? 4 * 256 : 0;           // GA: the group pair's activation scales, per wave
+  static constexpr int kStage = kA + kB + kS + kZ + kX;
+  static constexpr int kLoads8 = NA + 3 + (GA ? 1 : 0);   // loads per wave per group, 8-bit rows
+  static constexpr int kLoads4 = NA + 3 + (GA ? 1 : 0);   // 4-bit rows
 };
 
 // One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.  ACC:
 // store each group's exact int32 sums to a.acc_out instead of scaling them.
-template <int TM, bool Q4, bool ACC>
+// GA: activation scales per (token, group), [M][G] with G even: each group
+// brings the scales of its pair of groups for every token (4 bytes a token,
+// so the loads stay dword-aligned), and they multiply the weight scale.
+template <int TM, bool GA, bool Q4, bool ACC>
 __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend, int seg,
                                              int seg_groups) {
-  using C = StreamCfg<TM>;
+  constexpr bool SA = GA && !ACC;   // the activation scales are loaded (ACC stores unscaled sums)
+  using C = StreamCfg<TM, SA>;
   constexpr int kStages = C::kStages;
   constexpr int kLoads = Q4 ? C::kLoads4 : C::kLoads8;
   const uint32_t lbase = lds_u32(base);
@@ -593,6 +598,8 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     gdma4_once(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
     if constexpr (Q4)
       gdma4_once(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
+    if constexpr (SA)   // lane m: the scales of groups (grp & ~1) and (grp | 1) of token m
+      gdma4(a.xs + size_t(min(lane, a.M - 1)) * G + (grp & ~1), st + C::kA + C::kB + C::kS + C::kZ + wave * 256);
   };
 
   f32x4 tot[TM];
@@ -605,6 +612,9 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
 #pragma unroll
   for (int i = 0; i < TM; ++i) cp[i] = i32x4{0, 0, 0, 0};
   float swp = 0.0f;
+  f32x4 sap[TM];   // GA: the previous group's activation scales of this lane's outputs
+#pragma unroll
+  for (int i = 0; i < TM; ++i) sap[i] = f32x4{0, 0, 0, 0};
 
   // ACC: this lane's original row (-1: none), loaded and awaited before the
   // first global->LDS load, so no later wait of the compiler's covers them
@@ -639,6 +649,14 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
 #pragma unroll
       for (int h = 0; h < 2; ++h) av[i][h] = *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
     const float sw = (float)reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256)[r16];
+    f32x4 sac[TM];   // GA: this group's activation scales of the lane's outputs (token 16 i + 4 g + v)
+    if constexpr (SA) {
+      const _Float16* X = reinterpret_cast<const _Float16*>(st + C::kA + C::kB + C::kS + C::kZ + wave * 256);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sac[i][v] = (float)X[2 * (16 * i + 4 * g + v) + (grp & 1)];
+    }
     i32x4 bv[2];
     if constexpr (!Q4) {
       bv[0] = *reinterpret_cast<const i32x4*>(B + 16 * lane);
@@ -674,16 +692,21 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), swp, tot[i][v]);
+      for (int v = 0; v < 4; ++v)
+        tot[i][v] = __builtin_fmaf(float(cp[i][v]), GA ? swp * sap[i][v] : swp, tot[i][v]);
 #pragma unroll
     for (int i = 0; i < TM; ++i) cp[i] = c[i];
     swp = sw;
+    if constexpr (SA) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sap[i] = sac[i];
+    }
   }
   if constexpr (ACC) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), swp, tot[i][v]);
+    for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), GA ? swp * sap[i][v] : swp, tot[i][v]);
 
   if (t0 + wave >= tend) return;
   const int n = a.rows[16 * (t0 + wave) + r16];
@@ -707,13 +730,13 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 16 * i + 4 * g + v;
-      if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(tot[i][v] * (float)a.xs[m]);
+      if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(GA ? tot[i][v] : tot[i][v] * (float)a.xs[m]);
     }
 }
 
-template <int TM, bool ACC>
+template <int TM, bool GA, bool ACC>
 __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
-  using C = StreamCfg<TM>;
+  using C = StreamCfg<TM, GA && !ACC>;
   static_assert(2 * C::kStages * C::kStage <= 160 * 1024, "two workgroups per CU");
   __shared__ u32x4 lds[C::kStages * C::kStage / 16];
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
@@ -721,10 +744,10 @@ __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
   // segments first, then the 4-bit row blocks' kseg4
   const int nb8 = (a.T8 + 3) / 4, nb4 = (a.T4 + 3) / 4, w8 = nb8 * a.kseg8, b = int(blockIdx.x);
   if (b < w8) {
-    stream_tiles<TM, false, ACC>(a, base, (b % nb8) * 4, a.T8, b / nb8, a.seg8);
+    stream_tiles<TM, GA, false, ACC>(a, base, (b % nb8) * 4, a.T8, b / nb8, a.seg8);
   } else {
     const int c = b - w8;
-    stream_tiles<TM, true, ACC>(a, base, a.T8 + (c % nb4) * 4, a.T8 + a.T4, c / nb4, a.seg4);
+    stream_tiles<TM, GA, true, ACC>(a, base, a.T8 + (c % nb4) * 4, a.T8 + a.T4, c / nb4, a.seg4);
   }
 }
 
@@ -784,21 +807,29 @@ W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, 
   return a;
 }
 
-template <bool ACC>
-void launch_stream(const W48Args& a, hipStream_t s) {
+template <bool GA, bool ACC>
+void launch_stream_ga(const W48Args& a, hipStream_t s) {
   const dim3 grid(unsigned((a.T8 + 3) / 4 * a.kseg8 + (a.T4 + 3) / 4 * a.kseg4));
   if (a.M <= 16)
-    hipLaunchKernelGGL((w48_stream_kernel<1, ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w48_stream_kernel<1, GA, ACC>), grid, dim3(256), 0, s, a);
   else if (a.M <= 32)
-    hipLaunchKernelGGL((w48_stream_kernel<2, ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w48_stream_kernel<2, GA, ACC>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((w48_stream_kernel<4, ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w48_stream_kernel<4, GA, ACC>), grid, dim3(256), 0, s, a);
   if (!ACC && a.part) {
     const int P = 16 * (a.T8 + a.T4);
     const size_t total = size_t(a.M) * size_t(P);
     hipLaunchKernelGGL(w48_reduce_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a.part, a.rows,
-                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4, 1);
+                       a.xs, a.y, a.M, a.N, P, 16 * a.T8, a.kseg8, a.kseg4, GA ? 0 : 1);
   }
+}
+
+template <bool ACC>
+void launch_stream(const W48Args& a, hipStream_t s) {
+  if (a.ga == 128)
+    launch_stream_ga<true, ACC>(a, s);
+  else
+    launch_stream_ga<false, ACC>(a, s);
 }
 
 template <bool ACC>
@@ -899,9 +930,13 @@ W48Split w48_tile_split(int K, int T8, int T4, int M, int ga, size_t ws_bytes) {
 
 // Whether (M, ga) runs the stream kernel, in one pass (M <= 64) or in 64-token
 // passes (M <= 128 where the tile kernel's single row of workgroups would
-// leave CUs idle).
-bool w48_streams(int T8, int T4, int M, int ga) {
-  if (ga == 128 || M > 128) return false;
+// leave CUs idle).  Per-group activation scales need an even group count
+// (their loads take two groups' scales at a time) and take one pass only:
+// their scaling makes the stream kernel slower than the tile kernel at two
+// passes (28672 x 8192 at M = 96: 127 against 118 us).
+bool w48_streams(int K, int T8, int T4, int M, int ga) {
+  if (ga == 128) return M <= 64 && (K / 128) % 2 == 0;
+  if (M > 128) return false;
   return M <= 64 || (T8 + 3) / 4 + (T4 + 7) / 8 <= device_compute_units();
 }
 
@@ -918,18 +953,21 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
   const unsigned gy = unsigned((T + 4 * kNT - 1) / (4 * kNT));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool acc = a.acc_out != nullptr;
-  if (a.M > 64 && w48_streams(a.T8, a.T4, a.M, a.ga)) {
-    // The tile kernel does not split K, and here its single row of
-    // workgroups leaves CUs idle while each walks all of K, so two 64-token
-    // passes of the stream kernel, which reads the weights at HBM speed (and
-    // splits K where its own grid is small), are faster.  Per-token scales
-    // make a token range a self-contained call; the passes run one after the
-    // other on the stream, so they share the workspace.
+  // per-group activation scales are loaded two groups (4 bytes) at a time
+  const bool xs_ok = a.ga != 128 || reinterpret_cast<uintptr_t>(a.xs) % 4 == 0;
+  if (a.M > 64 && xs_ok && w48_streams(a.K, a.T8, a.T4, a.M, a.ga)) {
+    // Here the tile kernel's single row of workgroups leaves CUs idle, and
+    // two 64-token passes of the stream kernel, which reads the weights at
+    // HBM speed (and splits K where its own grid is small), are faster even
+    // than the tile kernel split (8192 x 28672 at M = 128: 134 against
+    // 175 us).  A token range is a self-contained call (its rows of the
+    // activation scales, per token or per group, come with it); the passes
+    // run one after the other on the stream, so they share the workspace.
     W48Args c = a;
     for (int m0 = 0; m0 < a.M; m0 += 64) {
       c.M = a.M - m0 < 64 ? a.M - m0 : 64;
       c.xq = a.xq + size_t(m0) * size_t(a.K);
-      c.xs = a.xs ? a.xs + m0 : nullptr;
+      c.xs = a.xs ? a.xs + size_t(m0) * size_t(a.ga == 128 ? a.K / 128 : 1) : nullptr;
       c.y = a.y ? a.y + size_t(m0) * size_t(a.N) : nullptr;
       c.acc_out = acc ? a.acc_out + size_t(m0) * size_t(a.N) * size_t(a.K / 128) : nullptr;
       const int rc = launch(c, workspace, ws_bytes, stream);
@@ -937,7 +975,7 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
     }
     return 0;
   }
-  if (a.M <= 64 && a.ga != 128) {
+  if (a.M <= 64 && xs_ok && w48_streams(a.K, a.T8, a.T4, a.M, a.ga)) {
     const W48Split sp = w48_split(a.K, a.T8, a.T4, a.M, acc ? SIZE_MAX : workspace ? ws_bytes : 0);
     a.kseg8 = sp.kseg8;
     a.seg8 = sp.seg8;
@@ -959,7 +997,7 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
       launch_tile<true>(a, s);
     else
       launch_tile<false>(a, s);
-  } else if (a.M <= 32) {   // group activation scales, M <= 64
+  } else if (a.M <= 32) {   // group activation scales over an odd number of groups, M <= 64
     hipLaunchKernelGGL(w48_kernel<32>, dim3(unsigned((a.M + 31) / 32), gy), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(w48_kernel<64>, dim3(unsigned((a.M + 63) / 64), gy), dim3(256), 0, s, a);

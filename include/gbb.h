@@ -353,7 +353,8 @@ size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga);
 /* gbb_gemm_w48a8 with a caller workspace, for batches on matrices with few
  * output rows per compute unit (MixLLM page, section 3.3: the same
  * two-step product over a K range cut into segments).  The streaming kernel
- * (M <= 64 per pass, per-token activation scales) splits K where its row
+ * (M <= 64 per pass; per-token activation scales, or per-group ones over an
+ * even number of groups with xs 4-byte aligned) splits K where its row
  * blocks, an 8-bit one counted twice, number at most 3/4 of the compute
  * units; each row block's 128-column groups are cut into up to 16
  * segments of at least 8 groups, an 8-bit row block into twice as many as a

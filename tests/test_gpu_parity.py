@@ -958,10 +958,14 @@ def w48_split_call(img, N, K, n8, xq, xs, ws, ga=None):
 # of 10 groups (the last one 8) for the latter; M = 96 runs two 64-token
 # passes through one workspace; 4096 x 4096 at M = 1 has 4 segments of 8
 # groups for both.  M = 129 and 300 run the tile kernel (4 8-bit and 15
-# 4-bit row blocks per token tile), with per-token and per-group scales.
+# 4-bit row blocks per token tile), with per-token and per-group scales;
+# ga = 128 at M <= 64 runs the stream kernel with per-group scales, at
+# M = 96 the tile kernel.
 W48_SPLIT_CASES = [(2048, 16384, 1, None), (2048, 16384, 17, None), (2048, 16384, 64, None),
                    (2048, 16384, 96, None), (4096, 4096, 1, None), (2048, 16384, 129, None),
-                   (2048, 16384, 300, None), (2048, 16384, 300, 128), (4096, 4096, 256, None)]
+                   (2048, 16384, 300, None), (2048, 16384, 300, 128), (4096, 4096, 256, None),
+                   # the stream kernel with per-group activation scales
+                   (2048, 16384, 5, 128), (2048, 16384, 64, 128), (2048, 16384, 96, 128), (1024, 4096, 32, 128)]
 
 
 @pytest.mark.parametrize("N,K,M,ga", W48_SPLIT_CASES)

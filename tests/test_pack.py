@@ -381,9 +381,10 @@ def test_64x64_workspace_sizes():
 @pytest.mark.parametrize("N,K,frac", [(8192, 28672, 0.1), (28672, 8192, 0.1), (2048, 16384, 0.1), (4096, 4096, 0.1),
                                       (48, 256, 0.1), (300, 1024, 1.0)])
 def test_w48_split_workspace(N, K, frac):
-    """Host side of the W4.4A8 K split.  The streaming kernel (per-token
-    scales, M <= 64 per pass, and 64-token passes up to 128 tokens where the
-    tile kernel has at most one row block per CU) splits K when its row
+    """Host side of the W4.4A8 K split.  The streaming kernel (M <= 64 with
+    per-token scales, or per-group ones over an even group count; 64-token
+    passes up to 128 tokens with per-token scales where the tile kernel has
+    at most one row block per CU) splits K when its row
     blocks, an 8-bit one counted twice, number at most 3/4 of the CUs:
     segments of at least 8 groups, at most 16, an 8-bit row block taking
     twice the segments of a 4-bit one.  The tile kernel (M > 64 otherwise)
@@ -427,7 +428,10 @@ def test_w48_split_workspace(N, K, frac):
 
     for M in (1, 16, 32, 64, 65, 96, 128, 129, 256, 512, 2048):
         for ga in (K, 128):
-            streams = ga == K and (M <= 64 or (M <= 128 and nrb8 + nrb4 <= cus))
+            if ga == 128:
+                streams = M <= 64 and G % 2 == 0
+            else:
+                streams = M <= 64 or (M <= 128 and nrb8 + nrb4 <= cus)
             if streams:
                 want = stream_kmax * min(M, 64) * P * 4 if stream_kmax > 1 else 0
             elif M > 64:
