@@ -811,15 +811,18 @@ def w48_acc_reference(x, W, rows8, rows=None, ga=None):
 
 
 # (N, K, M, 8-bit row fraction, ga): the kernel gbb_gemm_w48a8 picks for the
-# same M and ga -- stream (M <= 64, per-token scales; 1, 2 and 4 token tiles),
-# two 64-token stream passes (65-128 tokens on a short tile grid), tile
-# (M > 64, both scale granularities), and the register-staged kernel (group
-# scales at M <= 64) -- forms the sums; K = 8192 with N reduced stands in for
-# the 28672 x 8192 layer
+# same M and ga -- stream (M <= 64, per-token scales or group scales over an
+# even group count; 1, 2 and 4 token tiles), two 64-token stream passes
+# (65-128 tokens with per-token scales on a short tile grid), tile (M > 64,
+# both scale granularities), and the register-staged kernel (group scales
+# over an odd group count at M <= 64, here K = 384) -- forms the sums, with
+# the K split of a call with a full workspace; K = 8192 with N reduced
+# stands in for the 28672 x 8192 layer
 W48_ACC_CASES = [(48, 256, 3, 0.1, None), (200, 384, 32, 0.1, None), (200, 384, 40, 0.1, None),
                  (64, 128, 17, 0.0, None), (40, 256, 70, 1.0, None), (300, 1024, 96, 0.2, None),
                  (300, 1024, 130, 0.2, None), (300, 1024, 40, 0.2, 128), (300, 1024, 130, 0.2, 128),
-                 (200, 512, 77, 0.5, 128), (2048, 8192, 32, 0.1, None), (2048, 8192, 96, 0.1, None),
+                 (200, 512, 77, 0.5, 128), (200, 384, 20, 0.1, 128), (200, 384, 50, 0.1, 128),
+                 (2048, 8192, 32, 0.1, None), (2048, 8192, 96, 0.1, None), (2048, 8192, 32, 0.1, 128),
                  (2048, 8192, 512, 0.1, None), (2048, 8192, 512, 0.1, 128)]
 
 
