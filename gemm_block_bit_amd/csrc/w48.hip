@@ -293,6 +293,10 @@ struct TileCfg {
 constexpr int kTileLds = TileCfg<true>::kStages * TileCfg<true>::kStage;
 static_assert(TileCfg<false>::kStages * TileCfg<false>::kStage <= kTileLds, "one LDS size serves both");
 static_assert(3 * kTileLds <= 160 * 1024, "three workgroups per CU");
+// Per-group activation scales staged in LDS: two buffers of 128 tokens x the
+// scales of a group pair (4 bytes), after the stages.
+constexpr int kTileXs = 2 * kTB * 4;
+static_assert(2 * (kTileLds + kTileXs) <= 160 * 1024, "two workgroups per CU with staged scales");
 
 // global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
 // LDS address lds + 16 l (4 l).  No output registers: completion is waited
@@ -330,7 +334,10 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // activation scales per (token, group), else per token.  ACC: store the exact
 // int32 group sums to a.acc_out instead of scaling them (the integer step of
 // this kernel, checked bit for bit).
-template <bool Q4, bool GA, bool ACC>
+// XS (with GA): the activation scales reach LDS with the group's loads (an
+// even group count and a 4-byte aligned scale array), else each output
+// reads its scale from memory.
+template <bool Q4, bool GA, bool ACC, bool XS>
 __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m0, int t0, int seg) {
   using C = TileCfg<Q4>;
   constexpr int S = C::kStages, NJ = C::NJ;
@@ -369,6 +376,11 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
     {   // scales: lanes 8 j + 0..7 bring tile j's 16 (the other lanes repeat them)
       const int tt = min(tw + ((lane >> 3) & (NJ - 1)), tend - 1);
       gdma4(a.s + (size_t(tt) * G + grp) * 16 + 2 * (lane & 7), sb + C::kA + C::kB + wave * 256);
+    }
+    if constexpr (GA && XS && !ACC) {   // waves 0 and 1: tokens 64 w + lane, the group pair's scales
+      if (wave < 2)
+        gdma4(a.xs + size_t(min(m0 + 64 * wave + lane, a.M - 1)) * G + (grp & ~1),
+              lbase + uint32_t(kTileLds + (grp & 1) * (kTB * 4) + wave * 256));
     }
     if constexpr (Q4) {   // zero points: lanes 4 j + 0..3 bring tile j's 16
       const int tt = min(tw + ((lane >> 2) & 1), tend - 1);
@@ -421,9 +433,14 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
           }
         }
       } else if constexpr (GA) {
+        // XS: the scales of tokens 16 i + 4 g ... + 3 in one 16-byte LDS read
+        u32x4 xp = u32x4{0, 0, 0, 0};
+        if constexpr (XS)
+          xp = *reinterpret_cast<const u32x4*>(base + kTileLds + (grp & 1) * (kTB * 4) + 4 * (16 * i + 4 * g));
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float sa = (float)a.xs[size_t(min(m0 + 16 * i + 4 * g + v, a.M - 1)) * G + grp];
+          const float sa = XS ? ((grp & 1) ? hi_half(xp[v]) : lo_half(xp[v]))
+                              : (float)a.xs[size_t(min(m0 + 16 * i + 4 * g + v, a.M - 1)) * G + grp];
 #pragma unroll
           for (int j = 0; j < NJ; ++j) tot[i][j][v] = __builtin_fmaf(float(ci[j][v]), sw[j] * sa, tot[i][j][v]);
         }
@@ -507,10 +524,10 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 constexpr int kGroupRows = 8;
 
 // per_xcd tiles of that order per XCD.
-template <bool GA, bool ACC>
+template <bool GA, bool ACC, bool XS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ? 2 : 3))) void w48_tile_kernel(
     W48Args a, int ntm, int nrb8, int nrb4, int per_xcd) {
-  __shared__ u32x4 lds[kTileLds / 16];
+  __shared__ u32x4 lds[(kTileLds + (GA && XS ? kTileXs : 0)) / 16];
   // workgroup i runs on XCD i % 8, which owns tiles [x per_xcd, (x + 1) per_xcd)
   // with a K split, each row block stands for kseg8 (kseg4) consecutive
   // (row block, K segment) units of the order
@@ -523,10 +540,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ?
   const int tm = r / gr, ru = q * kGroupRows + (r - tm * gr);
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
   if (ru < nu8) {
-    tile_body<false, GA, ACC>(a, base, tm * kTB, (ru / a.kseg8) * 4, ru % a.kseg8);
+    tile_body<false, GA, ACC, XS>(a, base, tm * kTB, (ru / a.kseg8) * 4, ru % a.kseg8);
   } else {
     const int r4 = ru - nu8;
-    tile_body<true, GA, ACC>(a, base, tm * kTB, a.T8 + (r4 / a.kseg4) * 8, r4 % a.kseg4);
+    tile_body<true, GA, ACC, XS>(a, base, tm * kTB, a.T8 + (r4 / a.kseg4) * 8, r4 % a.kseg4);
   }
 }
 
@@ -837,10 +854,14 @@ void launch_tile(const W48Args& a, hipStream_t s) {
   const int ntm = (a.M + kTB - 1) / kTB, nrb8 = (a.T8 + 3) / 4, nrb4 = (a.T4 + 7) / 8;
   const int per_xcd = (ntm * (nrb8 * a.kseg8 + nrb4 * a.kseg4) + 7) / 8;
   const dim3 grid(unsigned(8 * per_xcd));
-  if (a.ga == 128)
-    hipLaunchKernelGGL((w48_tile_kernel<true, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+  // per-group scales staged in LDS when they can be loaded two groups at a time
+  const bool xs_lds = (a.K / 128) % 2 == 0 && reinterpret_cast<uintptr_t>(a.xs) % 4 == 0;
+  if (a.ga == 128 && xs_lds)
+    hipLaunchKernelGGL((w48_tile_kernel<true, ACC, true>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+  else if (a.ga == 128)
+    hipLaunchKernelGGL((w48_tile_kernel<true, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   else
-    hipLaunchKernelGGL((w48_tile_kernel<false, ACC>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+    hipLaunchKernelGGL((w48_tile_kernel<false, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   if (!ACC && a.part) {
     const int P = 16 * (a.T8 + a.T4);
     const size_t total = size_t(a.M) * size_t(P);
