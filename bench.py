@@ -655,6 +655,20 @@ def main():
             if want_cpu:
                 oracle_inputs.setdefault("w44a8", {"img": img})[M] = sw
         extra["w44a8_28672x8192"] = w48
+        # the same layer with activation scales per group of 128 columns (the
+        # granularity the MixLLM page benchmarks)
+        w48g = {}
+        for M in (1, 32, 512):
+            x = torch.from_numpy(synth.activations(M, 8192, synth.WL_W44A8, 0)).to(dev)
+            xq, xs = gbb.quant_act_i8(x, 128)
+            y = torch.empty((M, 28672), dtype=torch.float16, device=dev)
+            sw = time_eager(torch, lambda: gbb.gemm_w48a8(rot.next(), 28672, 8192, rows8.size, xq, xs, 128, out=y), 30,
+                            min(200, max(4, int(30e-3 / (2.0 * M * 28672 * 8192 / 1e15)))))
+            ops = 2.0 * M * 28672 * 8192
+            w48g[f"M{M}"] = {"us": round(sw * 1e6, 1), "TOPs": round(ops / sw / 1e12, 1),
+                             "weight_GBps": round(img.size / sw / 1e9, 1)}
+            log(f"w44a8 group-128 activation scales M={M}: {w48g[f'M{M}']}")
+        extra["w44a8_28672x8192_group128_act_scales"] = w48g
         del imgd, rot
         torch.cuda.empty_cache()
 
