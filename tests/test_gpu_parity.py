@@ -590,6 +590,46 @@ def test_random_shapes(N, K, M, seed):
     assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
 
 
+def _random_route_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        N = 64 * int(g.integers(1, 129))
+        K = 128 * int(g.integers(1, 129))
+        M = int(g.choice([1, 4, 16, 32, 33, 48, 64, 65, 96, 97, 128, 160, 200, 256, 300, 400]))
+        fmt = str(g.choice(["block128", "block64", "w48", "w48ga"]))
+        cases.append((fmt, N, K, M, int(g.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("fmt,N,K,M,seed", _random_route_cases(32, 4242))
+def test_random_routes(fmt, N, K, M, seed):
+    """Seeded random shapes up to 8192 x 16384 and 400 tokens in both
+    formats, through whichever route the library picks (decode, 32-token
+    chunks, the prefill and tile kernels with or without their K splits,
+    stream passes, per-token or per-group activation scales), against the
+    oracle on sampled rows."""
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((N, K))).astype(np.float16)
+    rows = np.unique(np.concatenate([[0, N - 1], g.choice(N, min(N, 16), replace=False)]))
+    x = g.standard_normal((M, K)).astype(np.float16)
+    if fmt.startswith("block"):
+        bc = 64 if fmt == "block64" else 128
+        bits = (synth.random_bitmap64 if bc == 64 else synth.random_bitmap)(N, K, ALLOWED, seed % 1000)
+        img = to_dev(gbb.pack_blocks(W, bits, block_cols=bc)[0])
+        call = gbb.gemm_mixed_w_64x64 if bc == 64 else gbb.gemm_mixed_w
+        y = call(img, N, K, to_dev(x))
+        ref = bq.reference_rows(x, W, bits, rows, block_cols=bc)
+    else:
+        ga = 128 if fmt == "w48ga" else None
+        rows8 = synth.salient_rows_by_l2(W, float(g.choice([0.0, 0.1, 0.3])))
+        img = to_dev(gbb.pack_w48(W, rows8)[0])
+        xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+        y = gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, ga)
+        ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0], act_group=ga)
+    assert bq.rel_inf_err(y.cpu().numpy()[:, rows].astype(np.float64), ref) <= TOL
+
+
 @pytest.mark.parametrize("M", [33, 64, 96])
 def test_batches_as_decode_chunks(M):
     """Batches of up to three 32-token chunks on a matrix whose split
