@@ -274,6 +274,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg) {
   if (wave < 4) {
     const int rt = wave;
     const int n = br * 64 + 16 * rt + r16;
+    size_t idx[4 * MT];
+    float val[4 * MT];
+    bool act[4 * MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 s = red[0][rt][mt][lane];
@@ -282,13 +285,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int wg) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * mt + 4 * g + v;
-        const size_t idx = size_t(min(m, M - 1)) * a.N + n;
-        if (a.nseg == 1) {
-          if (m < M) a.y[idx] = (_Float16)s[v];
-        } else {
-          splitk_publish(a, idx, s[v], m < M);
-        }
+        idx[4 * mt + v] = size_t(min(m, M - 1)) * a.N + n;
+        val[4 * mt + v] = s[v];
+        act[4 * mt + v] = m < M;
       }
+    }
+    if (a.nseg == 1) {
+#pragma unroll
+      for (int k = 0; k < 4 * MT; ++k)
+        if (act[k]) a.y[idx[k]] = (_Float16)val[k];
+    } else {
+      splitk_publish_all<4 * MT>(a, idx, val, act);
     }
   }
 }
@@ -495,9 +502,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int mt = 0; mt < MT; ++mt) red[wave][r][rt][mt][lane] = acc[r][rt][mt];
   __syncthreads();
   const int rt = wave;
+  size_t idx[8 * MT];
+  float val[8 * MT];
+  bool act[8 * MT];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    if (r == 1 && !hasB) break;
     const int n = (r ? brB : brA) * 64 + 16 * rt + r16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -506,15 +515,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int w = 1; w < NW; ++w) s += red[w][r][rt][mt][lane];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = 16 * mt + 4 * g + v;
-        const size_t idx = size_t(min(m, M - 1)) * a.N + n;
-        if (a.nseg == 1) {
-          if (m < M) a.y[idx] = (_Float16)s[v];
-        } else {
-          splitk_publish(a, idx, s[v], m < M);
-        }
+        const int m = 16 * mt + 4 * g + v, k = 4 * (MT * r + mt) + v;
+        idx[k] = size_t(min(m, M - 1)) * a.N + n;
+        val[k] = s[v];
+        act[k] = m < M && (r == 0 || hasB);   // a repeated row A is not stored
       }
     }
+  }
+  if (a.nseg == 1) {
+#pragma unroll
+    for (int k = 0; k < 8 * MT; ++k)
+      if (act[k]) a.y[idx[k]] = (_Float16)val[k];
+  } else {
+    splitk_publish_all<8 * MT>(a, idx, val, act);
   }
 }
 

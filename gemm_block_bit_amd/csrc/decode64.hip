@@ -225,6 +225,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3)))
   if (wave < 4) {
     const int rt = wave;
     const int n = br * 64 + 16 * rt + r16;
+    size_t idx[4 * MT];
+    float val[4 * MT];
+    bool act[4 * MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 s = red[0][rt][mt][lane];
@@ -233,13 +236,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 3)))
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * mt + 4 * g + v;
-        const size_t idx = size_t(min(m, M - 1)) * a.N + n;
-        if (a.nseg == 1) {
-          if (m < M) a.y[idx] = (_Float16)s[v];
-        } else {
-          splitk_publish(a, idx, s[v], m < M);
-        }
+        idx[4 * mt + v] = size_t(min(m, M - 1)) * a.N + n;
+        val[4 * mt + v] = s[v];
+        act[4 * mt + v] = m < M;
       }
+    }
+    if (a.nseg == 1) {
+#pragma unroll
+      for (int k = 0; k < 4 * MT; ++k)
+        if (act[k]) a.y[idx[k]] = (_Float16)val[k];
+    } else {
+      splitk_publish_all<4 * MT>(a, idx, val, act);
     }
   }
 }

@@ -57,6 +57,57 @@ __device__ __forceinline__ void splitk_publish(const DecodeArgs& a, size_t idx, 
   __hip_atomic_store(a.acc + idx, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same hand-off for P output elements per lane.  Every element's
+// counting atomic is issued before any of their results is awaited, so the
+// wave waits for one round trip to the memory-side atomics instead of P in
+// a row (P = 16 for 32 tokens over two block rows).  Per element the
+// arithmetic, the order of the overflow add before its count, and the last
+// contribution's completion are those of splitk_publish.  Element 0 must be
+// active whenever any element of the lane is.
+template <int P>
+__device__ __forceinline__ void splitk_publish_all(const DecodeArgs& a, const size_t (&idx)[P], const float (&p)[P],
+                                                   const bool (&active)[P]) {
+  uint64_t word[P];
+  bool anybig = false;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const bool big = active[k] && !(__builtin_fabsf(p[k]) < kFixLimit);   // also NaN
+    word[k] = 1;
+    if (big) {
+      __hip_atomic_fetch_add(a.facc + idx[k], p[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      word[k] += 64;
+    } else {
+      word[k] += uint64_t(int64_t(__builtin_rintf(p[k] * kFixScale))) << 12;
+    }
+    anybig = anybig || big;
+  }
+  if (__builtin_amdgcn_ballot_w64(anybig)) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (!active[0]) return;
+  // An inactive element adds 0 to the lane's own element 0: with no branch
+  // around each atomic, nothing makes the compiler await one before issuing
+  // the next, and the extra adds meet no other lane's.
+  uint64_t tot[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const uint64_t w = active[k] ? word[k] : 0;
+    tot[k] = __hip_atomic_fetch_add(a.acc + (active[k] ? idx[k] : idx[0]), w, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) + w;
+  }
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if (!active[k] || int(tot[k] & 63) != a.nseg) continue;
+    // last contribution: the word holds the complete sum
+    float r = float(double(int64_t(tot[k]) >> 12) * (1.0 / 268435456.0));
+    if ((tot[k] >> 6) & 63) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      r += __hip_atomic_load(a.facc + idx[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.facc + idx[k], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    a.y[idx[k]] = (_Float16)r;
+    __hip_atomic_store(a.acc + idx[k], uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Default ring slots per wave (a power of two): a block takes 1 + nx + b
 // slots (nx = ceil(M / 4) activation slots of four tokens each).  The
 // launches for M <= 16 pass smaller rings (kRing8, kRing16) instead.
