@@ -522,12 +522,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  if (a.nseg == 1) {
+  // one K segment: y; else this segment's fp32 partials, which a second
+  // launch adds in segment order (2 M memory-side atomics per launch at 32
+  // tokens would cost more than that launch)
+  float* const dst = a.nseg == 1 ? nullptr : a.part + size_t(seg) * size_t(M) * size_t(a.N);
 #pragma unroll
-    for (int k = 0; k < 8 * MT; ++k)
-      if (act[k]) a.y[idx[k]] = (_Float16)val[k];
-  } else {
-    splitk_publish_all<8 * MT>(a, idx, val, act);
+  for (int k = 0; k < 8 * MT; ++k) {
+    if (!act[k]) continue;
+    if (dst)
+      dst[idx[k]] = val[k];
+    else
+      a.y[idx[k]] = (_Float16)val[k];
   }
 }
 
@@ -602,6 +607,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   a.y = y;
   a.acc = acc;
   a.facc = facc;
+  a.part = nullptr;
   a.N = N;
   a.K = K;
   a.M = M;
@@ -744,6 +750,7 @@ __device__ __forceinline__ DecodeArgs batch_args(const DecodeBatch& b, int i) {
   a.y = p.y;
   a.acc = p.acc;
   a.facc = p.facc;
+  a.part = nullptr;
   a.N = p.N;
   a.K = p.K;
   a.M = b.M;
@@ -812,7 +819,9 @@ DecodePlan decode_plan(int N, int K, int M) {
   nseg = min(nseg, kMaxSegments);
   p.seg_cols = (nbc + nseg - 1) / nseg;
   p.nseg = (nbc + p.seg_cols - 1) / p.seg_cols;
-  p.ws_bytes = p.nseg > 1 ? size_t(M) * size_t(N) * 12 : 0;
+  // split-K words and overflow floats per output (8 + 4 bytes), or for the
+  // two-row kernel fp32 partials per output and segment
+  p.ws_bytes = p.nseg == 1 ? 0 : size_t(M) * size_t(N) * (p.rows == 2 ? 4 * size_t(p.nseg) : 12);
   return p;
 }
 
@@ -827,6 +836,7 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   a.y = reinterpret_cast<_Float16*>(y);
   a.acc = plan.nseg > 1 ? static_cast<uint64_t*>(workspace) : nullptr;
   a.facc = plan.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + size_t(M) * im.N * 8) : nullptr;
+  a.part = plan.rows == 2 && plan.nseg > 1 ? static_cast<float*>(workspace) : nullptr;
   a.N = im.N;
   a.K = im.K;
   a.M = M;
@@ -848,6 +858,7 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
     hipLaunchKernelGGL((decode_kernel<4, 2>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode2_kernel<2>), grid, dim3(256), 0, s, a);
+  if (a.part) return launch_split_reduce(a.part, y, M, im.N, plan.nseg, stream);
   return int(hipGetLastError());
 }
 

@@ -430,6 +430,7 @@ int launch_decode64(const BlockImageView& im, const uint16_t* x, uint16_t* y, in
   a.y = reinterpret_cast<_Float16*>(y);
   a.acc = plan.nseg > 1 ? static_cast<uint64_t*>(workspace) : nullptr;
   a.facc = plan.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + size_t(M) * im.N * 8) : nullptr;
+  a.part = nullptr;
   a.N = im.N;
   a.K = im.K;
   a.M = M;

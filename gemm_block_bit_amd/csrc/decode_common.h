@@ -21,6 +21,7 @@ struct DecodeArgs {
   _Float16* y;
   uint64_t* acc;   // split-K fixed-point accumulators [M][N] (zero between calls)
   float* facc;     // split-K overflow accumulators [M][N] (zero between calls)
+  float* part;     // two-row kernel: K-segment partials [nseg][M][N] (zero between calls)
   int N, K, M, nbr, nbc, seg_cols, nseg;
 };
 

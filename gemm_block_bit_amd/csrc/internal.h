@@ -62,6 +62,9 @@ PrefillPlan prefill_plan(int N, int K, int M, int bc, size_t ws_bytes);
 // The least workspace a 64x128 block call of (N, K, M) runs with (the decode
 // accumulators; 0 on the prefill route, whose K split fits what it is given).
 size_t required_workspace(int N, int K, int M);
+// y[M][N] (fp16) = the sum over kseg of fp32 partials part[kseg][M][N] in
+// segment order, and the partials cleared to zero; N a multiple of 64.
+int launch_split_reduce(float* part, uint16_t* y, int M, int N, int kseg, void* stream);
 int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int M, void* workspace,
                    const PrefillPlan& plan, void* stream);
 // 64x64-block images, M <= 32: the plan (seg_cols and nbc in 64-column

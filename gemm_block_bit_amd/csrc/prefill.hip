@@ -583,11 +583,14 @@ int launch_prefill(const BlockImageView& im, const uint16_t* x, uint16_t* y, int
     hipLaunchKernelGGL(prefill64_kernel, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(prefill_kernel, grid, block, 0, s, a);
-  if (plan.kseg > 1) {
-    const size_t quads = size_t(M) * size_t(im.N) / 4;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0, s, a.part, a.y, quads,
-                       plan.kseg);
-  }
+  if (plan.kseg > 1) return launch_split_reduce(a.part, y, M, im.N, plan.kseg, stream);
+  return int(hipGetLastError());
+}
+
+int launch_split_reduce(float* part, uint16_t* y, int M, int N, int kseg, void* stream) {
+  const size_t quads = size_t(M) * size_t(N) / 4;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), part, reinterpret_cast<_Float16*>(y), quads, kseg);
   return int(hipGetLastError());
 }
 

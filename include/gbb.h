@@ -135,10 +135,13 @@ gbb_status gbb_check_image(const void* image, size_t image_bytes, int N, int K);
 
 /* Workspace bytes gbb_gemm_mixed_w needs for (N, K, M) (the fused product of
  * the ScaleBITS explainer page, section 3.2, when its K range is split over
- * workgroups); may be 0.  On the decode route it is M * N * 12 when K is
- * split across workgroups (per output element an int64 fixed-point and an
- * fp32 accumulator; for batches run as 32-token chunks, that of the largest
- * chunk), and a smaller workspace is an error.  On the prefill route it is
+ * workgroups); may be 0.  On the decode route, when K is split across
+ * workgroups, it is M * N * 12 (per output element an int64 fixed-point and
+ * an fp32 accumulator), or for 17 <= M <= 32 on matrices of at least 2^26
+ * weights (two block rows per workgroup) fp32 partials, segments * M * N * 4
+ * bytes, summed in segment order by a second launch; for batches run as
+ * 32-token chunks, that of the largest chunk; a smaller workspace is an
+ * error.  On the prefill route it is
  * the fp32 partials of the K split described under
  * gbb_gemm_mixed_w_path_workspace, and a smaller workspace only shortens the
  * split.  The workspace must be zero-filled once before its first use; every

@@ -50,12 +50,15 @@ def run_with_workspace(img, N, K, xd, M):
 
 
 # pairs of calls in a row, the second on a smaller input: split-K decode at
-# M = 1 and 8, the two-row kernel at M = 32, 32-token decode chunks (M = 64),
+# M = 1 and 8, one row per workgroup at M = 32, the two-row kernel with its
+# fp32 K-segment partials (8192 x 8192 at M = 32, 4096 x 16384 at M = 17),
+# 32-token decode chunks (M = 64),
 # the prefill kernel with no K split (2048 x 1024, M = 600) and with a K split
 # whose full size (67 MB) the array does not hold (2048 x 16384, M = 512:
 # 4 segments instead of 16), followed by decode chunks
 PAIRS = [((2048, 8192, 8), (1024, 4096, 1)),
          ((1024, 4096, 32), (256, 1024, 3)),
+         ((8192, 8192, 32), (4096, 16384, 17)),
          ((4096, 4096, 64), (1024, 2048, 33)),
          ((2048, 1024, 600), (1024, 4096, 16)),
          ((2048, 16384, 512), (512, 8192, 300))]
