@@ -522,9 +522,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  // one K segment: y; else this segment's fp32 partials, which a second
-  // launch adds in segment order (2 M memory-side atomics per launch at 32
-  // tokens would cost more than that launch)
+  // One K segment: y.  Else this segment's fp32 partials, which a second
+  // launch adds in segment order: at 32 tokens the split-K words would take
+  // a memory-side atomic per output and segment (about 2 M per launch), and
+  // those cost more than the second launch.
   float* const dst = a.nseg == 1 ? nullptr : a.part + size_t(seg) * size_t(M) * size_t(a.N);
 #pragma unroll
   for (int k = 0; k < 8 * MT; ++k) {
@@ -834,9 +835,12 @@ int launch_decode(const BlockImageView& im, const uint16_t* x, uint16_t* y, int 
   a.codes = im.codes;
   a.x = reinterpret_cast<const _Float16*>(x);
   a.y = reinterpret_cast<_Float16*>(y);
-  a.acc = plan.nseg > 1 ? static_cast<uint64_t*>(workspace) : nullptr;
-  a.facc = plan.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + size_t(M) * im.N * 8) : nullptr;
-  a.part = plan.rows == 2 && plan.nseg > 1 ? static_cast<float*>(workspace) : nullptr;
+  // a K split hands off through the split-K words (one block row per
+  // workgroup) or through fp32 partials and a second launch (two rows)
+  const bool words = plan.nseg > 1 && plan.rows == 1, partials = plan.nseg > 1 && plan.rows == 2;
+  a.acc = words ? static_cast<uint64_t*>(workspace) : nullptr;
+  a.facc = words ? reinterpret_cast<float*>(static_cast<char*>(workspace) + size_t(M) * im.N * 8) : nullptr;
+  a.part = partials ? static_cast<float*>(workspace) : nullptr;
   a.N = im.N;
   a.K = im.K;
   a.M = M;
