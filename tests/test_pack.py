@@ -357,6 +357,34 @@ def test_workspace_follows_the_batch_route(N, K):
             assert lib.gbb_gemm_mixed_w_64x64_path_workspace(N, K, M, 2) == _prefill_split(N, K, M, 64, cus)[2]
 
 
+def test_two_row_decode_workspace_is_partials():
+    """17 <= M <= 32 on a matrix of at least 2^26 weights runs two block rows
+    per workgroup; its K split keeps fp32 partials per segment (segments x M
+    x N x 4 bytes) for an ordered second launch, with the documented segment
+    count: as many as fill two workgroups per CU once, at most nbc / 8 and
+    K / (32 M).  Elsewhere the decode route keeps 12 bytes per output (or
+    none).  Every such workspace fits the 16 MiB of the allocation-free
+    entry point."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    for N, K in [(8192, 8192), (8256, 8192), (4096, 16384), (10240, 8192), (8192, 28672), (57344, 8192),
+                 (1 << 17, 512), (1024, 1 << 16), (4096, 4096), (1024, 8192)]:
+        nbr, nbc = N // 64, K // 128
+        for M in (1, 8, 16, 17, 24, 32):
+            ws = gbb.gemm_mixed_w_workspace(N, K, M)
+            if M > 16 and N * K >= 1 << 26:
+                units = -(-nbr // 2)
+                nseg = 1
+                if units < 2 * cus:
+                    nseg = min(2 * cus // units, max(1, nbc // 8), max(1, K // (32 * M)), 32)
+                seg_cols = -(-nbc // nseg)
+                nseg = -(-nbc // seg_cols)
+                assert ws == (nseg * M * N * 4 if nseg > 1 else 0), (N, K, M, ws, nseg)
+            else:
+                assert ws in (0, M * N * 12), (N, K, M, ws)
+            assert ws <= 16 << 20, (N, K, M, ws)
+
+
 def test_64x64_workspace_sizes():
     """The 64x64 plans on the host (no device work): every shape with whole
     64-column blocks, down to a single block, gets a workspace of 0 or 12
