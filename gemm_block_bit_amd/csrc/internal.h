@@ -93,6 +93,7 @@ int launch_quant_act(const uint16_t* x, int M, int K, int ga, int8_t* xq, uint16
 struct W48Split {
   int kseg8, seg8, kseg4, seg4;
   size_t ws_bytes;
+  int tiles;   // the stream kernel's packed tiles per wave (1 or 2)
 };
 W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes);
 // The tile kernel's K split (M > 64), the same layout of partials.

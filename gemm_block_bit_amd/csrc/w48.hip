@@ -122,6 +122,7 @@ struct W48Args {
   float* part;
   int N, K, M, T8, T4, ga;
   int kseg8, seg8, kseg4, seg4;
+  int tiles;   // the stream kernel's packed tiles per wave (1 or 2)
 };
 
 constexpr int kNT = 2;  // 16-row weight tiles per wave
@@ -550,28 +551,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ?
 // ---------------------------------------------------------------------------
 // Small batches (M <= 64, per-token activation scales): the weights dominate,
 // so the kernel streams them.  A workgroup owns four packed tiles (64 rows,
-// homogeneous 8-bit or 4-bit) and walks K one 128-column group at a time
-// through a 5-stage (M > 32: 4-stage) LDS pipeline: per group each wave issues the same number
-// of global->LDS loads (its share of the activation fragments, its tile's
-// weight fragments, scales and zero points), so every wait is a fixed vmcnt.
-// One barrier per group publishes the shared activation fragments.
+// homogeneous 8-bit or 4-bit), or eight (two per wave) where K is split, and
+// walks K one 128-column group at a time through an LDS pipeline: per group
+// each wave issues the same number of global->LDS loads (its share of the
+// activation fragments, its tiles' weight fragments, scales and zero
+// points), so every wait is a fixed vmcnt.  One barrier per group publishes
+// the shared activation fragments.
 // ---------------------------------------------------------------------------
-template <int TM, bool GA>   // token tiles: M <= 16 TM; GA: per-group activation scales
+// TM token tiles (M <= 16 TM); GA: per-group activation scales; TW packed
+// tiles per wave, so that a workgroup's one copy of a group's activation
+// fragments serves 64 TW weight rows.
+template <int TM, bool GA, int TW>
 struct StreamCfg {
   // Stages - 1 groups per workgroup are in flight, two workgroups per CU:
-  // five stages still fit two workgroups in the LDS for M <= 32, four for
-  // M <= 64.  (Deeper pipelines for the 4-bit rows, whose stages are
-  // smaller, measured the same: the loads themselves bound the kernel.)
-  static constexpr int kStages = TM <= 2 ? 5 : 4;
+  // with one tile per wave, five stages for M <= 32 and four for M <= 64
+  // (deeper pipelines for the 4-bit rows, whose stages are smaller, measured
+  // the same); with two, whose stages are twice as large, three and two.
+  static constexpr int kStages = TW == 1 ? (TM > 2 ? 4 : 5) : (TM > 2 ? 2 : 3);
   static constexpr int NA = (2 * TM + 3) / 4;           // activation loads per wave per group
   static constexpr int kA = 4 * NA * 1024;              // activation fragments per stage
-  static constexpr int kB = 4 * 2048;                   // weight fragments, 2 KiB per wave
-  static constexpr int kS = 4 * 256;                    // scales, 256 B per wave
-  static constexpr int kZ = 4 * 256;                    // zero points, 256 B per wave
+  static constexpr int kB = 4 * TW * 2048;              // weight fragments, 2 KiB per tile
+  static constexpr int kS = 4 * TW * 256;               // scales, 256 B per tile
+  static constexpr int kZ = 4 * TW * 256;               // zero points, 256 B per tile
   static constexpr int kX = GA ? 4 * 256 : 0;           // GA: the group pair's activation scales, per wave
   static constexpr int kStage = kA + kB + kS + kZ + kX;
-  static constexpr int kLoads8 = NA + 3 + (GA ? 1 : 0);   // loads per wave per group, 8-bit rows
-  static constexpr int kLoads4 = NA + 3 + (GA ? 1 : 0);   // 4-bit rows
+  static constexpr int kLoads8 = NA + 3 * TW + (GA ? 1 : 0);   // loads per wave per group, 8-bit rows
+  static constexpr int kLoads4 = NA + 3 * TW + (GA ? 1 : 0);   // 4-bit rows
+  static_assert(2 * kStages * kStage <= 160 * 1024, "two workgroups per CU");
+  static_assert(3 * kLoads8 < 64, "vmcnt range");
 };
 
 // One workgroup's four tiles, all 8-bit (Q4 false) or all 4-bit rows.  ACC:
@@ -579,17 +586,19 @@ struct StreamCfg {
 // GA: activation scales per (token, group), [M][G] with G even: each group
 // brings the scales of its pair of groups for every token (4 bytes a token,
 // so the loads stay dword-aligned), and they multiply the weight scale.
-template <int TM, bool GA, bool Q4, bool ACC>
+template <int TM, bool GA, bool Q4, bool ACC, int TW>
 __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, int t0, int tend, int seg,
                                              int seg_groups) {
   constexpr bool SA = GA && !ACC;   // the activation scales are loaded (ACC stores unscaled sums)
-  using C = StreamCfg<TM, SA>;
+  using C = StreamCfg<TM, SA, TW>;
   constexpr int kStages = C::kStages;
   constexpr int kLoads = Q4 ? C::kLoads4 : C::kLoads8;
   const uint32_t lbase = lds_u32(base);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int t = min(t0 + wave, tend - 1);   // this wave's tile (clamped; results discarded)
+  int t[TW];   // this wave's tiles, t0 + wave + 4 k (clamped; results discarded)
+#pragma unroll
+  for (int k = 0; k < TW; ++k) t[k] = min(t0 + wave + 4 * k, tend - 1);
   const int G = a.K / 128, KT = a.K / 64;
   // this workgroup's K segment: groups g0 ... g0 + ng - 1
   const int g0 = seg * seg_groups, ng = min(G - g0, seg_groups);
@@ -604,40 +613,54 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
       const int m = min(16 * i + r16, a.M - 1);
       gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g, st + f * 1024);
     }
-    const uint32_t sb = st + C::kA + wave * 2048;
-    if constexpr (!Q4) {
-      gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp) * 1024 + 16 * lane, sb);
-      gdma16_once(a.c8 + (size_t(t) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
-    } else {
-      // the group's two 512-byte fragments are contiguous: one 1 KiB load
-      gdma16_once(a.c4 + (size_t(t - a.T8) * KT + 2 * grp) * 512 + 16 * lane, sb);
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+      const int slot = TW * wave + k;   // this tile's weight, scale and zero slots in the stage
+      const uint32_t sb = st + C::kA + slot * 2048;
+      if constexpr (!Q4) {
+        gdma16_once(a.c8 + (size_t(t[k]) * KT + 2 * grp) * 1024 + 16 * lane, sb);
+        gdma16_once(a.c8 + (size_t(t[k]) * KT + 2 * grp + 1) * 1024 + 16 * lane, sb + 1024);
+      } else {
+        // the group's two 512-byte fragments are contiguous: one 1 KiB load
+        gdma16_once(a.c4 + (size_t(t[k] - a.T8) * KT + 2 * grp) * 512 + 16 * lane, sb);
+      }
+      gdma4_once(a.s + (size_t(t[k]) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + slot * 256);
+      if constexpr (Q4)
+        gdma4_once(a.z + (size_t(t[k] - a.T8) * G + grp) * 16 + 4 * (lane & 3),
+                   st + C::kA + C::kB + C::kS + slot * 256);
     }
-    gdma4_once(a.s + (size_t(t) * G + grp) * 16 + 2 * (lane & 7), st + C::kA + C::kB + wave * 256);
-    if constexpr (Q4)
-      gdma4_once(a.z + (size_t(t - a.T8) * G + grp) * 16 + 4 * (lane & 3), st + C::kA + C::kB + C::kS + wave * 256);
     if constexpr (SA)   // lane m: the scales of groups (grp & ~1) and (grp | 1) of token m
       gdma4(a.xs + size_t(min(lane, a.M - 1)) * G + (grp & ~1), st + C::kA + C::kB + C::kS + C::kZ + wave * 256);
   };
 
-  f32x4 tot[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) tot[i] = f32x4{0, 0, 0, 0};
-  // the previous group's int32 sums and weight scale: they are scaled into
+  f32x4 tot[TW][TM];
+  // the previous group's int32 sums and weight scales: they are scaled into
   // tot while the current group's MFMAs run, so no step waits for its own
   // matrix-core results
-  i32x4 cp[TM];
+  i32x4 cp[TW][TM];
+  float swp[TW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) cp[i] = i32x4{0, 0, 0, 0};
-  float swp = 0.0f;
+  for (int k = 0; k < TW; ++k) {
+    swp[k] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      tot[k][i] = f32x4{0, 0, 0, 0};
+      cp[k][i] = i32x4{0, 0, 0, 0};
+    }
+  }
   f32x4 sap[TM];   // GA: the previous group's activation scales of this lane's outputs
 #pragma unroll
   for (int i = 0; i < TM; ++i) sap[i] = f32x4{0, 0, 0, 0};
 
   // ACC: this lane's original row (-1: none), loaded and awaited before the
   // first global->LDS load, so no later wait of the compiler's covers them
-  int n_acc = -1;
+  int n_acc[TW];
+#pragma unroll
+  for (int k = 0; k < TW; ++k) n_acc[k] = -1;
   if constexpr (ACC) {
-    if (t0 + wave < tend) n_acc = a.rows[16 * (t0 + wave) + r16];
+#pragma unroll
+    for (int k = 0; k < TW; ++k)
+      if (t0 + wave + 4 * k < tend) n_acc[k] = a.rows[16 * (t0 + wave + 4 * k) + r16];
     wait_vm<0>();
   }
   for (int p = 0; p < kStages - 1 && p < ng; ++p) issue(p);
@@ -659,13 +682,15 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     if (j + kStages - 1 < ng) issue(j + kStages - 1);   // into step j - 1's stage
     // every LDS read of the step first, then one wait
     const uint8_t* st = base + stage(j);
-    const uint8_t* B = st + C::kA + wave * 2048;
     i32x4 av[TM][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h) av[i][h] = *reinterpret_cast<const i32x4*>(st + (2 * i + h) * 1024 + 16 * lane);
-    const float sw = (float)reinterpret_cast<const _Float16*>(st + C::kA + C::kB + wave * 256)[r16];
+    float sw[TW];
+#pragma unroll
+    for (int k = 0; k < TW; ++k)
+      sw[k] = (float)reinterpret_cast<const _Float16*>(st + C::kA + C::kB + (TW * wave + k) * 256)[r16];
     f32x4 sac[TM];   // GA: this group's activation scales of the lane's outputs (token 16 i + 4 g + v)
     if constexpr (SA) {
       const _Float16* X = reinterpret_cast<const _Float16*>(st + C::kA + C::kB + C::kS + C::kZ + wave * 256);
@@ -674,46 +699,59 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
 #pragma unroll
         for (int v = 0; v < 4; ++v) sac[i][v] = (float)X[2 * (16 * i + 4 * g + v) + (grp & 1)];
     }
-    i32x4 bv[2];
-    if constexpr (!Q4) {
-      bv[0] = *reinterpret_cast<const i32x4*>(B + 16 * lane);
-      bv[1] = *reinterpret_cast<const i32x4*>(B + 1024 + 16 * lane);
-    } else {
-      const uint2 w0 = *reinterpret_cast<const uint2*>(B + 8 * lane);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(B + 512 + 8 * lane);
-      const uint32_t z = st[C::kA + C::kB + C::kS + wave * 256 + r16];
-      const uint32_t zb = (128u - z) * 0x01010101u;
-      bv[0] = expand4(w0, zb);
-      bv[1] = expand4(w1, zb);
-    }
-    i32x4 c[TM];
+    i32x4 bv[TW][2];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      c[i] = mfma16_i8(av[i][0], bv[0], i32x4{0, 0, 0, 0});
-      c[i] = mfma16_i8(av[i][1], bv[1], c[i]);
+    for (int k = 0; k < TW; ++k) {
+      const uint8_t* B = st + C::kA + (TW * wave + k) * 2048;
+      if constexpr (!Q4) {
+        bv[k][0] = *reinterpret_cast<const i32x4*>(B + 16 * lane);
+        bv[k][1] = *reinterpret_cast<const i32x4*>(B + 1024 + 16 * lane);
+      } else {
+        const uint2 w0 = *reinterpret_cast<const uint2*>(B + 8 * lane);
+        const uint2 w1 = *reinterpret_cast<const uint2*>(B + 512 + 8 * lane);
+        const uint32_t z = st[C::kA + C::kB + C::kS + (TW * wave + k) * 256 + r16];
+        const uint32_t zb = (128u - z) * 0x01010101u;
+        bv[k][0] = expand4(w0, zb);
+        bv[k][1] = expand4(w1, zb);
+      }
     }
+    i32x4 c[TW][TM];
+#pragma unroll
+    for (int k = 0; k < TW; ++k)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        c[k][i] = mfma16_i8(av[i][0], bv[k][0], i32x4{0, 0, 0, 0});
+        c[k][i] = mfma16_i8(av[i][1], bv[k][1], c[k][i]);
+      }
     if constexpr (ACC) {
       // the group sums as they are, at their original rows (stores add to the
       // vector-memory count, which only makes the fixed waits above stricter)
-      if (n_acc >= 0) {
+#pragma unroll
+      for (int k = 0; k < TW; ++k) {
+        if (n_acc[k] < 0) continue;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int m = 16 * i + 4 * g + v;
-            if (m < a.M) a.acc_out[(size_t(m) * a.N + n_acc) * G + grp] = c[i][v];
+            if (m < a.M) a.acc_out[(size_t(m) * a.N + n_acc[k]) * G + grp] = c[k][i][v];
           }
       }
       continue;
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int k = 0; k < TW; ++k)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        tot[i][v] = __builtin_fmaf(float(cp[i][v]), GA ? swp * sap[i][v] : swp, tot[i][v]);
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) cp[i] = c[i];
-    swp = sw;
+        for (int v = 0; v < 4; ++v)
+          tot[k][i][v] = __builtin_fmaf(float(cp[k][i][v]), GA ? swp[k] * sap[i][v] : swp[k], tot[k][i][v]);
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) cp[k][i] = c[k][i];
+      swp[k] = sw[k];
+    }
     if constexpr (SA) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) sap[i] = sac[i];
@@ -721,50 +759,57 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
   }
   if constexpr (ACC) return;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int k = 0; k < TW; ++k)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) tot[i][v] = __builtin_fmaf(float(cp[i][v]), GA ? swp * sap[i][v] : swp, tot[i][v]);
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tot[k][i][v] = __builtin_fmaf(float(cp[k][i][v]), GA ? swp[k] * sap[i][v] : swp[k], tot[k][i][v]);
 
-  if (t0 + wave >= tend) return;
-  const int n = a.rows[16 * (t0 + wave) + r16];
-  if (n < 0) return;
-  if (a.part) {
-    // this segment's partial sums, at the packed row; w48_reduce_kernel adds
-    // the segments, applies the activation scale and scatters
-    const int P = 16 * (a.T8 + a.T4), pr = 16 * (t0 + wave) + r16;
-    float* pp = a.part + size_t(seg) * size_t(a.M) * size_t(P);
+#pragma unroll
+  for (int k = 0; k < TW; ++k) {
+    const int tk = t0 + wave + 4 * k;
+    if (tk >= tend) continue;
+    const int n = a.rows[16 * tk + r16];
+    if (n < 0) continue;
+    if (a.part) {
+      // this segment's partial sums, at the packed row; w48_reduce_kernel
+      // adds the segments, applies the activation scale and scatters
+      const int P = 16 * (a.T8 + a.T4), pr = 16 * tk + r16;
+      float* pp = a.part + size_t(seg) * size_t(a.M) * size_t(P);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 16 * i + 4 * g + v;
+          if (m < a.M) pp[size_t(m) * P + pr] = tot[k][i][v];
+        }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 16 * i + 4 * g + v;
-        if (m < a.M) pp[size_t(m) * P + pr] = tot[i][v];
+        if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(GA ? tot[k][i][v] : tot[k][i][v] * (float)a.xs[m]);
       }
-    return;
   }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 16 * i + 4 * g + v;
-      if (m < a.M) a.y[size_t(m) * a.N + n] = (_Float16)(GA ? tot[i][v] : tot[i][v] * (float)a.xs[m]);
-    }
 }
 
-template <int TM, bool GA, bool ACC>
+template <int TM, bool GA, bool ACC, int TW>
 __global__ __launch_bounds__(256) void w48_stream_kernel(W48Args a) {
-  using C = StreamCfg<TM, GA && !ACC>;
-  static_assert(2 * C::kStages * C::kStage <= 160 * 1024, "two workgroups per CU");
+  using C = StreamCfg<TM, GA && !ACC, TW>;
   __shared__ u32x4 lds[C::kStages * C::kStage / 16];
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
-  // workgroup = (K segment, row block): the 8-bit row blocks' kseg8
-  // segments first, then the 4-bit row blocks' kseg4
-  const int nb8 = (a.T8 + 3) / 4, nb4 = (a.T4 + 3) / 4, w8 = nb8 * a.kseg8, b = int(blockIdx.x);
+  // workgroup = (K segment, row block of 4 TW packed tiles): the 8-bit row
+  // blocks' kseg8 segments first, then the 4-bit row blocks' kseg4
+  constexpr int RB = 4 * TW;
+  const int nb8 = (a.T8 + RB - 1) / RB, nb4 = (a.T4 + RB - 1) / RB, w8 = nb8 * a.kseg8, b = int(blockIdx.x);
   if (b < w8) {
-    stream_tiles<TM, GA, false, ACC>(a, base, (b % nb8) * 4, a.T8, b / nb8, a.seg8);
+    stream_tiles<TM, GA, false, ACC, TW>(a, base, (b % nb8) * RB, a.T8, b / nb8, a.seg8);
   } else {
     const int c = b - w8;
-    stream_tiles<TM, GA, true, ACC>(a, base, a.T8 + (c % nb4) * 4, a.T8 + a.T4, c / nb4, a.seg4);
+    stream_tiles<TM, GA, true, ACC, TW>(a, base, a.T8 + (c % nb4) * RB, a.T8 + a.T4, c / nb4, a.seg4);
   }
 }
 
@@ -821,18 +866,29 @@ W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, 
   a.part = nullptr;
   a.kseg8 = a.kseg4 = 1;
   a.seg8 = a.seg4 = im.K / 128;
+  a.tiles = 1;
   return a;
 }
 
 template <bool GA, bool ACC>
 void launch_stream_ga(const W48Args& a, hipStream_t s) {
-  const dim3 grid(unsigned((a.T8 + 3) / 4 * a.kseg8 + (a.T4 + 3) / 4 * a.kseg4));
-  if (a.M <= 16)
-    hipLaunchKernelGGL((w48_stream_kernel<1, GA, ACC>), grid, dim3(256), 0, s, a);
-  else if (a.M <= 32)
-    hipLaunchKernelGGL((w48_stream_kernel<2, GA, ACC>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((w48_stream_kernel<4, GA, ACC>), grid, dim3(256), 0, s, a);
+  const int RB = 4 * a.tiles;   // packed tiles per workgroup
+  const dim3 grid(unsigned((a.T8 + RB - 1) / RB * a.kseg8 + (a.T4 + RB - 1) / RB * a.kseg4));
+  if (a.tiles == 2) {
+    if (a.M <= 16)
+      hipLaunchKernelGGL((w48_stream_kernel<1, GA, ACC, 2>), grid, dim3(256), 0, s, a);
+    else if (a.M <= 32)
+      hipLaunchKernelGGL((w48_stream_kernel<2, GA, ACC, 2>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((w48_stream_kernel<4, GA, ACC, 2>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.M <= 16)
+      hipLaunchKernelGGL((w48_stream_kernel<1, GA, ACC, 1>), grid, dim3(256), 0, s, a);
+    else if (a.M <= 32)
+      hipLaunchKernelGGL((w48_stream_kernel<2, GA, ACC, 1>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((w48_stream_kernel<4, GA, ACC, 1>), grid, dim3(256), 0, s, a);
+  }
   if (!ACC && a.part) {
     const int P = 16 * (a.T8 + a.T4);
     const size_t total = size_t(a.M) * size_t(P);
@@ -893,6 +949,7 @@ W48Split split_for(int k8, int k4, int K, int T8, int T4, int M, size_t ws_bytes
   p.seg4 = (G + k4 - 1) / k4;
   p.kseg4 = (G + p.seg4 - 1) / p.seg4;
   p.ws_bytes = need(max(p.kseg8, p.kseg4));
+  p.tiles = 1;
   return p;
 }
 
@@ -900,18 +957,24 @@ W48Split split_for(int k8, int k4, int K, int T8, int T4, int M, size_t ws_bytes
 
 // The stream kernel's K split for a pass of M <= 64 tokens.  An 8-bit row
 // block streams twice the bytes of a 4-bit one.  Counting it twice, when the
-// row blocks number at most 3/4 of the CUs, each row block's groups are cut
-// into segments of at least 8 groups (1024 columns), at most 16, so that the
-// workgroups, two per CU, stream about equal bytes: an 8-bit row block takes
-// twice the segments of a 4-bit one.  (With more row blocks the second
-// launch costs more than the extra workgroups gain: 14336 x 4096 at M = 64,
-// 248 units, ran 25 us split against 22 us.)  With fewer than ws_bytes for
-// the fp32 partials (segments x M x packed rows), fewer segments.
+// row blocks of one tile per wave (64 rows) number at most 3/4 of the CUs,
+// the kernel takes two tiles per wave (128-row blocks, so each workgroup's
+// activation fragments serve twice the weights), and each row block's
+// groups are cut into segments of at least 8 groups (1024 columns), at most
+// 16, so that the workgroups, two per CU, stream about equal bytes: an
+// 8-bit row block takes twice the segments of a 4-bit one.  (With more row
+// blocks the second launch costs more than the extra workgroups gain:
+// 14336 x 4096 at M = 64, 248 units, ran 25 us split against 22 us; and
+// 128-row blocks without a split leave CUs idle: 28672 x 8192 at M = 1, 30
+// against 35 us.)  With fewer than ws_bytes for the fp32 partials
+// (segments x M x packed rows), fewer segments.
 W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
-  const int nb8 = (T8 + 3) / 4, nb4 = (T4 + 3) / 4, G = K / 128, cus = device_compute_units();
+  const int G = K / 128, cus = device_compute_units();
   const int kcap = max(1, min(16, G / 8));
-  int k8 = 1, k4 = 1;
-  if (4 * (2 * nb8 + nb4) <= 3 * cus) {
+  int k8 = 1, k4 = 1, tiles = 1;
+  if (4 * (2 * ((T8 + 3) / 4) + (T4 + 3) / 4) <= 3 * cus) {
+    tiles = 2;
+    const int nb8 = (T8 + 7) / 8, nb4 = (T4 + 7) / 8;
     if (nb4) {
       k4 = max(1, min(kcap, 2 * cus / (2 * nb8 + nb4)));
       k8 = nb8 ? min(kcap, 2 * k4) : 1;
@@ -919,7 +982,10 @@ W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
       k8 = max(1, min(kcap, 2 * cus / nb8));
     }
   }
-  return split_for(k8, k4, K, T8, T4, M, ws_bytes);
+  W48Split p = split_for(k8, k4, K, T8, T4, M, ws_bytes);
+  // without a split (too little workspace), 64-row blocks fill more CUs
+  p.tiles = p.kseg8 > 1 || p.kseg4 > 1 ? tiles : 1;
+  return p;
 }
 
 // The tile kernel's K split (M > 64).  A 4-bit row block (128 rows) does
@@ -1002,6 +1068,7 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
     a.seg8 = sp.seg8;
     a.kseg4 = sp.kseg4;
     a.seg4 = sp.seg4;
+    a.tiles = sp.tiles;
     if (!acc && (sp.kseg8 > 1 || sp.kseg4 > 1)) a.part = static_cast<float*>(workspace);
     if (acc)
       launch_stream<true>(a, s);

@@ -412,10 +412,11 @@ def test_w48_split_workspace(N, K, frac):
     """Host side of the W4.4A8 K split.  The streaming kernel (M <= 64 with
     per-token scales, or per-group ones over an even group count; 64-token
     passes up to 128 tokens with per-token scales where the tile kernel has
-    at most one row block per CU) splits K when its row
-    blocks, an 8-bit one counted twice, number at most 3/4 of the CUs:
-    segments of at least 8 groups, at most 16, an 8-bit row block taking
-    twice the segments of a 4-bit one.  The tile kernel (M > 64 otherwise)
+    at most one row block per CU) splits K when its 64-row blocks, an 8-bit
+    one counted twice, number at most 3/4 of the CUs; it then streams
+    128-row blocks (two tiles per wave), cut into segments of at least 8
+    groups, at most 16, about enough for two workgroups per CU, an 8-bit
+    row block taking twice the segments of a 4-bit one.  The tile kernel (M > 64 otherwise)
     splits K when its token tiles x row blocks, a 4-bit one counted twice,
     fill at most half of its resident workgroups (three per CU, two with
     group scales), a 4-bit row block taking twice the segments of an 8-bit
@@ -434,11 +435,12 @@ def test_w48_split_workspace(N, K, frac):
     P = 16 * (T8 + T4)
     k8 = k4 = 1
     if 4 * (2 * nb8 + nb4) <= 3 * cus:
-        if nb4:
-            k4 = max(1, min(kcap, 2 * cus // (2 * nb8 + nb4)))
-            k8 = min(kcap, 2 * k4) if nb8 else 1
+        b8, b4 = -(-T8 // 8), -(-T4 // 8)   # split: 128-row blocks (two tiles per wave)
+        if b4:
+            k4 = max(1, min(kcap, 2 * cus // (2 * b8 + b4)))
+            k8 = min(kcap, 2 * k4) if b8 else 1
         else:
-            k8 = max(1, min(kcap, 2 * cus // nb8))
+            k8 = max(1, min(kcap, 2 * cus // b8))
     stream_kmax = max(kseg(k8), kseg(k4))
 
     def tile_kmax(M, ga):
