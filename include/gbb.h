@@ -357,11 +357,12 @@ size_t gbb_gemm_w48a8_workspace(int N, int K, int n8, int M, int ga);
  * output rows per compute unit (MixLLM page, section 3.3: the same
  * two-step product over a K range cut into segments).  The streaming kernel
  * (M <= 64 per pass; per-token activation scales, or per-group ones over an
- * even number of groups with xs 4-byte aligned) splits K where its row
+ * even number of groups with xs 4-byte aligned) splits K where its 64-row
  * blocks, an 8-bit one counted twice, number at most 3/4 of the compute
- * units; each row block's 128-column groups are cut into up to 16
- * segments of at least 8 groups, an 8-bit row block into twice as many as a
- * 4-bit one, so that every workgroup streams about the same bytes.  The tile
+ * units; it then streams 128-row blocks, and each one's 128-column groups
+ * are cut into up to 16 segments of at least 8 groups, an 8-bit row block
+ * into twice as many as a 4-bit one, so that every workgroup streams about
+ * the same bytes.  The tile
  * kernel (larger M) splits K where its token tiles x row blocks fill at most
  * half of its resident workgroups, a 4-bit row block (twice the rows)
  * counted twice and cut into twice the segments.  Each segment writes its
