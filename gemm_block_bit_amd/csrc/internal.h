@@ -94,6 +94,7 @@ struct W48Split {
   int kseg8, seg8, kseg4, seg4;
   size_t ws_bytes;
   int tiles;   // the stream kernel's packed tiles per wave (1 or 2)
+  int tt;      // the tile kernel's 16-token tiles per workgroup (8 or 4)
 };
 W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes);
 // The tile kernel's K split (M > 64), the same layout of partials.

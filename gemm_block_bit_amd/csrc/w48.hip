@@ -123,6 +123,7 @@ struct W48Args {
   int N, K, M, T8, T4, ga;
   int kseg8, seg8, kseg4, seg4;
   int tiles;   // the stream kernel's packed tiles per wave (1 or 2)
+  int tt;      // the tile kernel's 16-token tiles per workgroup (8 or 4)
 };
 
 constexpr int kNT = 2;  // 16-row weight tiles per wave
@@ -258,46 +259,57 @@ __global__ __launch_bounds__(256) void w48_kernel(W48Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large batches: tiles of 128 tokens x 128 packed 4-bit rows or 128 tokens x
-// 64 packed 8-bit rows per workgroup, one row set per workgroup.  Wave w
-// owns NJ packed row tiles (two 4-bit tiles or one 8-bit tile) for all eight
-// 16-token tiles, so each weight fragment is read and, for 4-bit rows,
-// expanded to int8 (q - z) by one wave only, and its expansion serves eight
+// Large batches: tiles of 128 (or 64) tokens x 128 packed 4-bit rows or x 64
+// packed 8-bit rows per workgroup, one row set per workgroup.  Wave w owns NJ
+// packed row tiles (two 4-bit tiles or one 8-bit tile) for all TT 16-token
+// tiles (TT = 8 or 4), so each weight fragment is read and, for 4-bit rows,
+// expanded to int8 (q - z) by one wave only, and its expansion serves TT
 // MFMAs.  Per 128-column group everything the matrix cores read reaches LDS
 // by global->LDS loads in MFMA fragment order: the activation fragments (16
 // tokens x 64 columns each, shared by the four waves), each wave's own weight
 // fragments, scales and zero points, so no staging registers are needed and
 // every operand read is a lane-linear LDS read.  Groups flow through two LDS
 // stages: the next group's loads fly while the current group runs; one fixed
-// vmcnt wait and one barrier per group.  Either tile takes 52 KiB, so three
-// workgroups share a CU.  Each token tile's int32 sums are scaled into fp32
+// vmcnt wait and one barrier per group.  A 128-token tile takes 52 KiB, so
+// three workgroups share a CU; a 64-token tile 36 KiB, so four do.  Each token tile's int32 sums are scaled into fp32
 // while the next tile's MFMAs run.  Workgroups are dealt to the XCDs in
 // contiguous stretches of a grouped tile order, so the tiles in flight on an
 // XCD share their activation and weight tiles in its L2.
 // ---------------------------------------------------------------------------
-constexpr int kTB = 128;   // tokens per workgroup
+constexpr int kTB = 128;   // tokens per workgroup of the larger tile
 
-template <bool Q4>
+// TT 16-token tiles per workgroup (8 or 4)
+template <bool Q4, int TT>
 struct TileCfg {
   static constexpr int NJ = Q4 ? 2 : 1;             // packed row tiles per wave
   static constexpr int kRows = 64 * NJ;             // packed rows per workgroup
   static constexpr int kStages = 2;
-  static constexpr int kA = 16 * 1024;              // activation fragments (8 token tiles x 2 k halves)
+  static constexpr int kA = TT * 2 * 1024;          // activation fragments (TT token tiles x 2 k halves)
   static constexpr int kBw = 2048;                  // weight fragments of one wave (NJ tiles x 2 halves)
   static constexpr int kB = 4 * kBw;
   static constexpr int kS = 4 * 256;                // weight scales, 256 B per wave
   static constexpr int kZ = Q4 ? 4 * 256 : 0;       // zero points, 256 B per wave
   static constexpr int kStage = kA + kB + kS + kZ;
-  // global->LDS loads per wave per group: 4 activation, 2 weight, scales, zero points
-  static constexpr int kLoads = 4 + 2 + 1 + (Q4 ? 1 : 0);
 };
-constexpr int kTileLds = TileCfg<true>::kStages * TileCfg<true>::kStage;
-static_assert(TileCfg<false>::kStages * TileCfg<false>::kStage <= kTileLds, "one LDS size serves both");
-static_assert(3 * kTileLds <= 160 * 1024, "three workgroups per CU");
-// Per-group activation scales staged in LDS: two buffers of 128 tokens x the
-// scales of a group pair (4 bytes), after the stages.
-constexpr int kTileXs = 2 * kTB * 4;
-static_assert(2 * (kTileLds + kTileXs) <= 160 * 1024, "two workgroups per CU with staged scales");
+// LDS bytes of the stages (one size serves both row sets), and of the
+// per-group activation scales staged after them: two buffers of 16 TT tokens
+// x the scales of a group pair (4 bytes).
+template <int TT>
+constexpr int tile_lds() {
+  return TileCfg<true, TT>::kStages * TileCfg<true, TT>::kStage;
+}
+template <int TT>
+constexpr int tile_xs() {
+  return 2 * 16 * TT * 4;
+}
+static_assert(TileCfg<false, 8>::kStages * TileCfg<false, 8>::kStage <= tile_lds<8>(), "one LDS size serves both");
+static_assert(3 * tile_lds<8>() <= 160 * 1024, "three 128-token workgroups per CU");
+static_assert(2 * (tile_lds<8>() + tile_xs<8>()) <= 160 * 1024, "two with staged scales");
+static_assert(4 * tile_lds<4>() <= 160 * 1024, "four 64-token workgroups per CU");
+static_assert(3 * (tile_lds<4>() + tile_xs<4>()) <= 160 * 1024, "three with staged scales");
+// resident workgroups per CU of the tile kernel (at 128 tokens, per-group
+// activation scales need more registers)
+__host__ __device__ constexpr int tile_wgs_per_cu(int TT, bool ga) { return TT == 8 ? (ga ? 2 : 3) : 4; }
 
 // global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
 // LDS address lds + 16 l (4 l).  No output registers: completion is waited
@@ -330,7 +342,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
 
-// One workgroup's tile: tokens m0 ... m0 + 127, packed tiles t0 ... t0 +
+// One workgroup's tile: tokens m0 ... m0 + 16 TT - 1, packed tiles t0 ... t0 +
 // 4 NJ - 1 of one row set.  Q4: the row set (4-bit or 8-bit rows).  GA:
 // activation scales per (token, group), else per token.  ACC: store the exact
 // int32 group sums to a.acc_out instead of scaling them (the integer step of
@@ -338,9 +350,10 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // XS (with GA): the activation scales reach LDS with the group's loads (an
 // even group count and a 4-byte aligned scale array), else each output
 // reads its scale from memory.
-template <bool Q4, bool GA, bool ACC, bool XS>
+template <int TT, bool Q4, bool GA, bool ACC, bool XS>
 __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m0, int t0, int seg) {
-  using C = TileCfg<Q4>;
+  using C = TileCfg<Q4, TT>;
+  constexpr int kLds = tile_lds<TT>();
   constexpr int S = C::kStages, NJ = C::NJ;
   const uint32_t lbase = lds_u32(base);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -357,7 +370,7 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
   auto issue = [&](int grp) {
     const uint32_t sb = lbase + uint32_t((grp % S) * C::kStage);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {   // activation fragment f: token tile f / 2, k half f % 2
+    for (int q = 0; q < TT / 2; ++q) {   // activation fragment f: token tile f / 2, k half f % 2
       const int f = wave + 4 * q, i = f >> 1, h = f & 1;
       const int m = min(m0 + 16 * i + r16, a.M - 1);
       gdma16(a.xq + size_t(m) * a.K + size_t(grp) * 128 + 64 * h + 16 * g, sb + f * 1024);
@@ -378,10 +391,10 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
       const int tt = min(tw + ((lane >> 3) & (NJ - 1)), tend - 1);
       gdma4(a.s + (size_t(tt) * G + grp) * 16 + 2 * (lane & 7), sb + C::kA + C::kB + wave * 256);
     }
-    if constexpr (GA && XS && !ACC) {   // waves 0 and 1: tokens 64 w + lane, the group pair's scales
-      if (wave < 2)
+    if constexpr (GA && XS && !ACC) {   // waves 0 ... TT / 4 - 1: tokens 64 w + lane, the group pair's scales
+      if (wave < TT / 4)
         gdma4(a.xs + size_t(min(m0 + 64 * wave + lane, a.M - 1)) * G + (grp & ~1),
-              lbase + uint32_t(kTileLds + (grp & 1) * (kTB * 4) + wave * 256));
+              lbase + uint32_t(kLds + (grp & 1) * (16 * TT * 4) + wave * 256));
     }
     if constexpr (Q4) {   // zero points: lanes 4 j + 0..3 bring tile j's 16
       const int tt = min(tw + ((lane >> 2) & 1), tend - 1);
@@ -389,9 +402,9 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
     }
   };
 
-  f32x4 tot[8][NJ];
+  f32x4 tot[TT][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
 
@@ -437,7 +450,7 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
         // XS: the scales of tokens 16 i + 4 g ... + 3 in one 16-byte LDS read
         u32x4 xp = u32x4{0, 0, 0, 0};
         if constexpr (XS)
-          xp = *reinterpret_cast<const u32x4*>(base + kTileLds + (grp & 1) * (kTB * 4) + 4 * (16 * i + 4 * g));
+          xp = *reinterpret_cast<const u32x4*>(base + kLds + (grp & 1) * (16 * TT * 4) + 4 * (16 * i + 4 * g));
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float sa = XS ? ((grp & 1) ? hi_half(xp[v]) : lo_half(xp[v]))
@@ -456,27 +469,27 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
     // every LDS read of the group first; then the first k half's MFMAs, and
     // the second half token tile by token tile, each tile's sums scaled while
     // the next tile's MFMAs run
-    i32x4 av0[8], av1[8], b0[NJ], b1[NJ];
+    i32x4 av0[TT], av1[TT], b0[NJ], b1[NJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) av0[i] = afrag(i, 0);
+    for (int i = 0; i < TT; ++i) av0[i] = afrag(i, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b0[j] = bfrag(0, j);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) av1[i] = afrag(i, 1);
-    i32x4 c[8][NJ];
+    for (int i = 0; i < TT; ++i) av1[i] = afrag(i, 1);
+    i32x4 c[TT][NJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TT; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av0[i], b0[j], i32x4{0, 0, 0, 0});
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b1[j] = bfrag(1, j);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TT; ++i) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av1[i], b1[j], c[i][j]);
       if (i > 0) finish(i - 1, c[i - 1]);
     }
-    finish(7, c[7]);
+    finish(TT - 1, c[TT - 1]);
   }
   if constexpr (ACC) return;
 
@@ -490,7 +503,7 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
       const int tt = tw + j;
       if (tt >= tend || a.rows[16 * tt + r16] < 0) continue;   // padding rows: no partials
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < TT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = m0 + 16 * i + 4 * g + v;
@@ -507,7 +520,7 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
     const int n = a.rows[16 * tt + r16];
     if (n < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TT; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + 16 * i + 4 * g + v;
@@ -524,11 +537,12 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 // share both their activation and their weight tiles in its L2.
 constexpr int kGroupRows = 8;
 
-// per_xcd tiles of that order per XCD.
-template <bool GA, bool ACC, bool XS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ? 2 : 3))) void w48_tile_kernel(
-    W48Args a, int ntm, int nrb8, int nrb4, int per_xcd) {
-  __shared__ u32x4 lds[(kTileLds + (GA && XS ? kTileXs : 0)) / 16];
+// per_xcd tiles of that order per XCD; token tiles of 16 TT tokens.
+template <int TT, bool GA, bool ACC, bool XS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 8 ? (GA || ACC ? 2 : 3)
+                                                                                : (GA && !XS ? 3 : 4)))) void
+w48_tile_kernel(W48Args a, int ntm, int nrb8, int nrb4, int per_xcd) {
+  __shared__ u32x4 lds[(tile_lds<TT>() + (GA && XS ? tile_xs<TT>() : 0)) / 16];
   // workgroup i runs on XCD i % 8, which owns tiles [x per_xcd, (x + 1) per_xcd)
   // with a K split, each row block stands for kseg8 (kseg4) consecutive
   // (row block, K segment) units of the order
@@ -541,10 +555,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GA || ACC ?
   const int tm = r / gr, ru = q * kGroupRows + (r - tm * gr);
   uint8_t* const base = reinterpret_cast<uint8_t*>(lds);
   if (ru < nu8) {
-    tile_body<false, GA, ACC, XS>(a, base, tm * kTB, (ru / a.kseg8) * 4, ru % a.kseg8);
+    tile_body<TT, false, GA, ACC, XS>(a, base, tm * 16 * TT, (ru / a.kseg8) * 4, ru % a.kseg8);
   } else {
     const int r4 = ru - nu8;
-    tile_body<true, GA, ACC, XS>(a, base, tm * kTB, a.T8 + (r4 / a.kseg4) * 8, r4 % a.kseg4);
+    tile_body<TT, true, GA, ACC, XS>(a, base, tm * 16 * TT, a.T8 + (r4 / a.kseg4) * 8, r4 % a.kseg4);
   }
 }
 
@@ -867,6 +881,7 @@ W48Args make_args(const W48ImageView& im, const int8_t* xq, const uint16_t* xs, 
   a.kseg8 = a.kseg4 = 1;
   a.seg8 = a.seg4 = im.K / 128;
   a.tiles = 1;
+  a.tt = 8;
   return a;
 }
 
@@ -905,19 +920,27 @@ void launch_stream(const W48Args& a, hipStream_t s) {
     launch_stream_ga<false, ACC>(a, s);
 }
 
-template <bool ACC>
-void launch_tile(const W48Args& a, hipStream_t s) {
-  const int ntm = (a.M + kTB - 1) / kTB, nrb8 = (a.T8 + 3) / 4, nrb4 = (a.T4 + 7) / 8;
+template <int TT, bool ACC>
+void launch_tile_tt(const W48Args& a, hipStream_t s) {
+  const int ntm = (a.M + 16 * TT - 1) / (16 * TT), nrb8 = (a.T8 + 3) / 4, nrb4 = (a.T4 + 7) / 8;
   const int per_xcd = (ntm * (nrb8 * a.kseg8 + nrb4 * a.kseg4) + 7) / 8;
   const dim3 grid(unsigned(8 * per_xcd));
   // per-group scales staged in LDS when they can be loaded two groups at a time
   const bool xs_lds = (a.K / 128) % 2 == 0 && reinterpret_cast<uintptr_t>(a.xs) % 4 == 0;
   if (a.ga == 128 && xs_lds)
-    hipLaunchKernelGGL((w48_tile_kernel<true, ACC, true>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+    hipLaunchKernelGGL((w48_tile_kernel<TT, true, ACC, true>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   else if (a.ga == 128)
-    hipLaunchKernelGGL((w48_tile_kernel<true, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+    hipLaunchKernelGGL((w48_tile_kernel<TT, true, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
   else
-    hipLaunchKernelGGL((w48_tile_kernel<false, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+    hipLaunchKernelGGL((w48_tile_kernel<TT, false, ACC, false>), grid, dim3(256), 0, s, a, ntm, nrb8, nrb4, per_xcd);
+}
+
+template <bool ACC>
+void launch_tile(const W48Args& a, hipStream_t s) {
+  if (a.tt == 4)
+    launch_tile_tt<4, ACC>(a, s);
+  else
+    launch_tile_tt<8, ACC>(a, s);
   if (!ACC && a.part) {
     const int P = 16 * (a.T8 + a.T4);
     const size_t total = size_t(a.M) * size_t(P);
@@ -950,6 +973,7 @@ W48Split split_for(int k8, int k4, int K, int T8, int T4, int M, size_t ws_bytes
   p.kseg4 = (G + p.seg4 - 1) / p.seg4;
   p.ws_bytes = need(max(p.kseg8, p.kseg4));
   p.tiles = 1;
+  p.tt = 8;
   return p;
 }
 
@@ -988,6 +1012,33 @@ W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
   return p;
 }
 
+// The tile kernel's token tile for an unsplit launch.  Its workgroups run
+// in rounds of the resident slots (three 128-token or four 64-token
+// workgroups per CU with per-token activation scales), and a 4-bit row
+// block's workgroup takes about twice as long as an 8-bit one's.  A round
+// only partly filled still costs a whole workgroup's time (28672 x 8192 at
+// M = 512: 808 4-bit workgroups for 768 slots).  At full occupancy a 64-token
+// workgroup takes about 6/8 of the time of a 128-token one (each 4-bit
+// expansion and weight load serves half as many MFMAs), so 64-token tiles are
+// taken when their rounds end sooner by that measure.  With per-group
+// activation scales a 128-token workgroup needs 204 registers and only two
+// are resident per CU, against four 64-token ones that take about as long
+// each: there 64-token tiles are taken unless the launch runs eight rounds or
+// more of 128-token tiles, where the two are within a few per cent.
+// Measured on 28672 x 8192 and 8192 x 28672, M = 129 ... 4096 (both tiles
+// give bit-identical outputs).
+static int tile_token_tiles(int T8, int T4, int M, int ga) {
+  const int cus = device_compute_units();
+  const long u = long((T8 + 3) / 4) + 2L * long((T4 + 7) / 8);   // row blocks in 8-bit units
+  auto rounds = [&](int tt) {
+    const long units = long((M + 16 * tt - 1) / (16 * tt)) * u;
+    const long slots2 = 2L * tile_wgs_per_cu(tt, ga == 128) * cus;
+    return (units + slots2 - 1) / slots2;
+  };
+  if (ga == 128) return rounds(8) < 8 ? 4 : 8;
+  return 6L * rounds(4) < 8L * rounds(8) ? 4 : 8;
+}
+
 // The tile kernel's K split (M > 64).  A 4-bit row block (128 rows) does
 // twice the matrix-core work of an 8-bit one (64 rows).  Counting it twice,
 // when the token tiles x row blocks fill at most half of the resident
@@ -1012,7 +1063,9 @@ W48Split w48_tile_split(int K, int T8, int T4, int M, int ga, size_t ws_bytes) {
       k4 = max(1, min(kcap, slots / (ntm * nrb4)));
     }
   }
-  return split_for(k8, k4, K, T8, T4, M, ws_bytes);
+  W48Split p = split_for(k8, k4, K, T8, T4, M, ws_bytes);
+  if (p.kseg8 == 1 && p.kseg4 == 1) p.tt = tile_token_tiles(T8, T4, M, ga);
+  return p;
 }
 
 // Whether (M, ga) runs the stream kernel, in one pass (M <= 64) or in 64-token
@@ -1080,6 +1133,7 @@ int launch(const W48Args& a0, void* workspace, size_t ws_bytes, void* stream) {
     a.seg8 = sp.seg8;
     a.kseg4 = sp.kseg4;
     a.seg4 = sp.seg4;
+    a.tt = sp.tt;
     if (!acc && (sp.kseg8 > 1 || sp.kseg4 > 1)) a.part = static_cast<float*>(workspace);
     if (acc)
       launch_tile<true>(a, s);

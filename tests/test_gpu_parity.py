@@ -884,7 +884,10 @@ def test_w48_group_acc_bit_exact(N, K, M, frac, ga):
                                            # MixLLM's 20 % and 50 % 8-bit row fractions
                                            (320, 1024, 48, None, 0.2), (192, 512, 130, 128, 0.5), (192, 512, 24, None, 0.5),
                                            # batches above 64 with no 8-bit rows / only 8-bit rows
-                                           (64, 256, 100, None, 0.0), (80, 256, 200, 128, 1.0)])
+                                           (64, 256, 100, None, 0.0), (80, 256, 200, 128, 1.0),
+                                           # 64-token tiles, ragged: per-group scales over an odd
+                                           # group count (read per output), per-token scales
+                                           (200, 384, 100, 128, 0.1), (200, 384, 300, None, 0.1)])
 def test_w48_parity(N, K, M, ga, frac):
     W = small(N, K, 3 * N + M)
     rows8 = synth.salient_rows_by_l2(W, frac)
@@ -980,6 +983,40 @@ def test_w44a8_28672x8192_group_acc_bit_exact(M):
     got = acc[:, torch.from_numpy(rows).to(acc.device)].cpu().numpy().astype(np.int64)
     del acc
     assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows))
+
+
+@functools.lru_cache(maxsize=1)
+def w48_tall_image():
+    """28672 x 1024, 10 % 8-bit rows: the 28672-row layer's row blocks with K
+    reduced (the tile kernel's token tile depends on the row blocks and M,
+    not on K)."""
+    W = small(28672, 1024, 23)
+    rows8 = synth.salient_rows_by_l2(W, 0.1)
+    img, _, _ = gbb.pack_w48(W, rows8)
+    return W, rows8, to_dev(img)
+
+
+# (M, ga) of unsplit tile-kernel launches on 256 compute units: per-token
+# scales take 64-token tiles at M = 200 (ragged) and 512 and 128-token tiles
+# at M = 768; per-group scales take 64-token tiles at M = 512 and 128-token
+# tiles at M = 2048 (eight rounds of them)
+@pytest.mark.parametrize("M,ga", [(200, None), (512, None), (768, None), (512, 128), (2048, 128)])
+def test_w48_tile_token_tiles(M, ga):
+    """Both token tiles of the tile kernel: exact int32 group sums and y
+    against the oracle, one checked row in every 16-row tile."""
+    W, rows8, img = w48_tall_image()
+    N, K = W.shape
+    x = rand_x(M, K, 31 + M)
+    xq, xs = gbb.quant_act_i8(to_dev(x), ga)
+    rows = one_row_per(packed_rows(N, rows8), 16, M)
+    sel = torch.from_numpy(rows).to(xq.device)
+    acc = gbb.w48_group_acc(img, N, K, rows8.size, xq, ga)
+    got = acc[:, sel].cpu().numpy().astype(np.int64)
+    del acc
+    assert np.array_equal(got, w48_acc_reference(x, W, rows8, rows, ga=ga))
+    y = gbb.gemm_w48a8(img, N, K, rows8.size, xq, xs, ga)[:, sel].cpu().numpy()
+    ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0], act_group=ga)
+    assert bq.rel_inf_err(y.astype(np.float64), ref) <= TOL
 
 
 def w48_split_call(img, N, K, n8, xq, xs, ws, ga=None):
