@@ -277,6 +277,10 @@ __global__ __launch_bounds__(256) void w48_kernel(W48Args a) {
 // XCD share their activation and weight tiles in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kTB = 128;   // tokens per workgroup of the larger tile
+// 1.5 2^23 and its fp32 bits: the float with bits kOffI + n is kOffF + n for
+// |n| < 2^22 (every int32 group sum: |127 * 127 * 128| < 2^21)
+constexpr int32_t kOffI = 0x4B400000;
+constexpr float kOffF = 12582912.0f;
 
 // TT 16-token tiles per workgroup (8 or 4)
 template <bool Q4, int TT>
@@ -408,6 +412,20 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 #pragma unroll
     for (int j = 0; j < NJ; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
 
+  // Offset sums (the 64-token tile with per-token scales, which has the
+  // registers): each group's MFMAs start from the bits of kOffF = 1.5 2^23
+  // instead of 0, so the int32 result read as fp32 is kOffF + sum exactly
+  // (|sum| < 2^22) and scaling it takes one fma instead of a conversion and
+  // an fma.  The offsets' total kOffF (s_a + s_b) comes off after every pair
+  // of groups (and after a segment's last group), so the running sum never
+  // holds more than two offsets: its extra rounding stays within a few s_w
+  // against sums of ~10^4 s_w.
+  constexpr bool kOff = !GA && !ACC && TT == 4;
+  const i32x4 cinit = kOff ? i32x4{kOffI, kOffI, kOffI, kOffI} : i32x4{0, 0, 0, 0};
+  float pend[NJ];   // scales whose offsets are still in tot
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pend[j] = 0.0f;
+
   issue(g0);
   for (int grp = g0; grp < gend; ++grp) {
     wait_vm<0>();      // this wave's loads of group grp have landed
@@ -458,6 +476,14 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 #pragma unroll
           for (int j = 0; j < NJ; ++j) tot[i][j][v] = __builtin_fmaf(float(ci[j][v]), sw[j] * sa, tot[i][j][v]);
         }
+      } else if constexpr (kOff) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int32_t e = ci[j][v];   // (a bit cast of the vector element itself reads element 0)
+            tot[i][j][v] = __builtin_fmaf(__builtin_bit_cast(float, e), sw[j], tot[i][j][v]);
+          }
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
@@ -480,7 +506,7 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 #pragma unroll
     for (int i = 0; i < TT; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av0[i], b0[j], i32x4{0, 0, 0, 0});
+      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av0[i], b0[j], cinit);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b1[j] = bfrag(1, j);
 #pragma unroll
@@ -490,6 +516,21 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
       if (i > 0) finish(i - 1, c[i - 1]);
     }
     finish(TT - 1, c[TT - 1]);
+    if constexpr (kOff) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pend[j] += sw[j];
+      if (((grp - g0) & 1) || grp + 1 == gend) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float off = kOffF * pend[j];
+          pend[j] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < TT; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) tot[i][j][v] -= off;
+        }
+      }
+    }
   }
   if constexpr (ACC) return;
 

@@ -389,9 +389,11 @@ gbb_status gbb_gemm_w48a8_split(const void* image, int N, int K, int n8, const i
  * original row n (device int32 [M][N][K/128]), for bit-exact tests.  The call
  * runs the kernel gbb_gemm_w48a8 runs for the same M and ga (K or 128), with
  * that kernel's scaling step replaced by a store of the group sums, so the
- * integers checked are those the product path forms; the streaming kernel
- * runs with the K segments that gbb_gemm_w48a8_split takes with a full
- * workspace.  Errors as gbb_gemm_w48a8. */
+ * integers checked are those the product path forms (where the product
+ * kernel starts a group's sums from the constant 0x4B400000 so that the
+ * result reads as a float, its integers are these plus that constant); the
+ * streaming kernel runs with the K segments that gbb_gemm_w48a8_split takes
+ * with a full workspace.  Errors as gbb_gemm_w48a8. */
 gbb_status gbb_w48_group_acc(const void* image, int N, int K, int n8, const int8_t* xq, int ga,
                              int32_t* acc, int M, void* stream);
 
