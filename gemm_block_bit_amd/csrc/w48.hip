@@ -412,15 +412,14 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
 #pragma unroll
     for (int j = 0; j < NJ; ++j) tot[i][j] = f32x4{0, 0, 0, 0};
 
-  // Offset sums (the 64-token tile with per-token scales, which has the
-  // registers): each group's MFMAs start from the bits of kOffF = 1.5 2^23
-  // instead of 0, so the int32 result read as fp32 is kOffF + sum exactly
-  // (|sum| < 2^22) and scaling it takes one fma instead of a conversion and
-  // an fma.  The offsets' total kOffF (s_a + s_b) comes off after every pair
+  // Offset sums (per-token scales): each group's MFMAs start from the bits
+  // of kOffF = 1.5 2^23 instead of 0, so the int32 result read as fp32 is
+  // kOffF + sum exactly (|sum| < 2^22) and scaling it takes one fma instead
+  // of a conversion and an fma.  The offsets' total kOffF (s_a + s_b) comes off after every pair
   // of groups (and after a segment's last group), so the running sum never
   // holds more than two offsets: its extra rounding stays within a few s_w
   // against sums of ~10^4 s_w.
-  constexpr bool kOff = !GA && !ACC && TT == 4;
+  constexpr bool kOff = !GA && !ACC;
   const i32x4 cinit = kOff ? i32x4{kOffI, kOffI, kOffI, kOffI} : i32x4{0, 0, 0, 0};
   float pend[NJ];   // scales whose offsets are still in tot
 #pragma unroll
@@ -492,30 +491,33 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
       }
     };
 
-    // every LDS read of the group first; then the first k half's MFMAs, and
-    // the second half token tile by token tile, each tile's sums scaled while
-    // the next tile's MFMAs run
-    i32x4 av0[TT], av1[TT], b0[NJ], b1[NJ];
-#pragma unroll
-    for (int i = 0; i < TT; ++i) av0[i] = afrag(i, 0);
+    // token tiles in runs of four: each run's first k half for all its
+    // tiles, then the second half tile by tile, each tile's sums scaled
+    // while the next tile's MFMAs run; only four tiles' sums are live at a
+    // time (with all eight the offset sums spilled at three waves per SIMD)
+    i32x4 b0[NJ], b1[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b0[j] = bfrag(0, j);
 #pragma unroll
-    for (int i = 0; i < TT; ++i) av1[i] = afrag(i, 1);
-    i32x4 c[TT][NJ];
-#pragma unroll
-    for (int i = 0; i < TT; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av0[i], b0[j], cinit);
-#pragma unroll
     for (int j = 0; j < NJ; ++j) b1[j] = bfrag(1, j);
 #pragma unroll
-    for (int i = 0; i < TT; ++i) {
+    for (int i0 = 0; i0 < TT; i0 += 4) {
+      i32x4 c[4][NJ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(av1[i], b1[j], c[i][j]);
-      if (i > 0) finish(i - 1, c[i - 1]);
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 a0 = afrag(i0 + i, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(a0, b0[j], cinit);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 a1 = afrag(i0 + i, 1);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) c[i][j] = mfma16_i8(a1, b1[j], c[i][j]);
+        if (i > 0) finish(i0 + i - 1, c[i - 1]);
+      }
+      finish(i0 + 3, c[3]);
     }
-    finish(TT - 1, c[TT - 1]);
     if constexpr (kOff) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pend[j] += sw[j];
