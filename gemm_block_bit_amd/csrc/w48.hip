@@ -415,10 +415,10 @@ __device__ __forceinline__ void tile_body(const W48Args& a, uint8_t* base, int m
   // Offset sums (per-token scales): each group's MFMAs start from the bits
   // of kOffF = 1.5 2^23 instead of 0, so the int32 result read as fp32 is
   // kOffF + sum exactly (|sum| < 2^22) and scaling it takes one fma instead
-  // of a conversion and an fma.  The offsets' total kOffF (s_a + s_b) comes off after every pair
-  // of groups (and after a segment's last group), so the running sum never
-  // holds more than two offsets: its extra rounding stays within a few s_w
-  // against sums of ~10^4 s_w.
+  // of a conversion and an fma.  The offsets' total kOffF (s_a + s_b) comes
+  // off after every pair of groups (and after a segment's last group), so
+  // the running sum never holds more than two offsets: its extra rounding
+  // stays within a few s_w against sums of ~10^4 s_w.
   constexpr bool kOff = !GA && !ACC;
   const i32x4 cinit = kOff ? i32x4{kOffI, kOffI, kOffI, kOffI} : i32x4{0, 0, 0, 0};
   float pend[NJ];   // scales whose offsets are still in tot
@@ -708,6 +708,48 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
   f32x4 sap[TM];   // GA: the previous group's activation scales of this lane's outputs
 #pragma unroll
   for (int i = 0; i < TM; ++i) sap[i] = f32x4{0, 0, 0, 0};
+  // Offset sums with per-token scales and four token tiles, as in the tile
+  // kernel: a group's MFMAs start from the bits of 1.5 2^23, one fma scales
+  // each sum, and the offsets come off after every second scaled group and
+  // after the last.  (With one or two token tiles the saved conversions do
+  // not pay for the subtractions: 28672 x 8192 at M = 1 took 31 us against
+  // 28, M = 64 53 against 57.)
+  constexpr bool kOff = !GA && !ACC && TM == 4;
+  const i32x4 cinit = kOff ? i32x4{kOffI, kOffI, kOffI, kOffI} : i32x4{0, 0, 0, 0};
+  float pend[TW];   // scales whose offsets are still in tot
+#pragma unroll
+  for (int k = 0; k < TW; ++k) pend[k] = 0.0f;
+  // tot += the previous group's sums times their scales
+  auto scale_prev = [&]() {
+#pragma unroll
+    for (int k = 0; k < TW; ++k)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if constexpr (kOff) {
+            const int32_t e = cp[k][i][v];   // (a bit cast of the vector element itself reads element 0)
+            tot[k][i][v] = __builtin_fmaf(__builtin_bit_cast(float, e), swp[k], tot[k][i][v]);
+          } else {
+            tot[k][i][v] = __builtin_fmaf(float(cp[k][i][v]), GA ? swp[k] * sap[i][v] : swp[k], tot[k][i][v]);
+          }
+        }
+    if constexpr (kOff) {
+#pragma unroll
+      for (int k = 0; k < TW; ++k) pend[k] += swp[k];
+    }
+  };
+  auto drop_offsets = [&]() {
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+      const float off = kOffF * pend[k];
+      pend[k] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tot[k][i][v] -= off;
+    }
+  };
 
   // ACC: this lane's original row (-1: none), loaded and awaited before the
   // first global->LDS load, so no later wait of the compiler's covers them
@@ -777,7 +819,7 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     for (int k = 0; k < TW; ++k)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        c[k][i] = mfma16_i8(av[i][0], bv[k][0], i32x4{0, 0, 0, 0});
+        c[k][i] = mfma16_i8(av[i][0], bv[k][0], cinit);
         c[k][i] = mfma16_i8(av[i][1], bv[k][1], c[k][i]);
       }
     if constexpr (ACC) {
@@ -796,13 +838,9 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
       }
       continue;
     }
-#pragma unroll
-    for (int k = 0; k < TW; ++k)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          tot[k][i][v] = __builtin_fmaf(float(cp[k][i][v]), GA ? swp[k] * sap[i][v] : swp[k], tot[k][i][v]);
+    scale_prev();   // group j - 1 (at j = 0 zero sums with zero scales)
+    if constexpr (kOff)
+      if (j >= 2 && (j & 1) == 0) drop_offsets();   // groups j - 2 and j - 1
 #pragma unroll
     for (int k = 0; k < TW; ++k) {
 #pragma unroll
@@ -815,13 +853,8 @@ __device__ __forceinline__ void stream_tiles(const W48Args& a, uint8_t* base, in
     }
   }
   if constexpr (ACC) return;
-#pragma unroll
-  for (int k = 0; k < TW; ++k)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        tot[k][i][v] = __builtin_fmaf(float(cp[k][i][v]), GA ? swp[k] * sap[i][v] : swp[k], tot[k][i][v]);
+  scale_prev();   // the last group
+  if constexpr (kOff) drop_offsets();
 
 #pragma unroll
   for (int k = 0; k < TW; ++k) {
