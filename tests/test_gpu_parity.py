@@ -967,7 +967,13 @@ def test_w44a8_28672x8192(M):
     y = gbb.gemm_w48a8(img, 28672, 8192, rows8.size, xq, xs).cpu().numpy()
     rows = one_row_per(packed_rows(28672, rows8), 16 if M <= 128 else 128, M)
     ref = ow48.reference(x, W[rows], np.nonzero(np.isin(rows, rows8))[0])
-    assert bq.rel_inf_err(y[:, rows].astype(np.float64), ref) <= TOL
+    err = bq.rel_inf_err(y[:, rows].astype(np.float64), ref)
+    assert err <= TOL
+    # the offset group sums (one fma per output on int32 sums offset by
+    # 1.5 * 2^23, the offsets removed every second group) add ~2e-4 of
+    # ||y||_inf at most; with the fp16 output rounding the whole error stays
+    # near 3e-4 on this layer
+    assert err <= 1e-3
 
 
 @pytest.mark.parametrize("M", [32, 96, 512])
