@@ -311,8 +311,10 @@ static_assert(3 * tile_lds<8>() <= 160 * 1024, "three 128-token workgroups per C
 static_assert(2 * (tile_lds<8>() + tile_xs<8>()) <= 160 * 1024, "two with staged scales");
 static_assert(4 * tile_lds<4>() <= 160 * 1024, "four 64-token workgroups per CU");
 static_assert(3 * (tile_lds<4>() + tile_xs<4>()) <= 160 * 1024, "three with staged scales");
-// resident workgroups per CU of the tile kernel (at 128 tokens, per-group
-// activation scales need more registers)
+// resident workgroups per CU of the tile kernel as the token-tile rule
+// counts them (at 128 tokens with per-group activation scales two: that
+// kernel took 204 VGPRs; at 164 since its token tiles run in halves three
+// fit, which measured the same)
 __host__ __device__ constexpr int tile_wgs_per_cu(int TT, bool ga) { return TT == 8 ? (ga ? 2 : 3) : 4; }
 
 // global->LDS loads with per-lane addresses: lane l's 16 (4) bytes land at
@@ -1097,10 +1099,10 @@ W48Split w48_split(int K, int T8, int T4, int M, size_t ws_bytes) {
 // workgroup takes about 6/8 of the time of a 128-token one (each 4-bit
 // expansion and weight load serves half as many MFMAs), so 64-token tiles are
 // taken when their rounds end sooner by that measure.  With per-group
-// activation scales a 128-token workgroup needs 204 registers and only two
-// are resident per CU, against four 64-token ones that take about as long
-// each: there 64-token tiles are taken unless the launch runs eight rounds or
-// more of 128-token tiles, where the two are within a few per cent.
+// activation scales the 128-token tile was measured at two workgroups per
+// CU against four 64-token ones of about the same duration each: there
+// 64-token tiles are taken unless the launch runs eight rounds or more of
+// 128-token tiles, where the two are within a few per cent.
 // Measured on 28672 x 8192 and 8192 x 28672, M = 129 ... 4096 (both tiles
 // give bit-identical outputs).
 static int tile_token_tiles(int T8, int T4, int M, int ga) {
